@@ -1,0 +1,164 @@
+"""CPU oracle for the 4-bit dequantize-fused GEMV / skinny-GEMM family.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares no
+code with the HIP library (``gemm_qgemv_q4_amd``) and imports nothing from it.
+
+What it computes, and where the pages define it:
+
+* Every product is ``y[m, n] = sum_k x[m, k] * w[n, k]`` where ``w`` is the
+  dequantized weight; the weights are decoded to f64 from the packed bytes,
+  the dot products are taken in f64 and the result is rounded to f32 once.
+  This follows the f64 CPU reference ``qmm_affine_t_cpu`` in the tests of
+  mlx-native ``qmm_affine.rs`` (dequantize ``q*s + b`` in f64, accumulate in
+  f64, cast to f32 at the end); the same plain definition is used for the two
+  GGML block formats.
+* ``block_q4_0``: fp16 ``d`` then 16 nibble bytes, value ``(nibble - 8) * d``
+  (mlx-native ``fused_dual_proj_q4_0.rs``, preconditions of
+  ``dispatch_fused_dual_proj_q4_0``: "sizeof(half) + 16 nibbles").  Which
+  nibble is which element is not on the pages; the reading used (low nibble of
+  byte j = element j, high nibble = element j+16) is listed in the design doc.
+* ``block_q4_K``: 144 bytes per 256 weights, row-major ``[N][K/256]``
+  (ferrum-kernels ``q4_k_gemv_v2.rs``, module doc and ``nb01``).  The field
+  layout is not on the pages; the reading used is listed in the design doc.
+* The fused dual projection equals two single Q4_0 products
+  (mlx-native ``fused_dual_proj_q4_0.rs``, module doc: the math contract).
+* ``qkv_split_f32`` copies columns ``[0,q_sp)``, ``[q_sp,q_sp+k_sp)`` and
+  ``[q_sp+k_sp, qkv_ch)`` of each token row into q, k, v
+  (mlx-native ``qkv_split.rs``, module doc and ``dispatch_qkv_split_f32``).
+
+Pins (tests/test_oracle_pins.py) tie each function to hand-decoded blocks
+under tests/golden/, closed forms, exact rational brute force and the
+quantize-then-decode round trip.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "f16_bits_to_f64", "decode_q4_0", "decode_q4_k", "decode_affine",
+    "gemv_f64", "abs_bound", "qgemv_q4_0", "qgemv_q4_k", "qgemv_dual_q4_0",
+    "qmm_affine_t", "qkv_split_f32", "q4k_scale_min",
+]
+
+
+def f16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """IEEE binary16 bit patterns (uint16) -> f64, subnormals included (exact)."""
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def _le16(lo: np.ndarray, hi: np.ndarray) -> np.ndarray:
+    return lo.astype(np.uint16) | (hi.astype(np.uint16) << 8)
+
+
+def decode_q4_0(w: np.ndarray, n: int, k: int) -> np.ndarray:
+    """Packed ``block_q4_0`` rows (uint8 ``[n, k/32*18]``) -> f64 ``[n, k]``.
+
+    Per block: ``d`` = fp16 at bytes 0..1 (little endian); byte ``2+j`` holds
+    element ``j`` in its low nibble and element ``j+16`` in its high nibble;
+    value = ``(nibble - 8) * d``.
+    """
+    assert k % 32 == 0
+    blk = np.asarray(w, dtype=np.uint8).reshape(n, k // 32, 18)
+    d = f16_bits_to_f64(_le16(blk[..., 0], blk[..., 1]))
+    qs = blk[..., 2:18].astype(np.int64)
+    nib = np.concatenate([qs & 0x0F, qs >> 4], axis=-1)  # elements 0..15, 16..31
+    return ((nib - 8).astype(np.float64) * d[..., None]).reshape(n, k)
+
+
+def q4k_scale_min(scales12: np.ndarray):
+    """Unpack the 12 scale bytes of a ``block_q4_K`` into (sc[8], m[8]) integers.
+
+    For sub-block j < 4 the 6-bit scale is the low 6 bits of byte j and the
+    6-bit min is the low 6 bits of byte j+4.  For j >= 4 the low 4 bits come
+    from byte j+4 (scale: low nibble, min: high nibble) and the top 2 bits from
+    bits 6..7 of byte j-4 (scale) or byte j (min).
+    """
+    s = np.asarray(scales12, dtype=np.int64)
+    sc = np.empty(s.shape[:-1] + (8,), dtype=np.int64)
+    mn = np.empty_like(sc)
+    for j in range(8):
+        if j < 4:
+            sc[..., j] = s[..., j] & 63
+            mn[..., j] = s[..., j + 4] & 63
+        else:
+            sc[..., j] = (s[..., j + 4] & 0x0F) | ((s[..., j - 4] >> 6) << 4)
+            mn[..., j] = (s[..., j + 4] >> 4) | ((s[..., j] >> 6) << 4)
+    return sc, mn
+
+
+def decode_q4_k(w: np.ndarray, n: int, k: int) -> np.ndarray:
+    """Packed ``block_q4_K`` rows (uint8 ``[n, k/256*144]``) -> f64 ``[n, k]``.
+
+    Per super-block: fp16 ``d`` @0, fp16 ``dmin`` @2, 12 scale bytes @4, 128
+    nibble bytes @16.  Nibble bytes come in 4 chunks of 32: the low nibble of
+    ``qs[32c + l]`` is element ``64c + l`` (sub-block 2c), the high nibble is
+    element ``64c + 32 + l`` (sub-block 2c+1).  Value of an element in
+    sub-block j: ``d * sc[j] * q - dmin * m[j]``.
+    """
+    assert k % 256 == 0
+    sb = np.asarray(w, dtype=np.uint8).reshape(n, k // 256, 144)
+    d = f16_bits_to_f64(_le16(sb[..., 0], sb[..., 1]))
+    dmin = f16_bits_to_f64(_le16(sb[..., 2], sb[..., 3]))
+    sc, mn = q4k_scale_min(sb[..., 4:16])
+    qs = sb[..., 16:144].astype(np.int64).reshape(n, k // 256, 4, 32)
+    q = np.concatenate([qs & 0x0F, qs >> 4], axis=-1).reshape(n, k // 256, 8, 32)
+    val = (d[..., None, None] * sc[..., None].astype(np.float64) * q.astype(np.float64)
+           - dmin[..., None, None] * mn[..., None].astype(np.float64))
+    return val.reshape(n, k)
+
+
+def decode_affine(q: np.ndarray, scales: np.ndarray, biases: np.ndarray,
+                  n: int, k: int, group_size: int) -> np.ndarray:
+    """u8 codes ``[n, k]`` with f32 ``scales``/``biases`` ``[n, k/gs]`` -> f64
+    ``w = q * s + b`` (mlx-native ``qmm_affine.rs``, ``qmm_affine_t_cpu``)."""
+    assert k % group_size == 0
+    qq = np.asarray(q, dtype=np.uint8).reshape(n, k).astype(np.float64)
+    s = np.asarray(scales, dtype=np.float32).reshape(n, k // group_size).astype(np.float64)
+    b = np.asarray(biases, dtype=np.float32).reshape(n, k // group_size).astype(np.float64)
+    s_full = np.repeat(s, group_size, axis=1)
+    b_full = np.repeat(b, group_size, axis=1)
+    return qq * s_full + b_full
+
+
+def gemv_f64(w64: np.ndarray, x: np.ndarray) -> np.ndarray:
+    """``y[m, n] = sum_k x[m, k] * w[n, k]`` in f64, rounded once to f32."""
+    x64 = np.asarray(x, dtype=np.float32).astype(np.float64)
+    return (x64 @ w64.T).astype(np.float32)
+
+
+def abs_bound(w64: np.ndarray, x: np.ndarray) -> np.ndarray:
+    """``sum_k |x[m, k] * w[n, k]|`` in f64: the scale of the parity tolerance."""
+    x64 = np.abs(np.asarray(x, dtype=np.float32).astype(np.float64))
+    return x64 @ np.abs(w64).T
+
+
+def qgemv_q4_0(w: np.ndarray, x: np.ndarray, m: int, n: int, k: int) -> np.ndarray:
+    """f32 ``y[m, n]`` for Q4_0 weights ``[n][k/32]`` and f32 ``x[m, k]``."""
+    return gemv_f64(decode_q4_0(w, n, k), np.asarray(x).reshape(m, k))
+
+
+def qgemv_q4_k(w: np.ndarray, x: np.ndarray, m: int, n: int, k: int) -> np.ndarray:
+    """f32 ``y[m, n]`` for Q4_K weights ``[n][k/256]`` and f32 ``x[m, k]``."""
+    return gemv_f64(decode_q4_k(w, n, k), np.asarray(x).reshape(m, k))
+
+
+def qgemv_dual_q4_0(w_a: np.ndarray, w_b: np.ndarray, x: np.ndarray,
+                    m: int, n: int, k: int):
+    """Two single Q4_0 products sharing ``x`` (the dual projection's contract)."""
+    return qgemv_q4_0(w_a, x, m, n, k), qgemv_q4_0(w_b, x, m, n, k)
+
+
+def qmm_affine_t(x: np.ndarray, q: np.ndarray, scales: np.ndarray, biases: np.ndarray,
+                 m: int, n: int, k: int, group_size: int) -> np.ndarray:
+    """f32 ``y = x * (s*q + b)^T`` with the weights dequantized in f64."""
+    return gemv_f64(decode_affine(q, scales, biases, n, k, group_size),
+                    np.asarray(x).reshape(m, k))
+
+
+def qkv_split_f32(qkv: np.ndarray, seq: int, q_sp: int, k_sp: int, v_sp: int):
+    """Split ``qkv[seq, q_sp+k_sp+v_sp]`` into contiguous q, k, v (bit copies)."""
+    a = np.asarray(qkv, dtype=np.float32).reshape(seq, q_sp + k_sp + v_sp)
+    return (np.ascontiguousarray(a[:, :q_sp]),
+            np.ascontiguousarray(a[:, q_sp:q_sp + k_sp]),
+            np.ascontiguousarray(a[:, q_sp + k_sp:]))
