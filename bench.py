@@ -1,0 +1,310 @@
+#!/usr/bin/env python3
+"""Benchmark of the 4-bit dequantize-fused GEMV library on one MI355X.
+
+Headline (the JSON line's `value`): effective HBM bandwidth of the Q4_K GEMV at
+M = 1, N = K = 4096 (an o_proj-sized decode product), i.e.
+    (weight bytes + x bytes + y bytes) / time per call,
+with the weights rotated over >= 1 GiB of distinct device copies so that the
+256 MB Infinity Cache cannot serve them, and the K timed calls captured in a
+HIP graph and replayed (the per-call launch cost of Python is not timed).
+
+The other four workloads (Q4_0 GEMV 1024^2, dual Q4_0 at M = 1/4/8, affine
+12288x4096 at M = 1/8, prefill affine GEMM 512x8192x2048 + qkv split) are
+measured the same way and reported under "per_config".
+
+`cpu_baseline` times the f64 CPU oracle on a bounded sample of the same
+workload on the host; `roofline.traffic` comes from the committed rocprofv3
+counter summary when it was taken on the current kernel source.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
+ROTATE_BYTES = 1 << 30
+HEADLINE = "q4_k_gemv_4096"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q4_k_gemv_4096_traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in ("gemm_qgemv_q4_amd/csrc/kernels/gemv.hpp", "gemm_qgemv_q4_amd/csrc/kernels/common.hpp",
+                "gemm_qgemv_q4_amd/csrc/api.hip"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Case:
+    """One workload: device inputs rotated over copies, a launch closure, byte/flop counts."""
+
+    def __init__(self, name, desc, nbytes, flops, copies, launch, bound="hbm"):
+        self.name, self.desc, self.nbytes, self.flops = name, desc, nbytes, flops
+        self.copies, self.launch, self.bound = copies, launch, bound
+
+
+def n_copies(weight_bytes):
+    return max(2, min(4096, -(-ROTATE_BYTES // weight_bytes)))
+
+
+def build_cases(qg, torch, only=None):
+    import synth
+    cfg = synth.CONFIGS
+    cases = []
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    def want(n):
+        return only is None or n == only or n.startswith(only)
+
+    def rot(t, r):
+        # r distinct device copies of one tensor (HBM does not deduplicate)
+        return [t] + [t.clone() for _ in range(r - 1)]
+
+    # --- Q4_K GEMV 4096^2, M = 1 (headline)
+    if want("q4_k_gemv_4096"):
+        c = cfg["q4_k_gemv_4096"]
+        w, x = synth.q4_k_case(c["seed"], c["m"], c["n"], c["k"])
+        r = n_copies(w.nbytes)
+        ws, dx = rot(dev(w), r), dev(x)
+        y = torch.empty((c["m"], c["n"]), dtype=torch.float32, device="cuda")
+        nb = w.nbytes + x.nbytes + y.numel() * 4
+        cases.append(Case("q4_k_gemv_4096", "Q4_K GEMV M=1 N=4096 K=4096", nb, 2 * c["n"] * c["k"], r,
+                          lambda i, ws=ws, dx=dx, y=y, r=r, n=c["n"], k=c["k"]:
+                          qg.qgemv_q4_k(ws[i % r], dx, n, k, y=y)))
+    # --- Q4_0 GEMV 1024^2, M = 1
+    if want("q4_0_gemv_1024"):
+        c = cfg["q4_0_gemv_1024"]
+        w, x = synth.q4_0_case(c["seed"], c["m"], c["n"], c["k"])
+        r = n_copies(w.nbytes)
+        ws, dx = rot(dev(w), r), dev(x)
+        y = torch.empty((c["m"], c["n"]), dtype=torch.float32, device="cuda")
+        nb = w.nbytes + x.nbytes + y.numel() * 4
+        cases.append(Case("q4_0_gemv_1024", "Q4_0 GEMV M=1 N=1024 K=1024", nb, 2 * c["n"] * c["k"], r,
+                          lambda i, ws=ws, dx=dx, y=y, r=r, n=c["n"], k=c["k"]:
+                          qg.qgemv_q4_0(ws[i % r], dx, n, k, y=y)))
+    # --- dual Q4_0 4096 -> 2 x 4096, M = 1, 4, 8
+    if want("dual_q4_0_4096"):
+        c = cfg["dual_q4_0_4096"]
+        wa, wb, x8 = synth.dual_q4_0_case(c["seed"], c["m"], c["n"], c["k"])
+        r = n_copies(wa.nbytes + wb.nbytes)
+        was, wbs = rot(dev(wa), r), rot(dev(wb), r)
+        for m in (1, 4, 8):
+            dx = dev(x8[:m])
+            ya = torch.empty((m, c["n"]), dtype=torch.float32, device="cuda")
+            yb = torch.empty_like(ya)
+            nb = wa.nbytes + wb.nbytes + m * c["k"] * 4 + 2 * m * c["n"] * 4
+            cases.append(Case(f"dual_q4_0_4096_m{m}", f"dual Q4_0 M={m} N=4096 K=4096", nb,
+                              4 * m * c["n"] * c["k"], r,
+                              lambda i, was=was, wbs=wbs, dx=dx, ya=ya, yb=yb, r=r, n=c["n"], k=c["k"]:
+                              qg.qgemv_dual_q4_0(was[i % r], wbs[i % r], dx, n, k, y_a=ya, y_b=yb)))
+    # --- affine 12288 x 4096 gs 64, M = 1, 8
+    if want("affine_12288x4096_gs64"):
+        c = cfg["affine_12288x4096_gs64"]
+        x8, q, s, b = synth.affine_case(c["seed"], c["m"], c["n"], c["k"], c["gs"])
+        wbytes = q.nbytes + s.nbytes + b.nbytes
+        r = n_copies(wbytes)
+        qs_, ss_, bs_ = rot(dev(q), r), rot(dev(s), r), rot(dev(b), r)
+        for m in (1, 8):
+            dx = dev(x8[:m])
+            y = torch.empty((m, c["n"]), dtype=torch.float32, device="cuda")
+            nb = wbytes + m * c["k"] * 4 + m * c["n"] * 4
+            cases.append(Case(f"affine_12288x4096_gs64_m{m}", f"affine gs64 M={m} N=12288 K=4096", nb,
+                              2 * m * c["n"] * c["k"], r,
+                              lambda i, qs_=qs_, ss_=ss_, bs_=bs_, dx=dx, y=y, r=r, gs=c["gs"]:
+                              qg.qmm_affine_t(dx, qs_[i % r], ss_[i % r], bs_[i % r], gs, y=y)))
+    # --- prefill affine GEMM 512 x 8192 x 2048 (matrix cores) + qkv split
+    if want("prefill_qkv_512x2048"):
+        c = cfg["prefill_qkv_512x2048"]
+        x, q, s, b = synth.affine_case(c["seed"], c["m"], c["n"], c["k"], c["gs"])
+        wbytes = q.nbytes + s.nbytes + b.nbytes
+        r = n_copies(wbytes)
+        qs_, ss_, bs_ = rot(dev(q), r), rot(dev(s), r), rot(dev(b), r)
+        dx = dev(x)
+        qkv = torch.empty((c["m"], c["n"]), dtype=torch.float32, device="cuda")
+        nb = wbytes + x.nbytes + qkv.numel() * 4
+        cases.append(Case("prefill_gemm_512x8192x2048", "affine gs64 M=512 N=8192 K=2048 (MFMA)", nb,
+                          2 * c["m"] * c["n"] * c["k"], r,
+                          lambda i, qs_=qs_, ss_=ss_, bs_=bs_, dx=dx, qkv=qkv, r=r, gs=c["gs"]:
+                          qg.qmm_affine_t(dx, qs_[i % r], ss_[i % r], bs_[i % r], gs, y=qkv),
+                          bound="mfma"))
+        qkv_r = rot(qkv, max(2, min(64, -(-ROTATE_BYTES // (qkv.numel() * 4)))))
+        rr = len(qkv_r)
+        qo = torch.empty((c["m"], c["q_sp"]), dtype=torch.float32, device="cuda")
+        ko = torch.empty((c["m"], c["k_sp"]), dtype=torch.float32, device="cuda")
+        vo = torch.empty((c["m"], c["v_sp"]), dtype=torch.float32, device="cuda")
+        cases.append(Case("qkv_split_512x8192", "qkv_split seq=512 2048|2048|4096", 2 * qkv.numel() * 4, 0, rr,
+                          lambda i, qkv_r=qkv_r, rr=rr, c=c, qo=qo, ko=ko, vo=vo:
+                          qg.qkv_split_f32(qkv_r[i % rr], c["m"], c["q_sp"], c["k_sp"], c["v_sp"],
+                                           q=qo, k=ko, v=vo)))
+    return cases
+
+
+def time_case(torch, case, steps, warmup):
+    """Warm up, capture `steps` calls in a graph, replay once untimed, then time
+    exactly one replay of `steps` calls with events on the launch stream."""
+    s = torch.cuda.current_stream()
+    for i in range(warmup):
+        case.launch(i)
+    torch.cuda.synchronize()
+    graph = None
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                case.launch(i)
+        graph = g
+    except Exception as e:  # capture not possible for this call: time eager launches
+        log(f"[bench] {case.name}: graph capture failed ({e}); timing eager launches")
+        torch.cuda.synchronize()
+    run = (lambda: graph.replay()) if graph is not None else (lambda: [case.launch(i) for i in range(steps)])
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = []
+    for _ in range(3):
+        torch.cuda.synchronize()
+        e0.record(s)
+        run()
+        e1.record(s)
+        torch.cuda.synchronize()
+        reps.append(e0.elapsed_time(e1))
+    ms = reps[0]
+    us = ms * 1e3 / steps
+    out = {
+        "desc": case.desc, "us_per_call": round(us, 3), "us_per_call_reps": [round(r * 1e3 / steps, 3) for r in reps],
+        "bytes": case.nbytes, "GBps": round(case.nbytes / (us * 1e-6) / 1e9, 1),
+        "frac_hbm_peak": round(case.nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "graph": graph is not None, "rotation_copies": case.copies, "steps": steps,
+    }
+    if case.flops:
+        out["TFLOPs"] = round(case.flops / (us * 1e-6) / 1e12, 2)
+    if case.bound == "mfma":
+        out["frac_mfma_bf16_peak_useful"] = round(case.flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+    del graph
+    return ms, out
+
+
+def cpu_baseline(budget_s=12.0):
+    """The oracle as it stands, on the host, single BLAS thread, full Q4_K
+    4096x4096 M=1 calls repeated until ~budget_s seconds have passed."""
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover
+        limiter = None
+    c = synth.CONFIGS[HEADLINE]
+    w, x = synth.q4_k_case(c["seed"], c["m"], c["n"], c["k"])
+    nb = w.nbytes + x.nbytes + c["m"] * c["n"] * 4
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        oracle.qgemv_q4_k(w, x, c["m"], c["n"], c["k"])
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or calls >= 200:
+            break
+    if limiter is not None:
+        limiter.unregister()
+    per = el / calls
+    return {"value": round(nb / per / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{calls} full Q4_K GEMV calls (M=1, N=K=4096) in {el:.1f}s, numpy f64 decode + matvec, "
+                      f"1 BLAS thread; {per * 1e6:.0f} us/call; host has {len(os.sched_getaffinity(0))} cores"}
+
+
+def read_traffic():
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--only", default=None, help="run only workloads whose name starts with this")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); "
+              "the path shards by output rows, see DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gemm_qgemv_q4_amd as qg
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    cases = build_cases(qg, torch, args.only)
+    per = {}
+    head_ms = None
+    for case in cases:
+        log(f"[bench] {case.name}: {case.desc} ({case.copies} rotating copies)")
+        ms, res = time_case(torch, case, args.steps, args.warmup)
+        per[case.name] = res
+        log(f"[bench] {case.name}: {res['us_per_call']} us/call, {res['GBps']} GB/s")
+        if case.name == HEADLINE:
+            head_ms = ms
+    torch.cuda.synchronize()
+
+    if HEADLINE not in per:
+        print(json.dumps({"per_config": per}))
+        return
+    h = per[HEADLINE]
+    ms_per_step = head_ms / args.steps
+    value = h["bytes"] / (ms_per_step * 1e-3) / 1e9
+    line = {
+        "metric": "effective HBM GB/s (weights+acts) and % of peak; us per GEMV at M=1",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "us_per_gemv": round(ms_per_step * 1e3, 3),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "Q4_K GEMV M=1 N=4096 K=4096 (o_proj-sized decode)", "M": 1, "N": 4096,
+                   "K": 4096, "weight_format": "Q4_K", "bytes_per_call": h["bytes"],
+                   "rotation_copies": h["rotation_copies"], "timing": "hip graph of K calls, hip events"},
+        "roofline": {"bound": "hbm", "kernel": "gemv_kernel<Q4_K>", "achieved": round(value, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(value / HBM_PEAK_GBS, 4),
+                     "traffic": read_traffic()},
+        "per_config": per,
+    }
+    if not args.no_cpu:
+        log("[bench] cpu baseline (oracle)")
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

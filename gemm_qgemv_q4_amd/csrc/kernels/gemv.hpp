@@ -1,0 +1,400 @@
+// Dequantize-fused GEMV / skinny GEMM kernels for gfx950 (CDNA4, wave64).
+//
+// y[m, n] = sum_k x[m, k] * w[n, k] for f32 x and 4-bit block-quantized w.
+// Formats (byte layouts, see the headers in include/qgemv_q4.h):
+//   Q4_0  : 18-byte blocks of 32 weights (fp16 d + 16 nibble bytes),
+//           value (nibble - 8) * d            [mlx-native fused_dual_proj_q4_0.rs]
+//   Q4_K  : 144-byte super-blocks of 256 weights (fp16 d, fp16 dmin, 12 bytes
+//           of 6-bit sub-block scales/mins, 128 nibble bytes),
+//           value d*sc*q - dmin*m              [ferrum-kernels q4_k_gemv_v2.rs]
+//   affine: u8 codes, f32 scale and bias per group, value s*q + b
+//                                              [mlx-native qmm_affine.rs]
+//
+// Work decomposition (chosen for wave64 and HBM streaming, not taken from the
+// pages' Metal kernels):
+//   * A row of weights is cut into "chunks" of CH weights (64 for Q4_0 = two
+//     blocks = 36 contiguous bytes; 64 for Q4_K = one 32-byte nibble run of a
+//     super-block plus its 16-byte header; 16 for affine = one 16-byte code
+//     load).  Consecutive lanes take consecutive chunks, so every wave-wide
+//     load instruction covers contiguous memory of one row.
+//   * L lanes serve one row; a wave serves P = 64/L rows side by side and R
+//     such row sets one after the other; each lane keeps NW*R*MT f32
+//     accumulators (NW = 1, or 2 for the dual projection).
+//   * x (MT rows of the activation) is staged once per workgroup in LDS as
+//     float4 columns [m][e4][chunk] (e4 = which 4 elements of the chunk), so
+//     the lanes of a wave read consecutive 16-byte words (no bank conflicts)
+//     and every x word read feeds R*NW rows.  For Q4_0/Q4_K the per-32 sums of
+//     x are staged too, which lets the block offset (-8*d, -dmin*m) be applied
+//     once per 32 weights instead of once per weight.
+//   * The lanes of a row are summed with a fixed xor butterfly: no atomics,
+//     and the arithmetic of one output does not depend on R, NW, MT or the
+//     number of waves, which makes the dual kernel bitwise equal to two
+//     single calls.
+#pragma once
+#include "common.hpp"
+
+namespace qg {
+
+enum { FMT_Q40 = 0, FMT_Q4K = 1, FMT_AFF = 2 };
+
+struct GemvParams {
+  const uint8_t* w0;      // weights (stream 0)
+  const uint8_t* w1;      // weights (stream 1, dual only)
+  const float* scales;    // affine: [N, K/gs]
+  const float* biases;    // affine: [N, K/gs]
+  const float* x;         // [m_rows, K] of this m-tile
+  float* y0;              // [m_rows, N] of this m-tile (stream 0)
+  float* y1;              // stream 1 (dual only)
+  long long row_bytes;    // bytes per weight row
+  int m_rows;             // valid x rows in this tile (<= MT)
+  int n, k;
+  int gs;                 // affine group size
+  int kt;                 // K elements staged per LDS tile (multiple of L*CH, or == k)
+  int rows_per_block;     // waves_per_block * P * R
+};
+
+template <int FMT> struct FmtTraits;
+template <> struct FmtTraits<FMT_Q40> { static constexpr int CH = 64; static constexpr bool SUMS = true; };
+template <> struct FmtTraits<FMT_Q4K> { static constexpr int CH = 64; static constexpr bool SUMS = true; };
+template <> struct FmtTraits<FMT_AFF> { static constexpr int CH = 16; static constexpr bool SUMS = false; };
+
+// Raw bytes of one chunk of one row.
+struct ChunkQ40 { u32x4a4 a; u32x4a4 b; uint32_t c; };   // 36 bytes: blocks 2t, 2t+1
+struct ChunkQ4K { u32x4 h; u32x4 qa; u32x4 qb; };         // header + 32 nibble bytes
+struct ChunkAff { u32x4 q; float s; float b; };           // 16 codes + their group's s, b
+
+template <int FMT> struct ChunkOf;
+template <> struct ChunkOf<FMT_Q40> { using T = ChunkQ40; };
+template <> struct ChunkOf<FMT_Q4K> { using T = ChunkQ4K; };
+template <> struct ChunkOf<FMT_AFF> { using T = ChunkAff; };
+
+template <int FMT>
+__device__ __forceinline__ typename ChunkOf<FMT>::T load_chunk(const GemvParams& p, const uint8_t* w,
+                                                               int row, int tg) {
+  typename ChunkOf<FMT>::T c;
+  if constexpr (FMT == FMT_Q40) {
+    const uint8_t* base = w + (size_t)row * (size_t)p.row_bytes + 36 * (size_t)tg;
+    c.a = *(const u32x4a4*)(base);
+    c.b = *(const u32x4a4*)(base + 16);
+    c.c = *(const uint32_t*)(base + 32);
+  } else if constexpr (FMT == FMT_Q4K) {
+    const uint8_t* base = w + (size_t)row * (size_t)p.row_bytes + 144 * (size_t)(tg >> 2);
+    c.h = *(const u32x4*)(base);
+    c.qa = *(const u32x4*)(base + 16 + 32 * (tg & 3));
+    c.qb = *(const u32x4*)(base + 32 + 32 * (tg & 3));
+  } else {
+    c.q = *(const u32x4*)(w + (size_t)row * (size_t)p.k + 16 * (size_t)tg);
+    const int groups = p.k / p.gs;
+    const size_t gi = (size_t)row * groups + (16 * tg) / p.gs;
+    c.s = p.scales[gi];
+    c.b = p.biases[gi];
+  }
+  return c;
+}
+
+// Per-half (32-weight) scale factors of a chunk: y += A0*dot0 + B0*sumx0 + A1*dot1 + B1*sumx1
+struct HalfScales { float a0, b0, a1, b1; };
+
+__device__ __forceinline__ HalfScales q40_scales(const ChunkQ40& c) {
+  // block 2t: d in bytes 0..1; block 2t+1: d in bytes 18..19 (high half of dword 4)
+  const float d0 = f16_bits_to_f32(c.a.x);
+  const float d1 = f16_bits_to_f32(c.b.x >> 16);
+  return {d0, -8.0f * d0, d1, -8.0f * d1};
+}
+
+// Sub-blocks 2c and 2c+1 of a Q4_K super-block.  The 12 scale bytes S0 (bytes
+// 0..3), S1 (4..7), S2 (8..11) hold, for sub-block j < 4, scale = S0 byte j & 63
+// and min = S1 byte j & 63; for j = 4 + i, scale = (S2 byte i & 15) | (S0 byte i
+// >> 6) << 4 and min = (S2 byte i >> 4) | (S1 byte i >> 6) << 4.  Sub-blocks 2c,
+// 2c+1 are adjacent bytes, so both are decoded with 16-bit wide masks.
+__device__ __forceinline__ HalfScales q4k_scales(const ChunkQ4K& c, int cc) {
+  const uint32_t sh = (uint32_t)(cc & 1) * 16u;
+  const uint32_t a0 = c.h.y >> sh, a1 = c.h.z >> sh, a2 = c.h.w >> sh;
+  const uint32_t sc_lo = a0 & 0x3F3Fu, m_lo = a1 & 0x3F3Fu;
+  const uint32_t sc_hi = (a2 & 0x0F0Fu) | ((a0 >> 2) & 0x3030u);
+  const uint32_t m_hi = ((a2 >> 4) & 0x0F0Fu) | ((a1 >> 2) & 0x3030u);
+  const uint32_t scp = cc < 2 ? sc_lo : sc_hi;
+  const uint32_t mp = cc < 2 ? m_lo : m_hi;
+  const float d = f16_bits_to_f32(c.h.x);
+  const float dmin = f16_bits_to_f32(c.h.x >> 16);
+  // d*sc and dmin*m are exact in f32 (11-bit by 6-bit significands)
+  return {d * ubyte_f32<0>(scp), -(dmin * ubyte_f32<0>(mp)), d * ubyte_f32<1>(scp), -(dmin * ubyte_f32<1>(mp))};
+}
+
+// The 16 dwords of nibble values (each byte 0..15) of a 64-weight chunk, in
+// element order: dword e4 holds elements 4*e4 .. 4*e4+3.
+__device__ __forceinline__ void unpack_q40(const ChunkQ40& c, uint32_t (&v)[16]) {
+  // block 2t: nibble bytes start at byte 2 -> realign across dwords 0..4
+  const uint32_t d[9] = {c.a.x, c.a.y, c.a.z, c.a.w, c.b.x, c.b.y, c.b.z, c.b.w, c.c};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t qa = __builtin_amdgcn_alignbyte(d[i + 1], d[i], 2);
+    v[i] = opaque(qa & 0x0F0F0F0Fu);             // elements 4i..4i+3 of block 2t
+    v[4 + i] = opaque((qa >> 4) & 0x0F0F0F0Fu);  // elements 16+4i.. of block 2t
+    const uint32_t qb = d[5 + i];                // block 2t+1: nibbles at bytes 20..35
+    v[8 + i] = opaque(qb & 0x0F0F0F0Fu);
+    v[12 + i] = opaque((qb >> 4) & 0x0F0F0F0Fu);
+  }
+}
+
+__device__ __forceinline__ void unpack_q4k(const ChunkQ4K& c, uint32_t (&v)[16]) {
+  const uint32_t q[8] = {c.qa.x, c.qa.y, c.qa.z, c.qa.w, c.qb.x, c.qb.y, c.qb.z, c.qb.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[i] = opaque(q[i] & 0x0F0F0F0Fu);             // sub-block 2c: low nibbles
+    v[8 + i] = opaque((q[i] >> 4) & 0x0F0F0F0Fu);  // sub-block 2c+1: high nibbles
+  }
+}
+
+template <int FMT, int MT, int NW, int L, int R>
+__global__ void __launch_bounds__(256) gemv_kernel(GemvParams p) {
+  constexpr int CH = FmtTraits<FMT>::CH;
+  constexpr int NE4 = CH / 4;
+  constexpr int P = kWave / L;
+  constexpr bool SUMS = FmtTraits<FMT>::SUMS;
+  using Chunk = typename ChunkOf<FMT>::T;
+
+  extern __shared__ f32x4 smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid / kWave;
+  const int lc = lane % L;
+  const int rp = lane / L;
+
+  int rows[R];
+  bool rvalid[R];
+  const int row0 = blockIdx.x * p.rows_per_block + wv * (P * R) + rp;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int rr = row0 + r * P;
+    rvalid[r] = rr < p.n;
+    rows[r] = rvalid[r] ? rr : p.n - 1;  // clamp: loads stay in bounds, store is skipped
+  }
+  const uint8_t* wptr[2] = {p.w0, NW == 2 ? p.w1 : p.w0};
+
+  float acc[NW][R][MT];
+#pragma unroll
+  for (int s = 0; s < NW; ++s)
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) acc[s][r][m] = 0.0f;
+
+  const int ct_max = p.kt / CH;
+  const int ctp = ct_max + 1;  // LDS pitch in float4s (odd, spreads banks on the staging writes)
+  f32x4* xs = smem;                                           // [MT][NE4][ctp]
+  float2* xsum = reinterpret_cast<float2*>(smem + MT * NE4 * ctp);  // [MT][ct_max]
+
+  for (int k0 = 0; k0 < p.k; k0 += p.kt) {
+    const int ktile = min(p.kt, p.k - k0);
+    const int ct = ktile / CH;
+    __syncthreads();
+    // ---- stage x[:, k0:k0+ktile] as [m][e4][chunk] float4 columns
+    const int n4 = ktile / 4;
+    for (int i = tid; i < MT * n4; i += blockDim.x) {
+      const int m = i / n4;
+      const int kk = (i - m * n4) * 4;
+      const int t = kk / CH;
+      const int e4 = (kk % CH) / 4;
+      f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (m < p.m_rows) {
+        const float* src = p.x + (size_t)m * p.k + k0 + kk;
+        v = f32x4{src[0], src[1], src[2], src[3]};
+      }
+      xs[(m * NE4 + e4) * ctp + t] = v;
+    }
+    __syncthreads();
+    if constexpr (SUMS) {
+      for (int i = tid; i < MT * ct; i += blockDim.x) {
+        const int m = i / ct;
+        const int t = i - m * ct;
+        float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+        for (int e4 = 0; e4 < NE4 / 2; ++e4) {
+          const f32x4 v = xs[(m * NE4 + e4) * ctp + t];
+          s0 += v.x; s0 += v.y; s0 += v.z; s0 += v.w;
+        }
+#pragma unroll
+        for (int e4 = NE4 / 2; e4 < NE4; ++e4) {
+          const f32x4 v = xs[(m * NE4 + e4) * ctp + t];
+          s1 += v.x; s1 += v.y; s1 += v.z; s1 += v.w;
+        }
+        xsum[m * ct_max + t] = float2{s0, s1};
+      }
+      __syncthreads();
+    }
+
+    // ---- stream the weights of this K tile
+    for (int t = lc; t < ct; t += L) {
+      const int tg = k0 / CH + t;
+      Chunk ch[NW][R];
+#pragma unroll
+      for (int s = 0; s < NW; ++s)
+#pragma unroll
+        for (int r = 0; r < R; ++r) ch[s][r] = load_chunk<FMT>(p, wptr[s], rows[r], tg);
+
+      if constexpr (FMT == FMT_AFF) {
+#pragma unroll
+        for (int e4 = 0; e4 < NE4; ++e4) {
+          f32x4 xv[MT];
+#pragma unroll
+          for (int m = 0; m < MT; ++m) xv[m] = xs[(m * NE4 + e4) * ctp + t];
+#pragma unroll
+          for (int s = 0; s < NW; ++s)
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+              const uint32_t qd = opaque(ch[s][r].q[e4]);
+              const float sc = ch[s][r].s, bi = ch[s][r].b;
+              const float w0 = __builtin_fmaf(sc, ubyte_f32<0>(qd), bi);
+              const float w1 = __builtin_fmaf(sc, ubyte_f32<1>(qd), bi);
+              const float w2 = __builtin_fmaf(sc, ubyte_f32<2>(qd), bi);
+              const float w3 = __builtin_fmaf(sc, ubyte_f32<3>(qd), bi);
+#pragma unroll
+              for (int m = 0; m < MT; ++m) {
+                float a = acc[s][r][m];
+                a = __builtin_fmaf(xv[m].x, w0, a);
+                a = __builtin_fmaf(xv[m].y, w1, a);
+                a = __builtin_fmaf(xv[m].z, w2, a);
+                a = __builtin_fmaf(xv[m].w, w3, a);
+                acc[s][r][m] = a;
+              }
+            }
+        }
+      } else {
+        HalfScales hs[NW][R];
+        uint32_t nib[NW][R][16];
+#pragma unroll
+        for (int s = 0; s < NW; ++s)
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            if constexpr (FMT == FMT_Q40) {
+              hs[s][r] = q40_scales(ch[s][r]);
+              unpack_q40(ch[s][r], nib[s][r]);
+            } else {
+              hs[s][r] = q4k_scales(ch[s][r], tg & 3);
+              unpack_q4k(ch[s][r], nib[s][r]);
+            }
+          }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float sub[NW][R][MT];
+#pragma unroll
+          for (int s = 0; s < NW; ++s)
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+              for (int m = 0; m < MT; ++m) sub[s][r][m] = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int e4 = h * 8 + e;
+            f32x4 xv[MT];
+#pragma unroll
+            for (int m = 0; m < MT; ++m) xv[m] = xs[(m * NE4 + e4) * ctp + t];
+#pragma unroll
+            for (int s = 0; s < NW; ++s)
+#pragma unroll
+              for (int r = 0; r < R; ++r) {
+                const uint32_t v = nib[s][r][e4];
+                const float q0 = ubyte_f32<0>(v), q1 = ubyte_f32<1>(v);
+                const float q2 = ubyte_f32<2>(v), q3 = ubyte_f32<3>(v);
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                  float a = sub[s][r][m];
+                  a = __builtin_fmaf(xv[m].x, q0, a);
+                  a = __builtin_fmaf(xv[m].y, q1, a);
+                  a = __builtin_fmaf(xv[m].z, q2, a);
+                  a = __builtin_fmaf(xv[m].w, q3, a);
+                  sub[s][r][m] = a;
+                }
+              }
+          }
+          // fold this 32-weight half: acc += A*dot + B*sum(x)
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            const float2 xsm = xsum[m * ct_max + t];
+            const float sx = h == 0 ? xsm.x : xsm.y;
+#pragma unroll
+            for (int s = 0; s < NW; ++s)
+#pragma unroll
+              for (int r = 0; r < R; ++r) {
+                const float A = h == 0 ? hs[s][r].a0 : hs[s][r].a1;
+                const float B = h == 0 ? hs[s][r].b0 : hs[s][r].b1;
+                float a = acc[s][r][m];
+                a = __builtin_fmaf(A, sub[s][r][m], a);
+                a = __builtin_fmaf(B, sx, a);
+                acc[s][r][m] = a;
+              }
+          }
+        }
+      }
+    }
+  }
+
+  // ---- sum the L lanes of each row and store
+  float* yptr[2] = {p.y0, NW == 2 ? p.y1 : p.y0};
+#pragma unroll
+  for (int s = 0; s < NW; ++s)
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const float v = wave_sum_xor(acc[s][r][m], L);
+        if (lc == 0 && rvalid[r] && m < p.m_rows) yptr[s][(size_t)m * p.n + rows[r]] = v;
+      }
+}
+
+// ---------------------------------------------------------------------------
+// Plain kernel for shapes and alignments the chunked kernel does not take
+// (K not a multiple of 64 for Q4_0, misaligned Q4_K rows, affine K % 16 != 0
+// or group_size < 16): one thread per output, sequential f32 sum over K.
+template <int FMT, int NW>
+__global__ void __launch_bounds__(256) gemv_plain_kernel(GemvParams p, int m_count) {
+  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  const int m = blockIdx.y;
+  if (n >= p.n || m >= m_count) return;
+  const float* xr = p.x + (size_t)m * p.k;
+  const uint8_t* wptr[2] = {p.w0, NW == 2 ? p.w1 : p.w0};
+  float* yptr[2] = {p.y0, NW == 2 ? p.y1 : p.y0};
+#pragma unroll
+  for (int s = 0; s < NW; ++s) {
+    const uint8_t* row = wptr[s] + (size_t)n * (size_t)p.row_bytes;
+    float a = 0.0f;
+    for (int k = 0; k < p.k; ++k) {
+      float w;
+      if constexpr (FMT == FMT_Q40) {
+        const uint8_t* blk = row + 18 * (k / 32);
+        const uint32_t d = blk[0] | ((uint32_t)blk[1] << 8);
+        const int j = k % 32;
+        const uint32_t byte = blk[2 + (j & 15)];
+        const int nib = j < 16 ? (int)(byte & 15u) : (int)(byte >> 4);
+        w = f16_bits_to_f32(d) * (float)(nib - 8);
+      } else if constexpr (FMT == FMT_Q4K) {
+        const uint8_t* sb = row + 144 * (k / 256);
+        const int e = k % 256;
+        const int j = e / 32;
+        const float d = f16_bits_to_f32(sb[0] | ((uint32_t)sb[1] << 8));
+        const float dmin = f16_bits_to_f32(sb[2] | ((uint32_t)sb[3] << 8));
+        const uint8_t* s12 = sb + 4;
+        int sc, mn;
+        if (j < 4) {
+          sc = s12[j] & 63;
+          mn = s12[j + 4] & 63;
+        } else {
+          sc = (s12[j + 4] & 0x0F) | ((s12[j - 4] >> 6) << 4);
+          mn = (s12[j + 4] >> 4) | ((s12[j] >> 6) << 4);
+        }
+        const uint32_t byte = sb[16 + 32 * (e / 64) + (e % 32)];
+        const int q = (e % 64) < 32 ? (int)(byte & 15u) : (int)(byte >> 4);
+        w = __builtin_fmaf(d * (float)sc, (float)q, -(dmin * (float)mn));
+      } else {
+        const int groups = p.k / p.gs;
+        const size_t gi = (size_t)n * groups + k / p.gs;
+        w = __builtin_fmaf(p.scales[gi], (float)row[k], p.biases[gi]);
+      }
+      a = __builtin_fmaf(xr[k], w, a);
+    }
+    yptr[s][(size_t)m * p.n + n] = a;
+  }
+}
+
+}  // namespace qg

@@ -1,0 +1,122 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+declared in include/*.h, and rejects bad arguments (before any HIP call) with
+QG_EINVAL and a message.  No kernel runs here."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+qg = pytest.importorskip("gemm_qgemv_q4_amd")
+
+P = ctypes.c_void_p
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"\b([A-Za-z_][A-Za-z0-9_]*)\s*\(", text):
+            name = m.group(1)
+            if name.startswith("qg") or name in ("qmm_affine_t", "qkv_split_f32"):
+                names.add(name)
+    return names
+
+
+def test_header_declares_the_five_entry_points():
+    names = declared_functions()
+    for fn in ("qgemv_q4_0", "qgemv_q4_k", "qgemv_dual_q4_0", "qmm_affine_t", "qkv_split_f32",
+               "qg_last_error"):
+        assert fn in names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(qg.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(qg.SIGNATURES)
+
+
+def _err(status):
+    assert status == qg.QG_EINVAL
+    msg = qg.last_error()
+    assert msg
+    return msg
+
+
+A = P(4096)  # fake, aligned, never dereferenced: validation fails first
+B = P(8192)
+C = P(16384)
+D = P(32768)
+E = P(65536)
+
+
+@pytest.mark.parametrize("m,n,k", [(0, 1, 32), (1, 0, 32), (1, 1, 0), (-1, 4, 32)])
+def test_q4_0_rejects_nonpositive_dims(m, n, k):
+    assert "must all be > 0" in _err(qg.raw.qgemv_q4_0(A, B, C, m, n, k, None))
+
+
+def test_q4_0_rejects_k_not_multiple_of_32():
+    assert "QK4_0" in _err(qg.raw.qgemv_q4_0(A, B, C, 1, 1, 48, None))
+
+
+def test_q4_0_rejects_null_and_misaligned():
+    assert "null" in _err(qg.raw.qgemv_q4_0(None, B, C, 1, 1, 32, None))
+    assert "null" in _err(qg.raw.qgemv_q4_0(A, None, C, 1, 1, 32, None))
+    assert "aligned" in _err(qg.raw.qgemv_q4_0(P(4098), B, C, 1, 1, 32, None))
+    assert "aligned" in _err(qg.raw.qgemv_q4_0(A, P(8194), C, 1, 1, 32, None))
+    assert "alias" in _err(qg.raw.qgemv_q4_0(A, B, B, 1, 1, 32, None))
+
+
+def test_q4_k_rejects_k_not_multiple_of_256():
+    assert "256" in _err(qg.raw.qgemv_q4_k(A, B, C, 1, 4, 384, None))
+    assert "must all be > 0" in _err(qg.raw.qgemv_q4_k(A, B, C, 1, 0, 256, None))
+
+
+def test_dual_rejects_same_outputs_and_bad_weights():
+    assert "different" in _err(qg.raw.qgemv_dual_q4_0(A, B, C, D, D, 1, 4, 32, None))
+    assert "null" in _err(qg.raw.qgemv_dual_q4_0(A, None, C, D, E, 1, 4, 32, None))
+    assert "QK4_0" in _err(qg.raw.qgemv_dual_q4_0(A, B, C, D, E, 1, 4, 40, None))
+
+
+@pytest.mark.parametrize("gs", [0, 1, 3, 5, 48, 2048, -64])
+def test_affine_rejects_bad_group_size(gs):
+    assert "group_size" in _err(qg.raw.qmm_affine_t(A, B, C, D, E, 1, 1, 64, gs, None))
+
+
+def test_affine_rejects_k_not_divisible_by_group_size():
+    # the page's rejects_k_not_divisible_by_group_size case uses gs = 5; here K % gs
+    assert "divisible" in _err(qg.raw.qmm_affine_t(A, B, C, D, E, 1, 1, 96, 64, None))
+    assert "must all be > 0" in _err(qg.raw.qmm_affine_t(A, B, C, D, E, 0, 1, 64, 64, None))
+    assert "null" in _err(qg.raw.qmm_affine_t(A, None, C, D, E, 1, 1, 64, 64, None))
+
+
+def test_qkv_split_rejects_zero_and_overflow():
+    assert "> 0" in _err(qg.raw.qkv_split_f32(A, B, C, D, 0, 4, 4, 4, None))
+    assert "> 0" in _err(qg.raw.qkv_split_f32(A, B, C, D, 2, 4, 0, 4, None))
+    big = 0xFFFFFFFF
+    assert "overflows u32" in _err(qg.raw.qkv_split_f32(A, B, C, D, 1, big, 1, 1, None))
+    assert "alias" in _err(qg.raw.qkv_split_f32(A, B, B, D, 1, 4, 4, 4, None))
+
+
+def test_mfma_threshold_knob():
+    old = qg.qg_get_mfma_min_m()
+    try:
+        qg.qg_set_mfma_min_m(7)
+        assert qg.qg_get_mfma_min_m() == 7
+        with pytest.raises(qg.QGError):
+            qg.qg_set_mfma_min_m(0)
+        assert qg.qg_get_mfma_min_m() == 7
+    finally:
+        qg.qg_set_mfma_min_m(old)
+
+
+def test_error_message_is_per_call():
+    _err(qg.raw.qgemv_q4_0(A, B, C, 1, 1, 48, None))
+    assert "QK4_0" in qg.last_error()
+    _err(qg.raw.qgemv_q4_k(A, B, C, 1, 4, 384, None))
+    assert "256" in qg.last_error()

@@ -1,0 +1,66 @@
+"""Full-size parity on the five benchmark workloads, in the launch configuration
+bench.py times (same entry points, same shapes, default variant choice).
+The oracle finishes every one of these in seconds on the host, so every output
+element is compared, not a sample."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from test_gpu_parity import assert_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+CFG = synth.CONFIGS
+
+
+def test_config_q4_0_gemv_1024(lib):
+    c = CFG["q4_0_gemv_1024"]
+    w, x = synth.q4_0_case(c["seed"], c["m"], c["n"], c["k"])
+    y = host(lib.qgemv_q4_0(dev(w), dev(x), c["n"], c["k"]))
+    assert_close(y, oracle.decode_q4_0(w, c["n"], c["k"]), x, "C q4_0 1024")
+
+
+def test_config_q4_k_gemv_4096(lib):
+    c = CFG["q4_k_gemv_4096"]
+    w, x = synth.q4_k_case(c["seed"], c["m"], c["n"], c["k"])
+    y = host(lib.qgemv_q4_k(dev(w), dev(x), c["n"], c["k"]))
+    assert_close(y, oracle.decode_q4_k(w, c["n"], c["k"]), x, "C q4_k 4096")
+
+
+@pytest.mark.parametrize("m", [1, 4, 8])
+def test_config_dual_q4_0_4096(lib, m):
+    c = CFG["dual_q4_0_4096"]
+    wa, wb, x8 = synth.dual_q4_0_case(c["seed"], c["m"], c["n"], c["k"])
+    x = np.ascontiguousarray(x8[:m])
+    dwa, dwb, dx = dev(wa), dev(wb), dev(x)
+    ya, yb = lib.qgemv_dual_q4_0(dwa, dwb, dx, c["n"], c["k"])
+    sa = host(lib.qgemv_q4_0(dwa, dx, c["n"], c["k"]))
+    sb = host(lib.qgemv_q4_0(dwb, dx, c["n"], c["k"]))
+    ya, yb = host(ya), host(yb)
+    assert np.array_equal(ya.view(np.uint32), sa.view(np.uint32))
+    assert np.array_equal(yb.view(np.uint32), sb.view(np.uint32))
+    assert_close(ya, oracle.decode_q4_0(wa, c["n"], c["k"]), x, f"C dual a m{m}")
+    assert_close(yb, oracle.decode_q4_0(wb, c["n"], c["k"]), x, f"C dual b m{m}")
+
+
+@pytest.mark.parametrize("m", [1, 8])
+def test_config_affine_12288x4096(lib, m):
+    c = CFG["affine_12288x4096_gs64"]
+    x8, q, s, b = synth.affine_case(c["seed"], c["m"], c["n"], c["k"], c["gs"])
+    x = np.ascontiguousarray(x8[:m])
+    y = host(lib.qmm_affine_t(dev(x), dev(q), dev(s), dev(b), c["gs"]))
+    assert_close(y, oracle.decode_affine(q, s, b, c["n"], c["k"], c["gs"]), x, f"C affine m{m}")
+
+
+def test_config_prefill_qkv_512x2048(lib):
+    c = CFG["prefill_qkv_512x2048"]
+    x, q, s, b = synth.affine_case(c["seed"], c["m"], c["n"], c["k"], c["gs"])
+    assert c["m"] >= lib.qg_get_mfma_min_m()  # the matrix-core path is the one timed
+    qkv = lib.qmm_affine_t(dev(x), dev(q), dev(s), dev(b), c["gs"])
+    qo, ko, vo = lib.qkv_split_f32(qkv, c["m"], c["q_sp"], c["k_sp"], c["v_sp"])
+    qkv_h = host(qkv)
+    assert_close(qkv_h, oracle.decode_affine(q, s, b, c["n"], c["k"], c["gs"]), x, "C prefill gemm")
+    rq, rk, rv = oracle.qkv_split_f32(qkv_h, c["m"], c["q_sp"], c["k_sp"], c["v_sp"])
+    for got, ref in ((qo, rq), (ko, rk), (vo, rv)):
+        assert np.array_equal(host(got).view(np.uint32), ref.view(np.uint32))
