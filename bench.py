@@ -41,8 +41,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q4_k_gemv_4096_traffic.json")
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for rel in ("gemm_qgemv_q4_amd/csrc/kernels/gemv.hpp", "gemm_qgemv_q4_amd/csrc/kernels/common.hpp",
-                "gemm_qgemv_q4_amd/csrc/api.hip"):
+    for rel in ("gemm_qgemv_q4_amd/csrc/kernels/gemv.hpp", "gemm_qgemv_q4_amd/csrc/kernels/common.hpp"):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -247,6 +246,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", default=None, help="run only workloads whose name starts with this")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy (x*1 -> y), the reference the HBM "
+                         "byte counters of the profiles are scaled by")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); "
@@ -270,6 +272,14 @@ def main():
         if case.name == HEADLINE:
             head_ms = ms
     torch.cuda.synchronize()
+    if args.calibrate_copy:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")  # 256 MiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 3 x (read 268435456 B, write 268435456 B) in elementwise mul kernels")
+        del src, dst
 
     if HEADLINE not in per:
         print(json.dumps({"per_config": per}))

@@ -5,6 +5,7 @@
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "qgemv_q4.h"
@@ -41,43 +42,82 @@ inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintp
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;  // keeps every in-kernel 32-bit index in range
-constexpr size_t kLdsBudget = 96 * 1024;
+constexpr size_t kLdsBudget = 64 * 1024;       // per-workgroup x tile when K is tiled
+constexpr size_t kLdsPersistent = 150 * 1024;  // whole-K x tile of a persistent workgroup
 constexpr size_t kLdsMax = 160 * 1024;
 
 // ------------------------------------------------------------------ GEMV
 struct GemvPlan {
-  int mt, l, r, waves, kt;
+  int mt, l, r, waves, kt, grid;
   size_t lds;
+  bool persistent;
 };
 
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return 256;
+  return cus;
+}
+
+// Launch shape of the chunked GEMV kernel.  x of one m-tile is staged in LDS
+// once per workgroup when it fits (persistent workgroups walk several row
+// groups); otherwise each workgroup owns one row group and stages x in K tiles.
 template <int FMT>
 GemvPlan plan_gemv(int64_t m, int64_t n, int64_t k, int nw) {
   constexpr int CH = FmtTraits<FMT>::CH;
   constexpr bool SUMS = FmtTraits<FMT>::SUMS;
   GemvPlan pl{};
   const int64_t chunks = k / CH;
-  pl.l = chunks >= 64 ? 64 : chunks >= 32 ? 32 : chunks >= 16 ? 16 : 8;
   pl.mt = m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : 8;
-  const int p_rows = 64 / pl.l;
-  const int64_t mtiles = cdiv(m, pl.mt);
-  int r = (pl.mt * nw <= 2) ? 4 : 2;
-  while (r > 1 && cdiv(n, (int64_t)p_rows * r) * mtiles < 2048) r /= 2;
-  pl.r = r;
-  int waves = 4;
-  while (waves > 1 && cdiv(n, (int64_t)waves * p_rows * r) * mtiles < 512) waves /= 2;
-  pl.waves = waves;
+  // Measured on MI355X: at MT >= 4 two rows per wave side by side (L = 32) and
+  // one 512-thread workgroup per CU are best; at MT <= 2 a full wave per row.
+  // Rows shorter than 32 chunks still get 32 lanes (two rows per wave; the
+  // lanes past the row's end idle), which measured faster than narrower groups.
+  const int lmax = pl.mt >= 4 ? 32 : 64;
+  pl.l = chunks >= lmax ? lmax : 32;
   auto lds_for = [&](int64_t kt) {
     const int64_t ct = kt / CH;
     return (size_t)(pl.mt * (CH / 4) * (ct + 1) * 16 + (SUMS ? pl.mt * ct * 8 : 0));
   };
-  const int64_t step = (int64_t)pl.l * CH;
-  int64_t kt = k;
-  if (lds_for(kt) > kLdsBudget) {
-    kt = step;
-    while (kt + step <= k && lds_for(kt + step) <= kLdsBudget) kt += step;
+  // Tuning override "L,R,W,B" (0 keeps the automatic choice; B = workgroups per CU
+  // of the persistent grid), e.g. QG_GEMV_PLAN=32,2,4,2
+  int el = 0, er = 0, ew = 0, eb = 0;
+  if (const char* env = getenv("QG_GEMV_PLAN")) {
+    if (sscanf(env, "%d,%d,%d,%d", &el, &er, &ew, &eb) < 1) el = er = ew = eb = 0;
   }
-  pl.kt = (int)kt;
-  pl.lds = lds_for(kt);
+  if (el == 8 || el == 16 || el == 32 || el == 64) pl.l = el;
+  const int p_rows = 64 / pl.l;
+  const int64_t mtiles = cdiv(m, pl.mt);
+  int r = (pl.mt * nw <= 2 && chunks >= 64) ? 2 : 1;
+  if (er == 1 || (er == 2 && pl.mt * nw <= 2) || (er == 4 && pl.mt * nw == 1)) r = er;
+  pl.r = r;
+
+  pl.persistent = lds_for(k) <= kLdsPersistent;
+  if (pl.persistent) {
+    pl.kt = (int)k;
+    pl.lds = lds_for(k);
+    pl.waves = (FMT == FMT_AFF && pl.mt <= 2) ? 4 : 8;
+    if (ew == 1 || ew == 2 || ew == 4 || ew == 8) pl.waves = ew;
+    int bpc = (int)(kLdsMax / (pl.lds ? pl.lds : 1));
+    const int bpc_max = pl.waves == 8 ? 1 : 4;
+    bpc = bpc < 1 ? 1 : bpc > bpc_max ? bpc_max : bpc;
+    if (eb >= 1 && eb <= 8 && (size_t)eb * pl.lds <= kLdsMax) bpc = eb;
+    const int64_t groups = cdiv(n, (int64_t)pl.waves * p_rows * r);
+    const int64_t cap = (int64_t)device_cus() * bpc;
+    pl.grid = (int)(groups < cap ? groups : cap);
+  } else {
+    pl.waves = 4;
+    if (ew == 1 || ew == 2 || ew == 4) pl.waves = ew;
+    const int64_t step = (int64_t)pl.l * CH;
+    int64_t kt = step;
+    while (kt + step <= k && lds_for(kt + step) <= kLdsBudget) kt += step;
+    pl.kt = (int)kt;
+    pl.lds = lds_for(kt);
+    pl.grid = (int)cdiv(n, (int64_t)pl.waves * p_rows * r);
+  }
+  (void)mtiles;
   return pl;
 }
 
@@ -99,11 +139,14 @@ hipError_t launch_gemv_t(const GemvParams& p, dim3 grid, dim3 block, size_t lds,
 
 template <int FMT, int MT, int NW, int L>
 hipError_t launch_gemv_r(int r, const GemvParams& p, dim3 g, dim3 b, size_t lds, hipStream_t s) {
+  // row sets per wave that fit the 256-VGPR budget of a 512-thread workgroup
   switch (r) {
     case 4:
-      if constexpr (MT * NW <= 2) return launch_gemv_t<FMT, MT, NW, L, 4>(p, g, b, lds, s);
+      if constexpr (MT * NW == 1) return launch_gemv_t<FMT, MT, NW, L, 4>(p, g, b, lds, s);
       break;
-    case 2: return launch_gemv_t<FMT, MT, NW, L, 2>(p, g, b, lds, s);
+    case 2:
+      if constexpr (MT * NW <= 2) return launch_gemv_t<FMT, MT, NW, L, 2>(p, g, b, lds, s);
+      break;
     case 1: return launch_gemv_t<FMT, MT, NW, L, 1>(p, g, b, lds, s);
   }
   return hipErrorInvalidValue;
@@ -153,7 +196,7 @@ qg_status run_gemv(const char* op, GemvParams p, int64_t m, bool plain, hipStrea
   p.kt = pl.kt;
   p.rows_per_block = pl.waves * p_rows * pl.r;
   const dim3 block(64 * pl.waves);
-  const int64_t blocks_x = cdiv(p.n, p.rows_per_block);
+  const int64_t blocks_x = pl.grid;
   for (int64_t m0 = 0; m0 < m; m0 += pl.mt) {
     GemvParams q = p;
     q.x = p.x + m0 * p.k;

@@ -146,12 +146,121 @@ __device__ __forceinline__ void unpack_q4k(const ChunkQ4K& c, uint32_t (&v)[16])
   }
 }
 
+// Decode one chunk of every (stream, row) and accumulate it.
+template <int FMT, int MT, int NW, int R>
+__device__ __forceinline__ void compute_chunk(const typename ChunkOf<FMT>::T (&ch)[NW][R], const f32x4* xs,
+                                              const float* xsum, int ctp, int ct_max, int t, int tg,
+                                              float (&acc)[NW][R][MT]) {
+  constexpr int CH = FmtTraits<FMT>::CH;
+  constexpr int NE4 = CH / 4;
+  if constexpr (FMT == FMT_AFF) {
+#pragma unroll
+    for (int e4 = 0; e4 < NE4; ++e4) {
+      f32x4 xv[MT];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) xv[m] = xs[(m * NE4 + e4) * ctp + t];
+#pragma unroll
+      for (int s = 0; s < NW; ++s)
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const uint32_t qd = opaque(ch[s][r].q[e4]);
+          const float sc = ch[s][r].s, bi = ch[s][r].b;
+          const float w0 = __builtin_fmaf(sc, ubyte_f32<0>(qd), bi);
+          const float w1 = __builtin_fmaf(sc, ubyte_f32<1>(qd), bi);
+          const float w2 = __builtin_fmaf(sc, ubyte_f32<2>(qd), bi);
+          const float w3 = __builtin_fmaf(sc, ubyte_f32<3>(qd), bi);
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            float a = acc[s][r][m];
+            a = __builtin_fmaf(xv[m].x, w0, a);
+            a = __builtin_fmaf(xv[m].y, w1, a);
+            a = __builtin_fmaf(xv[m].z, w2, a);
+            a = __builtin_fmaf(xv[m].w, w3, a);
+            acc[s][r][m] = a;
+          }
+        }
+    }
+  } else {
+    HalfScales hs[NW][R];
+    uint32_t nib[NW][R][16];
+#pragma unroll
+    for (int s = 0; s < NW; ++s)
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if constexpr (FMT == FMT_Q40) {
+          hs[s][r] = q40_scales(ch[s][r]);
+          unpack_q40(ch[s][r], nib[s][r]);
+        } else {
+          hs[s][r] = q4k_scales(ch[s][r], tg & 3);
+          unpack_q4k(ch[s][r], nib[s][r]);
+        }
+      }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float sub[NW][R][MT];
+#pragma unroll
+      for (int s = 0; s < NW; ++s)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int m = 0; m < MT; ++m) sub[s][r][m] = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int e4 = h * 8 + e;
+        f32x4 xv[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) xv[m] = xs[(m * NE4 + e4) * ctp + t];
+#pragma unroll
+        for (int s = 0; s < NW; ++s)
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            const uint32_t v = nib[s][r][e4];
+            const float q0 = ubyte_f32<0>(v), q1 = ubyte_f32<1>(v);
+            const float q2 = ubyte_f32<2>(v), q3 = ubyte_f32<3>(v);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+              float a = sub[s][r][m];
+              a = __builtin_fmaf(xv[m].x, q0, a);
+              a = __builtin_fmaf(xv[m].y, q1, a);
+              a = __builtin_fmaf(xv[m].z, q2, a);
+              a = __builtin_fmaf(xv[m].w, q3, a);
+              sub[s][r][m] = a;
+            }
+          }
+      }
+      // fold this 32-weight half: acc += A*dot + B*sum(x)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const float sx = xsum[(m * ct_max + t) * 2 + h];
+#pragma unroll
+        for (int s = 0; s < NW; ++s)
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            const float A = h == 0 ? hs[s][r].a0 : hs[s][r].a1;
+            const float B = h == 0 ? hs[s][r].b0 : hs[s][r].b1;
+            float a = acc[s][r][m];
+            a = __builtin_fmaf(A, sub[s][r][m], a);
+            a = __builtin_fmaf(B, sx, a);
+            acc[s][r][m] = a;
+          }
+      }
+    }
+  }
+}
+
+// Workgroup = WV waves.  A "group" is WV*P*R consecutive rows (wave w takes
+// P*R of them).  When x fits in LDS (kt == K) a workgroup stages it once and
+// then walks groups blockIdx.x, blockIdx.x + gridDim.x, ... ("persistent");
+// otherwise it owns one group and stages x tile by tile.  The lane's weight
+// loads run one step ahead of its arithmetic across chunk, tile and group
+// boundaries.
 template <int FMT, int MT, int NW, int L, int R>
-__global__ void __launch_bounds__(256) gemv_kernel(GemvParams p) {
+__global__ void __launch_bounds__(512) gemv_kernel(GemvParams p) {
   constexpr int CH = FmtTraits<FMT>::CH;
   constexpr int NE4 = CH / 4;
   constexpr int P = kWave / L;
   constexpr bool SUMS = FmtTraits<FMT>::SUMS;
+  constexpr int SB = 4;  // float4s of x per thread per staging batch
   using Chunk = typename ChunkOf<FMT>::T;
 
   extern __shared__ f32x4 smem[];
@@ -160,187 +269,136 @@ __global__ void __launch_bounds__(256) gemv_kernel(GemvParams p) {
   const int wv = tid / kWave;
   const int lc = lane % L;
   const int rp = lane / L;
+  const int rows_per_group = p.rows_per_block;
+  const int n_groups = (p.n + rows_per_group - 1) / rows_per_group;
+  const int n_chunks = p.k / CH;
+  const int ct_max = p.kt / CH;
+  const int ctp = ct_max + 1;  // LDS pitch in float4s (odd: spreads banks on the staging writes)
+  f32x4* xs = smem;                                              // [MT][NE4][ctp]
+  float* xsum = reinterpret_cast<float*>(smem + MT * NE4 * ctp);  // [MT][ct_max][2]
+  const bool x_vec = (reinterpret_cast<uintptr_t>(p.x) & 15u) == 0;
+  const uint8_t* wptr[2] = {p.w0, NW == 2 ? p.w1 : p.w0};
+  float* yptr[2] = {p.y0, NW == 2 ? p.y1 : p.y0};
 
+  auto group_rows = [&](int g, int (&rows)[R], bool (&valid)[R]) {
+    const int row0 = g * rows_per_group + wv * (P * R) + rp;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int rr = row0 + r * P;
+      valid[r] = rr < p.n;
+      rows[r] = valid[r] ? rr : p.n - 1;  // clamp: loads stay in bounds, the store is skipped
+    }
+  };
+  auto fetch = [&](Chunk (&dst)[NW][R], const int (&rows)[R], int tg) {
+#pragma unroll
+    for (int s = 0; s < NW; ++s)
+#pragma unroll
+      for (int r = 0; r < R; ++r) dst[s][r] = load_chunk<FMT>(p, wptr[s], rows[r], tg);
+  };
+
+  // Stage x[:, k0:k0+ktile] as [m][e4][chunk] float4 columns plus the sums of
+  // each 32-element half (8 consecutive float4s = 8 consecutive lanes).  Index
+  // math is shifts only (CH is a power of two); loops are uniform so every lane
+  // takes part in the shuffles.
+  auto stage = [&](int k0, int ktile) {
+    const int n4 = ktile >> 2;
+    const int step = SB * (int)blockDim.x;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const float* xrow = p.x + (size_t)m * p.k + k0;
+      const bool live = m < p.m_rows;
+      for (int j0 = 0; j0 < n4; j0 += step) {
+        f32x4 v[SB];
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {
+          const int j = j0 + u * (int)blockDim.x + tid;
+          v[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+          if (live && j < n4) {
+            if (x_vec) v[u] = *reinterpret_cast<const f32x4*>(xrow + 4 * j);
+            else v[u] = f32x4{xrow[4 * j], xrow[4 * j + 1], xrow[4 * j + 2], xrow[4 * j + 3]};
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {
+          const int j = j0 + u * (int)blockDim.x + tid;
+          const int t = j / NE4;        // chunk (NE4 is a power of two)
+          const int e4 = j % NE4;       // float4 within the chunk
+          if (j < n4) xs[(m * NE4 + e4) * ctp + t] = v[u];
+          if constexpr (SUMS) {
+            float sm = ((v[u].x + v[u].y) + v[u].z) + v[u].w;
+            sm += __shfl_xor(sm, 1, kWave);
+            sm += __shfl_xor(sm, 2, kWave);
+            sm += __shfl_xor(sm, 4, kWave);
+            if (j < n4 && (e4 & 7) == 0) xsum[(m * ct_max + t) * 2 + (e4 >> 3)] = sm;
+          }
+        }
+      }
+    }
+    __syncthreads();
+  };
+
+  const bool persistent = p.kt >= p.k;
+  int g = blockIdx.x;
   int rows[R];
   bool rvalid[R];
-  const int row0 = blockIdx.x * p.rows_per_block + wv * (P * R) + rp;
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int rr = row0 + r * P;
-    rvalid[r] = rr < p.n;
-    rows[r] = rvalid[r] ? rr : p.n - 1;  // clamp: loads stay in bounds, store is skipped
-  }
-  const uint8_t* wptr[2] = {p.w0, NW == 2 ? p.w1 : p.w0};
+  group_rows(g, rows, rvalid);
+  Chunk cur[NW][R];
+  const int tg0 = lc < n_chunks ? lc : 0;
+  bool staged = false;
 
-  float acc[NW][R][MT];
+  while (g < n_groups) {
+    float acc[NW][R][MT];
 #pragma unroll
-  for (int s = 0; s < NW; ++s)
+    for (int s = 0; s < NW; ++s)
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+      for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int m = 0; m < MT; ++m) acc[s][r][m] = 0.0f;
+        for (int m = 0; m < MT; ++m) acc[s][r][m] = 0.0f;
+    const int g_next = g + gridDim.x;
+    int rows_next[R];
+    bool valid_next[R];
+    group_rows(g_next < n_groups ? g_next : g, rows_next, valid_next);
 
-  const int ct_max = p.kt / CH;
-  const int ctp = ct_max + 1;  // LDS pitch in float4s (odd, spreads banks on the staging writes)
-  f32x4* xs = smem;                                           // [MT][NE4][ctp]
-  float2* xsum = reinterpret_cast<float2*>(smem + MT * NE4 * ctp);  // [MT][ct_max]
-
-  for (int k0 = 0; k0 < p.k; k0 += p.kt) {
-    const int ktile = min(p.kt, p.k - k0);
-    const int ct = ktile / CH;
-    __syncthreads();
-    // ---- stage x[:, k0:k0+ktile] as [m][e4][chunk] float4 columns
-    const int n4 = ktile / 4;
-    for (int i = tid; i < MT * n4; i += blockDim.x) {
-      const int m = i / n4;
-      const int kk = (i - m * n4) * 4;
-      const int t = kk / CH;
-      const int e4 = (kk % CH) / 4;
-      f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (m < p.m_rows) {
-        const float* src = p.x + (size_t)m * p.k + k0 + kk;
-        v = f32x4{src[0], src[1], src[2], src[3]};
+    for (int k0 = 0; k0 < p.k; k0 += p.kt) {
+      const int ktile = min(p.kt, p.k - k0);
+      const int ct = ktile / CH;
+      if (!persistent || !staged) {
+        if (staged) __syncthreads();  // the previous tile's readers are done
+        else fetch(cur, rows, tg0);   // first weights in flight while x is staged
+        stage(k0, ktile);
+        staged = true;
       }
-      xs[(m * NE4 + e4) * ctp + t] = v;
-    }
-    __syncthreads();
-    if constexpr (SUMS) {
-      for (int i = tid; i < MT * ct; i += blockDim.x) {
-        const int m = i / ct;
-        const int t = i - m * ct;
-        float s0 = 0.0f, s1 = 0.0f;
-#pragma unroll
-        for (int e4 = 0; e4 < NE4 / 2; ++e4) {
-          const f32x4 v = xs[(m * NE4 + e4) * ctp + t];
-          s0 += v.x; s0 += v.y; s0 += v.z; s0 += v.w;
-        }
-#pragma unroll
-        for (int e4 = NE4 / 2; e4 < NE4; ++e4) {
-          const f32x4 v = xs[(m * NE4 + e4) * ctp + t];
-          s1 += v.x; s1 += v.y; s1 += v.z; s1 += v.w;
-        }
-        xsum[m * ct_max + t] = float2{s0, s1};
-      }
-      __syncthreads();
-    }
-
-    // ---- stream the weights of this K tile
-    for (int t = lc; t < ct; t += L) {
-      const int tg = k0 / CH + t;
-      Chunk ch[NW][R];
-#pragma unroll
-      for (int s = 0; s < NW; ++s)
-#pragma unroll
-        for (int r = 0; r < R; ++r) ch[s][r] = load_chunk<FMT>(p, wptr[s], rows[r], tg);
-
-      if constexpr (FMT == FMT_AFF) {
-#pragma unroll
-        for (int e4 = 0; e4 < NE4; ++e4) {
-          f32x4 xv[MT];
-#pragma unroll
-          for (int m = 0; m < MT; ++m) xv[m] = xs[(m * NE4 + e4) * ctp + t];
-#pragma unroll
-          for (int s = 0; s < NW; ++s)
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-              const uint32_t qd = opaque(ch[s][r].q[e4]);
-              const float sc = ch[s][r].s, bi = ch[s][r].b;
-              const float w0 = __builtin_fmaf(sc, ubyte_f32<0>(qd), bi);
-              const float w1 = __builtin_fmaf(sc, ubyte_f32<1>(qd), bi);
-              const float w2 = __builtin_fmaf(sc, ubyte_f32<2>(qd), bi);
-              const float w3 = __builtin_fmaf(sc, ubyte_f32<3>(qd), bi);
-#pragma unroll
-              for (int m = 0; m < MT; ++m) {
-                float a = acc[s][r][m];
-                a = __builtin_fmaf(xv[m].x, w0, a);
-                a = __builtin_fmaf(xv[m].y, w1, a);
-                a = __builtin_fmaf(xv[m].z, w2, a);
-                a = __builtin_fmaf(xv[m].w, w3, a);
-                acc[s][r][m] = a;
-              }
-            }
-        }
-      } else {
-        HalfScales hs[NW][R];
-        uint32_t nib[NW][R][16];
+      for (int t = lc; t < ct; t += L) {
+        const int tg = k0 / CH + t;
+        Chunk nxt[NW][R];
+        if (tg + L < n_chunks) fetch(nxt, rows, tg + L);
+        else if (g_next < n_groups) fetch(nxt, rows_next, tg0);
+        compute_chunk<FMT, MT, NW, R>(cur, xs, xsum, ctp, ct_max, t, tg, acc);
 #pragma unroll
         for (int s = 0; s < NW; ++s)
 #pragma unroll
-          for (int r = 0; r < R; ++r) {
-            if constexpr (FMT == FMT_Q40) {
-              hs[s][r] = q40_scales(ch[s][r]);
-              unpack_q40(ch[s][r], nib[s][r]);
-            } else {
-              hs[s][r] = q4k_scales(ch[s][r], tg & 3);
-              unpack_q4k(ch[s][r], nib[s][r]);
-            }
-          }
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          float sub[NW][R][MT];
-#pragma unroll
-          for (int s = 0; s < NW; ++s)
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-#pragma unroll
-              for (int m = 0; m < MT; ++m) sub[s][r][m] = 0.0f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int e4 = h * 8 + e;
-            f32x4 xv[MT];
-#pragma unroll
-            for (int m = 0; m < MT; ++m) xv[m] = xs[(m * NE4 + e4) * ctp + t];
-#pragma unroll
-            for (int s = 0; s < NW; ++s)
-#pragma unroll
-              for (int r = 0; r < R; ++r) {
-                const uint32_t v = nib[s][r][e4];
-                const float q0 = ubyte_f32<0>(v), q1 = ubyte_f32<1>(v);
-                const float q2 = ubyte_f32<2>(v), q3 = ubyte_f32<3>(v);
-#pragma unroll
-                for (int m = 0; m < MT; ++m) {
-                  float a = sub[s][r][m];
-                  a = __builtin_fmaf(xv[m].x, q0, a);
-                  a = __builtin_fmaf(xv[m].y, q1, a);
-                  a = __builtin_fmaf(xv[m].z, q2, a);
-                  a = __builtin_fmaf(xv[m].w, q3, a);
-                  sub[s][r][m] = a;
-                }
-              }
-          }
-          // fold this 32-weight half: acc += A*dot + B*sum(x)
-#pragma unroll
-          for (int m = 0; m < MT; ++m) {
-            const float2 xsm = xsum[m * ct_max + t];
-            const float sx = h == 0 ? xsm.x : xsm.y;
-#pragma unroll
-            for (int s = 0; s < NW; ++s)
-#pragma unroll
-              for (int r = 0; r < R; ++r) {
-                const float A = h == 0 ? hs[s][r].a0 : hs[s][r].a1;
-                const float B = h == 0 ? hs[s][r].b0 : hs[s][r].b1;
-                float a = acc[s][r][m];
-                a = __builtin_fmaf(A, sub[s][r][m], a);
-                a = __builtin_fmaf(B, sx, a);
-                acc[s][r][m] = a;
-              }
-          }
-        }
+          for (int r = 0; r < R; ++r) cur[s][r] = nxt[s][r];
       }
     }
-  }
 
-  // ---- sum the L lanes of each row and store
-  float* yptr[2] = {p.y0, NW == 2 ? p.y1 : p.y0};
+    // ---- sum the L lanes of each row and store
 #pragma unroll
-  for (int s = 0; s < NW; ++s)
+    for (int s = 0; s < NW; ++s)
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+      for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const float v = wave_sum_xor(acc[s][r][m], L);
-        if (lc == 0 && rvalid[r] && m < p.m_rows) yptr[s][(size_t)m * p.n + rows[r]] = v;
-      }
+        for (int m = 0; m < MT; ++m) {
+          const float v = group_sum(acc[s][r][m], L);
+          if (lc == 0 && rvalid[r] && m < p.m_rows) yptr[s][(size_t)m * p.n + rows[r]] = v;
+        }
+    g = g_next;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      rows[r] = rows_next[r];
+      rvalid[r] = valid_next[r];
+    }
+    if (!persistent) break;
+  }
 }
 
 // ---------------------------------------------------------------------------
