@@ -324,11 +324,13 @@ qg_status qmm_affine_t(const float* x, const uint8_t* q, const float* scales, co
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int gs = (int)group_size;
 
-  if (M >= g_mfma_min_m.load() && gs >= 32 && K % 64 == 0 && aligned(q, 16)) {
+  if (M >= g_mfma_min_m.load() && gs >= 32 && gs <= 512 && K % 64 == 0 && aligned(q, 16) &&
+      M * K < ((int64_t)1 << 31) && N * K < ((int64_t)1 << 31)) {
     // ---- matrix-core path: prepare x (bf16 hi/lo + group sums), then GEMM
     const int64_t groups = K / gs;
     const size_t bytes_x = (size_t)M * K * sizeof(__bf16);
-    const size_t bytes = 2 * bytes_x + (size_t)M * groups * sizeof(float) + 256;
+    const size_t bytes_s = (size_t)M * groups * sizeof(__bf16);
+    const size_t bytes = 2 * bytes_x + 2 * bytes_s + 512;
     (void)hipGetLastError();
     void* scratch = nullptr;
     hipError_t e = hipMallocAsync(&scratch, bytes, s);
@@ -337,16 +339,21 @@ qg_status qmm_affine_t(const float* x, const uint8_t* q, const float* scales, co
                hipGetErrorString(e));
       return QG_ELAUNCH;
     }
+    auto align256 = [](void* p) {
+      return reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(p) + 255) & ~(uintptr_t)255);
+    };
     __bf16* xh = static_cast<__bf16*>(scratch);
     __bf16* xl = xh + (size_t)M * K;
-    float* xs = reinterpret_cast<float*>(reinterpret_cast<uintptr_t>(xl + (size_t)M * K) + 255 & ~(uintptr_t)255);
-    const int64_t items = M * groups;
-    hipLaunchKernelGGL(affine_prep_kernel, dim3((unsigned)cdiv(items, 4)), dim3(256), 0, s, x, xh, xl, xs,
+    __bf16* sh = static_cast<__bf16*>(align256(xl + (size_t)M * K));
+    __bf16* sl = static_cast<__bf16*>(align256(sh + (size_t)M * groups));
+    const int64_t items = M * (K / 8);
+    hipLaunchKernelGGL(affine_prep_kernel, dim3((unsigned)cdiv(items, 256)), dim3(256), 0, s, x, xh, xl, sh, sl,
                        (int)M, (int)K, gs);
     MfmaParams mp{};
     mp.xh = xh;
     mp.xl = xl;
-    mp.xsum = xs;
+    mp.sh = sh;
+    mp.sl = sl;
     mp.q = q;
     mp.scales = scales;
     mp.biases = biases;
@@ -357,7 +364,7 @@ qg_status qmm_affine_t(const float* x, const uint8_t* q, const float* scales, co
     mp.gs = gs;
     mp.tiles_m = (int)cdiv(M, kBM);
     mp.tiles_n = (int)cdiv(N, kBN);
-    hipLaunchKernelGGL(affine_mfma_kernel, dim3((unsigned)(mp.tiles_m * mp.tiles_n)), dim3(256), 0, s, mp);
+    hipLaunchKernelGGL(affine_mfma_kernel, dim3((unsigned)(mp.tiles_m * mp.tiles_n)), dim3(512), 0, s, mp);
     const qg_status ls = launch_status(op);
     e = hipFreeAsync(scratch, s);
     if (ls == QG_OK && e != hipSuccess) {

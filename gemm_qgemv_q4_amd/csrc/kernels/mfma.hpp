@@ -8,55 +8,79 @@
 // x_hi = bf16(x) and x_lo = bf16(x - x_hi), so x_hi + x_lo carries 16
 // significant bits (relative error <= 2^-18); bf16 x bf16 products are exact
 // in the f32 MFMA accumulator.  Each group's partial product P_g = (x_hi +
-// x_lo) . q is accumulated by two v_mfma_f32_16x16x32_bf16 per 32 columns,
-// then scaled in f32: acc += s * P_g and acc += b * X_g.  This keeps
-// |y - y_exact| well inside 1e-5 * sum|x w| (a single bf16 or f16 operand
-// does not).
+// x_lo) . q is accumulated by two v_mfma_f32_16x16x32_bf16 per 32 columns and
+// scaled in f32 (acc += s * P_g).  The bias term is a product over the group
+// index with X and b both split into bf16 hi + lo (the lo*lo part, below
+// 2^-16 relative, is dropped).  Together this keeps |y - y_exact| well inside
+// 1e-5 * sum|x w|, which a single bf16 or f16 operand does not.
 //
 // Kernels:
-//   affine_prep_kernel : x [M,K] f32 -> x_hi, x_lo [M,K] bf16 and X [M, K/gs] f32.
-//   affine_mfma_kernel : 128x128 output tile per 256-thread workgroup (2x2
-//       waves of 64x64 = 4x4 MFMA tiles), K in stages of 64 staged through
-//       LDS (rows padded to 144 bytes so the 16-byte operand reads of a wave
-//       are bank-conflict free).  Workgroup ids are remapped so the tiles of
-//       one weight column block land on the same XCD (shared L2).
+//   affine_prep_kernel : x [M,K] f32 -> x_hi, x_lo [M,K] bf16 and X [M, K/gs]
+//                        as bf16 hi, lo.
+//   affine_mfma_kernel : 128x128 output tile per 256-thread workgroup.
 #pragma once
 #include "common.hpp"
 
 namespace qg {
 
 // ---------------------------------------------------------------------------
-// x -> (x_hi, x_lo) bf16 and per-group sums.  One wave per (row, group); the
-// lanes walk the group with stride 64 and the group sum is a fixed butterfly.
+// x -> (x_hi, x_lo) bf16 and per-group sums X_g, the sums also split into
+// bf16 hi/lo (they feed the bias product on the matrix cores).  Each thread
+// converts 8 consecutive elements; the gs/8 threads of a group (gs <= 512)
+// combine their partial sums with a fixed xor butterfly.
 __global__ void __launch_bounds__(256) affine_prep_kernel(const float* __restrict__ x,
                                                           __bf16* __restrict__ xh,
                                                           __bf16* __restrict__ xl,
-                                                          float* __restrict__ xsum,
+                                                          __bf16* __restrict__ sh,
+                                                          __bf16* __restrict__ sl,
                                                           int m_rows, int k, int gs) {
-  const int groups = k / gs;
-  const long long item = (long long)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-  if (item >= (long long)m_rows * groups) return;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int m = (int)(item / groups);
-  const int g = (int)(item - (long long)m * groups);
-  const size_t base = (size_t)m * k + (size_t)g * gs;
-  float s = 0.0f;
-  for (int i = lane; i < gs; i += kWave) {
-    const float v = x[base + i];
-    const __bf16 h = (__bf16)v;
-    const __bf16 l = (__bf16)(v - (float)h);
-    xh[base + i] = h;
-    xl[base + i] = l;
-    s += v;
+  const int per_row = k / 8;
+  const int item = blockIdx.x * blockDim.x + threadIdx.x;  // < 2^31: M*K/8 is checked on the host
+  const bool ok = item < m_rows * per_row;
+  const int m = ok ? item / per_row : 0;
+  const int c8 = ok ? item - m * per_row : 0;
+  const size_t base = (size_t)m * k + (size_t)c8 * 8;
+  float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (ok) {
+    const bool vec = (reinterpret_cast<uintptr_t>(x + base) & 15u) == 0;
+    if (vec) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(x + base);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(x + base + 4);
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = x[base + i];
+    }
   }
-  s = wave_sum_xor(s, kWave);
-  if (lane == 0) xsum[(size_t)m * groups + g] = s;
+  bf16x8 hv, lv;
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const __bf16 h = (__bf16)v[i];
+    hv[i] = h;
+    lv[i] = (__bf16)(v[i] - (float)h);
+    s += v[i];
+  }
+  if (ok) {
+    *reinterpret_cast<bf16x8*>(xh + base) = hv;
+    *reinterpret_cast<bf16x8*>(xl + base) = lv;
+  }
+  const int lanes = gs / 8;  // threads per group (4..64)
+  for (int off = 1; off < lanes; off <<= 1) s += __shfl_xor(s, off, kWave);
+  if (ok && (c8 % lanes) == 0) {
+    const int groups = k / gs;
+    const size_t gi = (size_t)m * groups + c8 / lanes;
+    const __bf16 h = (__bf16)s;
+    sh[gi] = h;
+    sl[gi] = (__bf16)(s - (float)h);
+  }
 }
 
 struct MfmaParams {
   const __bf16* xh;      // [M, K]
   const __bf16* xl;      // [M, K]
-  const float* xsum;     // [M, K/gs]
+  const __bf16* sh;      // [M, K/gs] group sums of x, hi
+  const __bf16* sl;      // [M, K/gs] group sums of x, lo
   const uint8_t* q;      // [N, K]
   const float* scales;   // [N, K/gs]
   const float* biases;   // [N, K/gs]
@@ -67,20 +91,25 @@ struct MfmaParams {
 
 constexpr int kBM = 128, kBN = 128, kBK = 64;
 constexpr int kPitch = kBK + 8;  // bf16 elements per LDS row (144 bytes)
+constexpr int kTileElems = kBM * kPitch;
 
+struct StageRegs { u32x4 ah[2], al[2], b; };
+
+// One 32-wide K step of the wave's 64x64 sub-tile: P += (A_hi + A_lo) * B.
+// All 16 hi products are issued before the 16 lo products, so consecutive
+// MFMAs never wait on each other's accumulator.
 template <bool FIRST>
 __device__ __forceinline__ void mfma_substep(const __bf16* sAh, const __bf16* sAl, const __bf16* sB,
-                                             int sub, int wm, int wn, int lane, f32x4 (&P)[4][4]) {
+                                             int kq, int wm, int wn, int lane, f32x4 (&P)[4][4]) {
   const int r16 = lane & 15;
-  const int kq = (lane >> 4) * 8 + sub * 32;
+  const int kk = (lane >> 4) * 8 + kq;
   bf16x8 bfrag[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    bfrag[j] = *(const bf16x8*)(sB + (wn * 64 + j * 16 + r16) * kPitch + kq);
+    bfrag[j] = *(const bf16x8*)(sB + (wn * 64 + j * 16 + r16) * kPitch + kk);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const bf16x8 ah = *(const bf16x8*)(sAh + (wm * 64 + i * 16 + r16) * kPitch + kq);
-    const bf16x8 al = *(const bf16x8*)(sAl + (wm * 64 + i * 16 + r16) * kPitch + kq);
+    const bf16x8 ah = *(const bf16x8*)(sAh + (wm * 64 + i * 16 + r16) * kPitch + kk);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if constexpr (FIRST) {
@@ -89,27 +118,40 @@ __device__ __forceinline__ void mfma_substep(const __bf16* sAh, const __bf16* sA
       } else {
         P[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bfrag[j], P[i][j], 0, 0, 0);
       }
-      P[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bfrag[j], P[i][j], 0, 0, 0);
     }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x8 al = *(const bf16x8*)(sAl + (wm * 64 + i * 16 + r16) * kPitch + kk);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      P[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bfrag[j], P[i][j], 0, 0, 0);
   }
 }
 
-__global__ void __launch_bounds__(256) affine_mfma_kernel(MfmaParams p) {
-  __shared__ __attribute__((aligned(16))) __bf16 sAh[kBM * kPitch];
-  __shared__ __attribute__((aligned(16))) __bf16 sAl[kBM * kPitch];
-  __shared__ __attribute__((aligned(16))) __bf16 sB[kBN * kPitch];
-  __shared__ float sS[2][kBN];
-  __shared__ float sBi[2][kBN];
-  __shared__ __attribute__((aligned(16))) float sX[2][kBM];
+// 128x128 output tile per 512-thread workgroup: 8 waves, two per SIMD.  Waves
+// w and w+4 own the same 64x64 sub-tile (2x2 sub-tiles, 4x4 MFMA tiles each)
+// and split every 64-wide K stage: wave half 0 takes columns 0..31, half 1
+// columns 32..63.  Their partial sums meet in LDS at the end.  K runs through
+// two LDS buffers; each stage's global loads are issued one stage ahead into
+// registers (one barrier per stage).  When a group of gs columns is complete,
+// a wave scales its partial product: acc += s[n, g] * P.  The bias term
+// sum_g b[n,g] * X_g[m] is one more small matrix product at the end, with
+// both factors split into bf16 hi + lo (three MFMAs per 32 groups).
+__global__ void __launch_bounds__(512) affine_mfma_kernel(MfmaParams p) {
+  __shared__ __attribute__((aligned(16))) __bf16 sA[2][2 * kTileElems];  // [buf][hi | lo]
+  __shared__ __attribute__((aligned(16))) __bf16 sB[2][kTileElems];
+  __shared__ float sS[2][2][kBN];  // [buf][group in stage][n]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
+  const int kh = wid >> 2;            // which 32-column half of each stage
+  const int wm = (wid >> 1) & 1, wn = wid & 1;
 
-  // Tile order: tiles of one column block (same weights) are consecutive, and
-  // consecutive ids are spread over the 8 XCDs by the dispatcher, so give each
-  // XCD a contiguous range of tiles when the count allows it.
+  // Tiles of one column block (same weights) are consecutive and the
+  // dispatcher spreads consecutive ids over the 8 XCDs, so give each XCD a
+  // contiguous range of tiles when the count allows it.
   const int total = p.tiles_m * p.tiles_n;
   int tile = blockIdx.x;
   if ((total & 7) == 0) tile = (tile & 7) * (total >> 3) + (tile >> 3);
@@ -117,6 +159,8 @@ __global__ void __launch_bounds__(256) affine_mfma_kernel(MfmaParams p) {
   const int tn = tile / p.tiles_m;
   const int m0 = tm * kBM, n0 = tn * kBN;
   const int groups = p.k / p.gs;
+  const int stages = p.k / kBK;
+  const int ng = p.gs < kBK ? kBK / p.gs : 1;  // groups per stage: 2 when gs == 32
 
   f32x4 acc[4][4], P[4][4];
 #pragma unroll
@@ -127,122 +171,171 @@ __global__ void __launch_bounds__(256) affine_mfma_kernel(MfmaParams p) {
       P[i][j] = acc[i][j];
     }
 
-  // global -> register staging of one K stage
-  u32x4 ra_h[4], ra_l[4], rb[2];
-  auto load_stage = [&](int k0) {
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int c = tid + it * 256;  // 1024 chunks of 8 bf16
-      const int row = c >> 3, kc = c & 7;
-      const int gm = m0 + row;
-      u32x4 vh = {0u, 0u, 0u, 0u}, vl = {0u, 0u, 0u, 0u};
-      if (gm < p.m) {
-        const size_t off = (size_t)gm * p.k + k0 + kc * 8;
-        vh = *(const u32x4*)(p.xh + off);
-        vl = *(const u32x4*)(p.xl + off);
-      }
-      ra_h[it] = vh;
-      ra_l[it] = vl;
-    }
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int c = tid + it * 256;  // 512 chunks of 16 codes
-      const int n = c >> 2, kc = c & 3;
-      const int gn = n0 + n;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (gn < p.n) v = *(const u32x4*)(p.q + (size_t)gn * p.k + k0 + kc * 16);
-      rb[it] = v;
-    }
+  // Chunks this thread moves per stage: 8-element pieces of x_hi/x_lo rows
+  // a_row0 and a_row0 + 64, and 16 codes of weight row b_n.  Offsets are 32-bit
+  // element offsets from the uniform base pointers (M*K and N*K are below 2^31,
+  // checked on the host).  Rows past M or N read nothing (zeros).
+  const int a_row0 = tid >> 3, a_kc = tid & 7;
+  const int b_n = tid >> 2, b_kc = tid & 3;
+  const bool a_ok0 = m0 + a_row0 < p.m, a_ok1 = m0 + a_row0 + 64 < p.m;
+  const bool b_ok = n0 + b_n < p.n;
+  const uint32_t a_off0 = (uint32_t)(a_ok0 ? m0 + a_row0 : 0) * (uint32_t)p.k + (uint32_t)(a_kc * 8);
+  const uint32_t a_off1 = (uint32_t)(a_ok1 ? m0 + a_row0 + 64 : 0) * (uint32_t)p.k + (uint32_t)(a_kc * 8);
+  const uint32_t b_off = (uint32_t)(b_ok ? n0 + b_n : 0) * (uint32_t)p.k + (uint32_t)(b_kc * 16);
+  const uint32_t s_off = (uint32_t)(n0 + (tid & 127) < p.n ? n0 + (tid & 127) : 0) * (uint32_t)groups;
+
+  auto load = [&](int st, StageRegs& r) {
+    const uint32_t k0 = (uint32_t)(st * kBK);
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    r.ah[0] = a_ok0 ? *(const u32x4*)(p.xh + (a_off0 + k0)) : z;
+    r.al[0] = a_ok0 ? *(const u32x4*)(p.xl + (a_off0 + k0)) : z;
+    r.ah[1] = a_ok1 ? *(const u32x4*)(p.xh + (a_off1 + k0)) : z;
+    r.al[1] = a_ok1 ? *(const u32x4*)(p.xl + (a_off1 + k0)) : z;
+    r.b = b_ok ? *(const u32x4*)(p.q + (b_off + k0)) : z;
   };
-  auto store_stage = [&](int k0) {
+  auto store = [&](int st, const StageRegs& r, int buf) {
+    __bf16* ah = sA[buf];
+    __bf16* al = sA[buf] + kTileElems;
+    *(u32x4*)(ah + a_row0 * kPitch + a_kc * 8) = r.ah[0];
+    *(u32x4*)(al + a_row0 * kPitch + a_kc * 8) = r.al[0];
+    *(u32x4*)(ah + (a_row0 + 64) * kPitch + a_kc * 8) = r.ah[1];
+    *(u32x4*)(al + (a_row0 + 64) * kPitch + a_kc * 8) = r.al[1];
+    // 16 codes -> 16 bf16 (exact: integers below 256)
+    bf16x8 lo, hi;
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int c = tid + it * 256;
-      const int row = c >> 3, kc = c & 7;
-      *(u32x4*)(sAh + row * kPitch + kc * 8) = ra_h[it];
-      *(u32x4*)(sAl + row * kPitch + kc * 8) = ra_l[it];
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t wlo = r.b[e >> 2], whi = r.b[2 + (e >> 2)];
+      lo[e] = (__bf16)(float)((wlo >> (8 * (e & 3))) & 0xFFu);
+      hi[e] = (__bf16)(float)((whi >> (8 * (e & 3))) & 0xFFu);
     }
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int c = tid + it * 256;
-      const int n = c >> 2, kc = c & 3;
-      // 16 codes -> 16 bf16 (exact: integers below 256)
-      bf16x8 lo, hi;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t wlo = rb[it][e >> 2], whi = rb[it][2 + (e >> 2)];
-        lo[e] = (__bf16)(float)((wlo >> (8 * (e & 3))) & 0xFFu);
-        hi[e] = (__bf16)(float)((whi >> (8 * (e & 3))) & 0xFFu);
-      }
-      *(bf16x8*)(sB + n * kPitch + kc * 16) = lo;
-      *(bf16x8*)(sB + n * kPitch + kc * 16 + 8) = hi;
-    }
-    // scales / biases / x sums of the group(s) this stage touches
-    const int g0 = k0 / p.gs;
-    const int ng = p.gs < kBK ? kBK / p.gs : 1;  // 2 when gs == 32
-    for (int i = tid; i < ng * kBN; i += 256) {
-      const int gi = i / kBN, n = i - gi * kBN;
-      const int gn = n0 + n;
-      float sv = 0.0f, bv = 0.0f;
-      if (gn < p.n) {
-        sv = p.scales[(size_t)gn * groups + g0 + gi];
-        bv = p.biases[(size_t)gn * groups + g0 + gi];
-      }
-      sS[gi][n] = sv;
-      sBi[gi][n] = bv;
-    }
-    for (int i = tid; i < ng * kBM; i += 256) {
-      const int gi = i / kBM, r = i - gi * kBM;
-      const int gm = m0 + r;
-      sX[gi][r] = gm < p.m ? p.xsum[(size_t)gm * groups + g0 + gi] : 0.0f;
-    }
+    *(bf16x8*)(sB[buf] + b_n * kPitch + b_kc * 16) = lo;
+    *(bf16x8*)(sB[buf] + b_n * kPitch + b_kc * 16 + 8) = hi;
+    const int g0 = st * kBK / p.gs;
+    if (tid < ng * kBN) sS[buf][tid >> 7][tid & 127] = p.scales[s_off + (uint32_t)(g0 + (tid >> 7))];
   };
-  auto epilogue = [&](int gi) {
+  auto scale_into_acc = [&](int buf, int gi) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int col = wn * 64 + j * 16 + (lane & 15);
-      const float sv = sS[gi][col], bv = sBi[gi][col];
+      const float sv = sS[buf][gi][wn * 64 + j * 16 + (lane & 15)];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(sv, P[i][j][e], acc[i][j][e]);
+    }
+  };
+  // this wave's 32-column half of stage st
+  auto compute = [&](int st, int buf) {
+    const __bf16* ah = sA[buf];
+    const __bf16* al = sA[buf] + kTileElems;
+    if (p.gs == 32) {  // the half is a whole group
+      mfma_substep<true>(ah, al, sB[buf], kh * 32, wm, wn, lane, P);
+      scale_into_acc(buf, kh);
+      return;
+    }
+    const int c0 = st * kBK;
+    if (c0 % p.gs == 0) mfma_substep<true>(ah, al, sB[buf], kh * 32, wm, wn, lane, P);
+    else mfma_substep<false>(ah, al, sB[buf], kh * 32, wm, wn, lane, P);
+    if ((c0 + kBK) % p.gs == 0) scale_into_acc(buf, 0);
+  };
+
+  StageRegs rg;
+  load(0, rg);
+  store(0, rg, 0);
+  __syncthreads();
+  for (int st = 0; st < stages; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < stages) load(st + 1, rg);
+    compute(st, buf);
+    if (st + 1 < stages) store(st + 1, rg, buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- combine the two K halves: half 1 hands its partial sums to half 0
+  float* red = reinterpret_cast<float*>(&sA[0][0]);  // 4 sub-tiles x 64 x 64 floats = 64 KB
+  float* mine = red + (size_t)(wm * 2 + wn) * 4096;
+  if (kh == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *(f32x4*)(mine + ((i * 4 + j) * 64 + lane) * 4) = acc[i][j];
+  }
+  __syncthreads();
+  if (kh == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 o = *(const f32x4*)(mine + ((i * 4 + j) * 64 + lane) * 4);
+        acc[i][j] += o;
+      }
+  }
+  __syncthreads();
+
+  // ---- bias term: acc += X[m, g] * b[n, g] over all groups, as a K = groups
+  // product on the matrix cores with X and b split into bf16 hi + lo
+  for (int g0 = 0; g0 < groups; g0 += 32) {
+    __bf16* xh_s = sA[1];                // [128 m][32 g], pitch kPitch
+    __bf16* xl_s = sA[1] + kTileElems;
+    __bf16* bh_s = sB[0];                // [128 n][32 g]
+    __bf16* bl_s = sB[1];
+    for (int i = tid; i < kBM * 32; i += 512) {
+      const int r = i >> 5, g = i & 31;
+      const int gm = m0 + r, gn = n0 + r, gg = g0 + g;
+      __bf16 xhv = (__bf16)0.0f, xlv = (__bf16)0.0f, bhv = (__bf16)0.0f, blv = (__bf16)0.0f;
+      if (gg < groups) {
+        if (gm < p.m) {
+          xhv = p.sh[(size_t)gm * groups + gg];
+          xlv = p.sl[(size_t)gm * groups + gg];
+        }
+        if (gn < p.n) {
+          const float b = p.biases[(size_t)gn * groups + gg];
+          bhv = (__bf16)b;
+          blv = (__bf16)(b - (float)bhv);
+        }
+      }
+      xh_s[r * kPitch + g] = xhv;
+      xl_s[r * kPitch + g] = xlv;
+      bh_s[r * kPitch + g] = bhv;
+      bl_s[r * kPitch + g] = blv;
+    }
+    __syncthreads();
+    if (kh == 0) {
+      const int r16 = lane & 15;
+      const int kk = (lane >> 4) * 8;
+      bf16x8 bh[4], bl[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bh[j] = *(const bf16x8*)(bh_s + (wn * 64 + j * 16 + r16) * kPitch + kk);
+        bl[j] = *(const bf16x8*)(bl_s + (wn * 64 + j * 16 + r16) * kPitch + kk);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const f32x4 xs4 = *(const f32x4*)(&sX[gi][wm * 64 + i * 16 + (lane >> 4) * 4]);
+        const bf16x8 ah = *(const bf16x8*)(xh_s + (wm * 64 + i * 16 + r16) * kPitch + kk);
+        const bf16x8 al = *(const bf16x8*)(xl_s + (wm * 64 + i * 16 + r16) * kPitch + kk);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float a = acc[i][j][e];
-          a = __builtin_fmaf(sv, P[i][j][e], a);
-          a = __builtin_fmaf(bv, xs4[e], a);
-          acc[i][j][e] = a;
+        for (int j = 0; j < 4; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh[j], acc[i][j], 0, 0, 0);
         }
       }
     }
-  };
-
-  load_stage(0);
-  for (int k0 = 0; k0 < p.k; k0 += kBK) {
     __syncthreads();
-    store_stage(k0);
-    __syncthreads();
-    if (k0 + kBK < p.k) load_stage(k0 + kBK);
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int kk = k0 + sub * 32;  // first column of this 32-wide step
-      const bool first = (kk % p.gs) == 0;
-      if (first) mfma_substep<true>(sAh, sAl, sB, sub, wm, wn, lane, P);
-      else mfma_substep<false>(sAh, sAl, sB, sub, wm, wn, lane, P);
-      if (((kk + 32) % p.gs) == 0) epilogue(p.gs < kBK ? sub : 0);
-    }
   }
 
   // store: lane holds rows 4*(lane/16)+e, column lane%16 of each 16x16 tile
+  if (kh == 0) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int gm = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + e;
-        const int gn = n0 + wn * 64 + j * 16 + (lane & 15);
-        if (gm < p.m && gn < p.n) p.y[(size_t)gm * p.n + gn] = acc[i][j][e];
-      }
+        for (int e = 0; e < 4; ++e) {
+          const int gm = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + e;
+          const int gn = n0 + wn * 64 + j * 16 + (lane & 15);
+          if (gm < p.m && gn < p.n) p.y[(size_t)gm * p.n + gn] = acc[i][j][e];
+        }
+  }
 }
 
 }  // namespace qg

@@ -93,11 +93,11 @@ qg_status qgemv_dual_q4_0(const void* w_a, const void* w_b, const float* x,
  *   x : [M, K] f32;  q : [N, K] u8 codes (any value 0..255);
  *   scales, biases : [N, K/group_size] f32;  y : [M, N] f32.
  *   group_size : power of two in [2, 1024], K % group_size == 0.
- * For M >= qg_get_mfma_min_m() (and group_size >= 32, K % 64 == 0) the
- * product runs on the matrix cores; x is split into two bf16 terms so the
- * f32 tolerance above still holds.  That path takes stream-ordered scratch
- * (hipMallocAsync / hipFreeAsync on `stream`) of M*K*4 + M*(K/group_size)*4
- * bytes.
+ * For M >= qg_get_mfma_min_m() (and 32 <= group_size <= 512, K % 64 == 0,
+ * q 16-byte aligned) the product runs on the matrix cores; x is split into
+ * two bf16 terms so the f32 tolerance above still holds.  That path takes
+ * stream-ordered scratch (hipMallocAsync / hipFreeAsync on `stream`) of
+ * M*K*4 + M*(K/group_size)*4 bytes (plus alignment).
  * Errors: M, N, K < 1; bad group_size; K % group_size != 0; null pointers;
  *         misaligned f32 pointers.
  */

@@ -174,7 +174,8 @@ def force_mfma(lib):
 
 @pytest.mark.parametrize("m,n,k,gs", [
     (1, 16, 64, 64), (16, 16, 64, 32), (128, 128, 256, 64), (130, 129, 512, 64),
-    (77, 300, 1024, 128), (256, 64, 2048, 1024), (33, 257, 192, 32), (5, 9, 128, 64),
+    (77, 300, 1024, 128), (256, 64, 2048, 512), (40, 70, 1024, 256), (33, 257, 192, 32), (5, 9, 128, 64),
+    (3, 11, 2048, 1024),  # group_size above 512: takes the GEMV path even when forced
 ])
 def test_affine_mfma_matches_oracle(lib, force_mfma, m, n, k, gs):
     x, q, s, b = synth.affine_case(5000 + m + n + k + gs, m, n, k, gs)
