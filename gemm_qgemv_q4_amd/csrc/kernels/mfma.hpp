@@ -17,7 +17,9 @@
 // Kernels:
 //   affine_prep_kernel : x [M,K] f32 -> x_hi, x_lo [M,K] bf16 and X [M, K/gs]
 //                        as bf16 hi, lo.
-//   affine_mfma_kernel : 128x128 output tile per 256-thread workgroup.
+//   affine_mfma_kernel : 128x128 output tile per 512-thread workgroup (eight
+//                        waves: 2x2 sub-tiles of 64x64, each shared by two
+//                        waves that split every 64-wide K stage).
 #pragma once
 #include "common.hpp"
 
