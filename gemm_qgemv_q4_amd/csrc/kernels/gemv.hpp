@@ -260,7 +260,8 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams p) {
   constexpr int NE4 = CH / 4;
   constexpr int P = kWave / L;
   constexpr bool SUMS = FmtTraits<FMT>::SUMS;
-  constexpr int SB = 4;  // float4s of x per thread per staging batch
+  constexpr int SB = 4;     // float4s of x per thread per staging batch
+  constexpr int XPRE = 4;   // float4 registers for x loaded ahead of the first weights
   using Chunk = typename ChunkOf<FMT>::T;
 
   extern __shared__ f32x4 smem[];
@@ -300,40 +301,60 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams p) {
   // each 32-element half (8 consecutive float4s = 8 consecutive lanes).  Index
   // math is shifts only (CH is a power of two); loops are uniform so every lane
   // takes part in the shuffles.
+  auto xload = [&](int m, int j, int k0, int n4) -> f32x4 {
+    f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (m < p.m_rows && j < n4) {
+      const float* xrow = p.x + (size_t)m * p.k + k0;
+      if (x_vec) v = *reinterpret_cast<const f32x4*>(xrow + 4 * j);
+      else v = f32x4{xrow[4 * j], xrow[4 * j + 1], xrow[4 * j + 2], xrow[4 * j + 3]};
+    }
+    return v;
+  };
+  auto xstore = [&](int m, int j, int n4, const f32x4& v) {
+    const int t = j / NE4;   // chunk (NE4 is a power of two)
+    const int e4 = j % NE4;  // float4 within the chunk
+    if (j < n4) xs[(m * NE4 + e4) * ctp + t] = v;
+    if constexpr (SUMS) {
+      float sm = ((v.x + v.y) + v.z) + v.w;
+      sm += __shfl_xor(sm, 1, kWave);
+      sm += __shfl_xor(sm, 2, kWave);
+      sm += __shfl_xor(sm, 4, kWave);
+      if (j < n4 && (e4 & 7) == 0) xsum[(m * ct_max + t) * 2 + (e4 >> 3)] = sm;
+    }
+  };
   auto stage = [&](int k0, int ktile) {
     const int n4 = ktile >> 2;
     const int step = SB * (int)blockDim.x;
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      const float* xrow = p.x + (size_t)m * p.k + k0;
-      const bool live = m < p.m_rows;
       for (int j0 = 0; j0 < n4; j0 += step) {
         f32x4 v[SB];
 #pragma unroll
-        for (int u = 0; u < SB; ++u) {
-          const int j = j0 + u * (int)blockDim.x + tid;
-          v[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-          if (live && j < n4) {
-            if (x_vec) v[u] = *reinterpret_cast<const f32x4*>(xrow + 4 * j);
-            else v[u] = f32x4{xrow[4 * j], xrow[4 * j + 1], xrow[4 * j + 2], xrow[4 * j + 3]};
-          }
-        }
+        for (int u = 0; u < SB; ++u) v[u] = xload(m, j0 + u * (int)blockDim.x + tid, k0, n4);
 #pragma unroll
-        for (int u = 0; u < SB; ++u) {
-          const int j = j0 + u * (int)blockDim.x + tid;
-          const int t = j / NE4;        // chunk (NE4 is a power of two)
-          const int e4 = j % NE4;       // float4 within the chunk
-          if (j < n4) xs[(m * NE4 + e4) * ctp + t] = v[u];
-          if constexpr (SUMS) {
-            float sm = ((v[u].x + v[u].y) + v[u].z) + v[u].w;
-            sm += __shfl_xor(sm, 1, kWave);
-            sm += __shfl_xor(sm, 2, kWave);
-            sm += __shfl_xor(sm, 4, kWave);
-            if (j < n4 && (e4 & 7) == 0) xsum[(m * ct_max + t) * 2 + (e4 >> 3)] = sm;
-          }
-        }
+        for (int u = 0; u < SB; ++u) xstore(m, j0 + u * (int)blockDim.x + tid, n4, v[u]);
       }
     }
+    __syncthreads();
+  };
+  // First staging of a single x row whose share per thread fits in XPRE
+  // registers: the x loads are issued before the first weight loads, so
+  // writing x to LDS waits only for x (loads retire in order) and the weights
+  // stay in flight.  (For MT > 1 the extra registers cost more than it saves.)
+  constexpr int XU = XPRE / MT > 0 ? XPRE / MT : 1;
+  auto stage_x_first = [&](int ktile, Chunk (&dst)[NW][R], const int (&rws)[R], int tg) {
+    const int n4 = ktile >> 2;
+    f32x4 v[MT][XU];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int u = 0; u < XU; ++u) v[m][u] = xload(m, u * (int)blockDim.x + tid, 0, n4);
+    fetch(dst, rws, tg);
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int u = 0; u < XU; ++u)
+        if (u * (int)blockDim.x < n4) xstore(m, u * (int)blockDim.x + tid, n4, v[m][u]);
     __syncthreads();
   };
 
@@ -363,9 +384,13 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams p) {
       const int ktile = min(p.kt, p.k - k0);
       const int ct = ktile / CH;
       if (!persistent || !staged) {
-        if (staged) __syncthreads();  // the previous tile's readers are done
-        else fetch(cur, rows, tg0);   // first weights in flight while x is staged
-        stage(k0, ktile);
+        if (MT == 1 && !staged && k0 == 0 && (ktile >> 2) <= XU * (int)blockDim.x) {
+          if constexpr (MT == 1) stage_x_first(ktile, cur, rows, tg0);
+        } else {
+          if (staged) __syncthreads();  // the previous tile's readers are done
+          else fetch(cur, rows, tg0);   // first weights in flight while x is staged
+          stage(k0, ktile);
+        }
         staged = true;
       }
       for (int t = lc; t < ct; t += L) {
