@@ -315,10 +315,7 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams p) {
     const int e4 = j % NE4;  // float4 within the chunk
     if (j < n4) xs[(m * NE4 + e4) * ctp + t] = v;
     if constexpr (SUMS) {
-      float sm = ((v.x + v.y) + v.z) + v.w;
-      sm += __shfl_xor(sm, 1, kWave);
-      sm += __shfl_xor(sm, 2, kWave);
-      sm += __shfl_xor(sm, 4, kWave);
+      const float sm = group_sum(((v.x + v.y) + v.z) + v.w, 8);
       if (j < n4 && (e4 & 7) == 0) xsum[(m * ct_max + t) * 2 + (e4 >> 3)] = sm;
     }
   };
