@@ -26,6 +26,18 @@ What it computes, and where the pages define it:
 * ``qkv_split_f32`` copies columns ``[0,q_sp)``, ``[q_sp,q_sp+k_sp)`` and
   ``[q_sp+k_sp, qkv_ch)`` of each token row into q, k, v
   (mlx-native ``qkv_split.rs``, module doc and ``dispatch_qkv_split_f32``).
+* Packed 4-bit affine codes: eight codes per u32 word, the code of element
+  ``8*kp + j`` in bits ``4j .. 4j+3`` of word ``kp`` (mlx-native
+  ``qmm_affine.rs``, the ``pack_b4_to_u32`` helper of its tests); the product
+  is the affine one of the unpacked codes (the byte-identity test of the
+  packed kernel against the unpacked one on the same page).
+* Multi-part projections: several weight tensors of one format share x and
+  each writes a disjoint column slice of one output (ferrum-kernels
+  ``q4_k_gemv_v2.rs``, doc of ``dispatch_gemv_q4k_v2_offset``: the parts of a
+  fused projection written into slices of a shared output buffer).
+* The fused projection + split: the affine product of a fused q|k|v weight,
+  split as ``qkv_split_f32`` splits it (mlx-native ``qkv_split.rs``, module
+  doc: the split follows the fused-QKV projection).
 
 Pins (tests/test_oracle_pins.py) tie each function to hand-decoded blocks
 under tests/golden/, closed forms, exact rational brute force and the
@@ -39,6 +51,8 @@ __all__ = [
     "f16_bits_to_f64", "decode_q4_0", "decode_q4_k", "decode_affine",
     "gemv_f64", "abs_bound", "qgemv_q4_0", "qgemv_q4_k", "qgemv_dual_q4_0",
     "qmm_affine_t", "qkv_split_f32", "q4k_scale_min",
+    "unpack_b4_u32", "decode_affine_b4", "qmm_affine_t_packed",
+    "qgemv_multi", "qmm_affine_t_qkv",
 ]
 
 
@@ -162,3 +176,44 @@ def qkv_split_f32(qkv: np.ndarray, seq: int, q_sp: int, k_sp: int, v_sp: int):
     return (np.ascontiguousarray(a[:, :q_sp]),
             np.ascontiguousarray(a[:, q_sp:q_sp + k_sp]),
             np.ascontiguousarray(a[:, q_sp + k_sp:]))
+
+
+def unpack_b4_u32(w_packed: np.ndarray, n: int, k: int) -> np.ndarray:
+    """u32 words ``[n, k/8]`` -> u8 codes ``[n, k]``: element ``8*kp + j`` is
+    bits ``4j .. 4j+3`` of word ``kp`` (low nibble first)."""
+    assert k % 8 == 0
+    wp = np.asarray(w_packed, dtype=np.uint32).reshape(n, k // 8)
+    out = np.empty((n, k // 8, 8), dtype=np.uint8)
+    for j in range(8):
+        out[..., j] = (wp >> np.uint32(4 * j)) & np.uint32(0xF)
+    return out.reshape(n, k)
+
+
+def decode_affine_b4(w_packed: np.ndarray, scales: np.ndarray, biases: np.ndarray,
+                     n: int, k: int, group_size: int) -> np.ndarray:
+    """Packed 4-bit affine weights -> f64 ``w = q * s + b``."""
+    return decode_affine(unpack_b4_u32(w_packed, n, k), scales, biases, n, k, group_size)
+
+
+def qmm_affine_t_packed(x: np.ndarray, w_packed: np.ndarray, scales: np.ndarray,
+                        biases: np.ndarray, m: int, n: int, k: int, group_size: int) -> np.ndarray:
+    """f32 ``y = x * (s*q + b)^T`` with the codes packed eight per u32."""
+    return gemv_f64(decode_affine_b4(w_packed, scales, biases, n, k, group_size),
+                    np.asarray(x).reshape(m, k))
+
+
+def qgemv_multi(decode, parts, x: np.ndarray, m: int, k: int) -> np.ndarray:
+    """Multi-part projection: ``parts`` is a list of ``(w_p, n_p)`` in one
+    format, ``decode(w, n, k)`` its decoder.  Returns f32 ``y[m, sum n_p]``
+    with part p in columns ``[sum_{q<p} n_q, sum_{q<=p} n_q)``."""
+    xm = np.asarray(x).reshape(m, k)
+    return np.concatenate([gemv_f64(decode(w, n, k), xm) for w, n in parts], axis=1)
+
+
+def qmm_affine_t_qkv(x: np.ndarray, q: np.ndarray, scales: np.ndarray, biases: np.ndarray,
+                     m: int, k: int, group_size: int, q_sp: int, k_sp: int, v_sp: int):
+    """The affine product of a fused ``[q_sp + k_sp + v_sp, k]`` weight, split
+    into contiguous q ``[m, q_sp]``, k ``[m, k_sp]``, v ``[m, v_sp]``."""
+    n = q_sp + k_sp + v_sp
+    y = qmm_affine_t(x, q, scales, biases, m, n, k, group_size)
+    return qkv_split_f32(y, m, q_sp, k_sp, v_sp)

@@ -17,6 +17,9 @@ Encodings written here (byte layouts; the readings are stated in the design doc):
 * MLX-style affine groups -- u8 codes ``[N, K]`` plus f32 ``scales`` and
   ``biases`` ``[N, K/group_size]`` (mlx-native ``qmm_affine.rs``, CPU oracle in
   the tests module).
+* Packed 4-bit affine codes -- u32 ``[N, K/8]``, the code of element
+  ``8*kp + j`` in bits ``4j .. 4j+3`` of word ``kp`` (mlx-native
+  ``qmm_affine.rs``, the ``pack_b4_to_u32`` test helper).
 
 Quantizers are plain input generators: any code assignment is a valid input,
 so their rounding choices do not affect parity.
@@ -164,6 +167,26 @@ def affine_case(seed: int, m: int, n: int, k: int, group_size: int, code_max: in
     return x, q, s, b
 
 
+def pack_b4_u32(codes: np.ndarray) -> np.ndarray:
+    """u8 codes ``[N, K]`` (each 0..15, K % 8 == 0) -> u32 ``[N, K/8]``."""
+    c = np.asarray(codes, dtype=np.uint32)
+    n, k = c.shape
+    assert k % 8 == 0 and int(c.max(initial=0)) <= 15
+    c = c.reshape(n, k // 8, 8)
+    out = np.zeros((n, k // 8), dtype=np.uint32)
+    for j in range(8):
+        out |= c[..., j] << np.uint32(4 * j)
+    return out
+
+
+def q4_k_multi_case(seed: int, m: int, ns, k: int):
+    """One Q4_K weight per part (rows ``ns[p]``), then x ``[m, k]``."""
+    g = rng(seed)
+    ws = [quantize_q4_k(normal_f32(g, (n, k), 0.02)) for n in ns]
+    x = normal_f32(g, (m, k))
+    return ws, x
+
+
 def qkv_payload(seq: int, q_sp: int, k_sp: int, v_sp: int) -> np.ndarray:
     """f32 [seq, q_sp+k_sp+v_sp] whose elements are distinct integers (exact in f32
     up to 2^24 elements), so every output element names its source position."""
@@ -180,4 +203,14 @@ CONFIGS = {
     "affine_12288x4096_gs64": dict(kind="affine", seed=104, m=8, n=12288, k=4096, gs=64),
     "prefill_qkv_512x2048": dict(kind="prefill", seed=105, m=512, n=8192, k=2048, gs=64,
                                  q_sp=2048, k_sp=2048, v_sp=4096),
+}
+
+
+# Workloads of the follow-on paths (multi-part Q4_K decode projection, packed
+# 4-bit affine GEMV, Q4_0 prefill on the matrix cores); the fused projection +
+# split reuses "prefill_qkv_512x2048" above.
+NEXT_CONFIGS = {
+    "q4_k_qkv_multi_4096": dict(kind="q4_k_multi", seed=106, m=1, ns=(4096, 1024, 1024), k=4096),
+    "affine_b4_12288x4096_gs64": dict(kind="affine_b4", seed=107, m=8, n=12288, k=4096, gs=64),
+    "q4_0_prefill_512x4096": dict(kind="q4_0", seed=108, m=512, n=4096, k=4096),
 }

@@ -291,3 +291,69 @@ def test_abs_bound_dominates_result():
     bound = oracle.abs_bound(w64, x)
     assert np.all(np.abs(y.astype(np.float64)) <= bound * (1 + 1e-6))
     assert np.all(bound > 0)
+
+
+# ------------------------------------------------------------- packed 4-bit affine
+def test_affine_b4_hand_words():
+    fx = _load("affine_b4_hand.json")
+    n, k, gs = fx["n"], fx["k"], fx["group_size"]
+    wp = np.array([[int(h, 16) for h in fx["words_hex"]]], dtype=np.uint32)
+    s = np.array(fx["scales"], np.float32)
+    b = np.array(fx["biases"], np.float32)
+    assert np.array_equal(oracle.unpack_b4_u32(wp, n, k)[0], np.arange(16))
+    assert np.array_equal(oracle.decode_affine_b4(wp, s, b, n, k, gs), np.array(fx["w"]))
+    ones = np.ones((1, k), np.float32)
+    ar = np.arange(k, dtype=np.float32)[None, :]
+    assert oracle.qmm_affine_t_packed(ones, wp, s, b, 1, n, k, gs)[0, 0] == fx["y_ones"]
+    assert oracle.qmm_affine_t_packed(ar, wp, s, b, 1, n, k, gs)[0, 0] == fx["y_arange"]
+
+
+def test_affine_b4_equals_unpacked_codes():
+    """Packing code j of each 8-code run into bits 4j..4j+3 (integer loop here)
+    and decoding must give the affine weights of the plain u8 codes."""
+    g = synth.rng(23)
+    n, k, gs = 6, 64, 32
+    codes = g.integers(0, 16, size=(n, k), dtype=np.uint8)
+    words = np.zeros((n, k // 8), dtype=np.uint32)
+    for r in range(n):
+        for kp in range(k // 8):
+            v = 0
+            for j in range(8):
+                v |= int(codes[r, 8 * kp + j]) << (4 * j)
+            words[r, kp] = v
+    s = g.uniform(0.001, 0.01, size=(n, k // gs)).astype(np.float32)
+    b = g.normal(0.0, 0.02, size=(n, k // gs)).astype(np.float32)
+    assert np.array_equal(oracle.decode_affine_b4(words, s, b, n, k, gs),
+                          oracle.decode_affine(codes, s, b, n, k, gs))
+    assert np.array_equal(synth.pack_b4_u32(codes), words)
+
+
+# ------------------------------------------------------------- multi-part projection
+def test_q4_k_multi_parts_land_in_their_columns():
+    """Parts [hand block, zero block, hand block] with x = ones: the hand
+    super-block gives 39 (its worked value), an all-zero super-block gives 0,
+    and each part lands in its own column."""
+    fx = _load("q4_k_hand_block.json")
+    hand = np.frombuffer(bytes.fromhex(fx["bytes_hex"]), dtype=np.uint8)[None, :]
+    zero = np.zeros_like(hand)
+    x = np.ones((1, 256), np.float32)
+    y = oracle.qgemv_multi(oracle.decode_q4_k, [(hand, 1), (zero, 1), (hand, 1)], x, 1, 256)
+    assert y.shape == (1, 3)
+    assert list(y[0]) == [fx["y_ones"], 0.0, fx["y_ones"]]
+    two = np.concatenate([zero, hand])
+    y2 = oracle.qgemv_multi(oracle.decode_q4_k, [(two, 2), (hand, 1)], x, 1, 256)
+    assert list(y2[0]) == [0.0, fx["y_ones"], fx["y_ones"]]
+
+
+# ------------------------------------------------------------- fused projection + split
+def test_affine_qkv_hand():
+    fx = _load("affine_qkv_hand.json")
+    x = np.array(fx["x"], np.float32)
+    q = np.array(fx["q"], np.uint8)
+    s = np.array(fx["scales"], np.float32)
+    b = np.array(fx["biases"], np.float32)
+    qo, ko, vo = oracle.qmm_affine_t_qkv(x, q, s, b, fx["m"], fx["k"], fx["group_size"],
+                                         fx["q_sp"], fx["k_sp"], fx["v_sp"])
+    assert np.array_equal(qo, np.array(fx["q_out"], np.float32))
+    assert np.array_equal(ko, np.array(fx["k_out"], np.float32))
+    assert np.array_equal(vo, np.array(fx["v_out"], np.float32))
