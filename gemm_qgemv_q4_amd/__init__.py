@@ -33,6 +33,9 @@ SIGNATURES = {
     "qgemv_dual_q4_0": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _P]),
     "qmm_affine_t": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "qkv_split_f32": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _I, _I, _P]),
+    "qgemv_q4_k_multi": (ctypes.c_int, [_P, _P, _P, _P, _I, _P, _I, _I, _P]),
+    "qmm_affine_t_packed": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
+    "qmm_affine_t_qkv": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "qg_set_mfma_min_m": (ctypes.c_int, [_I]),
     "qg_get_mfma_min_m": (ctypes.c_int64, []),
 }
@@ -47,7 +50,7 @@ class QGError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"libqgemv_q4 not built ({LIB_PATH} missing); run `python -m gemm_qgemv_q4_amd.build`")
+            f"libqgemv_q4 not built ({LIB_PATH} missing); run `python gemm_qgemv_q4_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)
@@ -164,6 +167,93 @@ def qmm_affine_t(x: torch.Tensor, q: torch.Tensor, scales: torch.Tensor, biases:
     _check(_lib.qmm_affine_t(px, pq, ps, pb, ctypes.c_void_p(y.data_ptr()), m, n, k, group_size,
                              _stream(x)))
     return y
+
+
+def qgemv_q4_k_multi(ws, x: torch.Tensor, ns, k: int, y: torch.Tensor | None = None, ys=None):
+    """Parts of a fused Q4_K projection in one launch: part p (weights ws[p],
+    ns[p] rows) writes columns [sum(ns[:p]), sum(ns[:p+1])) of one shared
+    output y[M, sum(ns)], or, when ``ys`` is given, its own output ys[p][M, ns[p]]."""
+    parts = len(ws)
+    if parts != len(ns) or parts < 1:
+        raise ValueError("ws and ns must be non-empty lists of the same length")
+    m = _mk(x, k)
+    if k % 256:
+        raise ValueError("K must be a multiple of 256")
+    px = _dev("x", x, torch.float32, numel=m * k)
+    pw = [_dev(f"ws[{i}]", w, torch.uint8, nbytes=n * (k // 256) * 144) for i, (w, n) in enumerate(zip(ws, ns))]
+    total = sum(ns)
+    if ys is None:
+        y = _out("y", y, (m, total), x)
+        col = [sum(ns[:i]) for i in range(parts)]
+        py = [ctypes.c_void_p(y.data_ptr() + 4 * c) for c in col]
+        ldy = [total] * parts
+        result = y
+    else:
+        if len(ys) != parts:
+            raise ValueError("ys must have one output per part")
+        ys = [_out(f"ys[{i}]", t, (m, n), x) for i, (t, n) in enumerate(zip(ys, ns))]
+        py = [ctypes.c_void_p(t.data_ptr()) for t in ys]
+        ldy = list(ns)
+        result = ys
+    arr_w = (ctypes.c_void_p * parts)(*pw)
+    arr_y = (ctypes.c_void_p * parts)(*py)
+    arr_n = (ctypes.c_int64 * parts)(*ns)
+    arr_l = (ctypes.c_int64 * parts)(*ldy)
+    _check(_lib.qgemv_q4_k_multi(arr_w, arr_y, arr_n, arr_l, parts, px, m, k, _stream(x)))
+    return result
+
+
+def qmm_affine_t_packed(x: torch.Tensor, w_packed: torch.Tensor, scales: torch.Tensor,
+                        biases: torch.Tensor, group_size: int, y: torch.Tensor | None = None):
+    """y[M, N] = x * (scales * q + biases)^T with the 4-bit codes packed eight per
+    32-bit word: w_packed[N, K/8] (int32 or uint32; code of element 8*kp + j in
+    bits 4j..4j+3 of word kp)."""
+    if w_packed.dim() != 2:
+        raise ValueError("w_packed must be [N, K/8]")
+    if w_packed.dtype not in (torch.int32, torch.uint32):
+        raise ValueError(f"w_packed dtype {w_packed.dtype} is not a 32-bit integer")
+    n, k = w_packed.shape[0], w_packed.shape[1] * 8
+    m = _mk(x, k)
+    if group_size <= 0 or k % group_size:
+        raise ValueError("K must be divisible by group_size")
+    g = n * (k // group_size)
+    px = _dev("x", x, torch.float32, numel=m * k)
+    pw = _dev("w_packed", w_packed, w_packed.dtype, numel=n * (k // 8))
+    ps = _dev("scales", scales, torch.float32, numel=g)
+    pb = _dev("biases", biases, torch.float32, numel=g)
+    y = _out("y", y, (m, n), x)
+    _check(_lib.qmm_affine_t_packed(px, pw, ps, pb, ctypes.c_void_p(y.data_ptr()), m, n, k, group_size,
+                                    _stream(x)))
+    return y
+
+
+def qmm_affine_t_qkv(x: torch.Tensor, q: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor,
+                     group_size: int, q_sp: int, k_sp: int, v_sp: int,
+                     q_out: torch.Tensor | None = None, k_out: torch.Tensor | None = None,
+                     v_out: torch.Tensor | None = None):
+    """The affine product of a fused [q_sp + k_sp + v_sp, K] weight written
+    straight into contiguous q[M, q_sp], k[M, k_sp], v[M, v_sp]; bitwise equal
+    to qmm_affine_t followed by qkv_split_f32."""
+    if q.dim() != 2:
+        raise ValueError("q must be [N, K]")
+    n, k = q.shape
+    if n != q_sp + k_sp + v_sp:
+        raise ValueError(f"q has {n} rows, spans add up to {q_sp + k_sp + v_sp}")
+    m = _mk(x, k)
+    if group_size <= 0 or k % group_size:
+        raise ValueError("K must be divisible by group_size")
+    g = n * (k // group_size)
+    px = _dev("x", x, torch.float32, numel=m * k)
+    pq = _dev("q_int", q, torch.uint8, numel=n * k)
+    ps = _dev("scales", scales, torch.float32, numel=g)
+    pb = _dev("biases", biases, torch.float32, numel=g)
+    q_out = _out("q_out", q_out, (m, q_sp), x)
+    k_out = _out("k_out", k_out, (m, k_sp), x)
+    v_out = _out("v_out", v_out, (m, v_sp), x)
+    _check(_lib.qmm_affine_t_qkv(px, pq, ps, pb, ctypes.c_void_p(q_out.data_ptr()),
+                                 ctypes.c_void_p(k_out.data_ptr()), ctypes.c_void_p(v_out.data_ptr()),
+                                 m, k, group_size, q_sp, k_sp, v_sp, _stream(x)))
+    return q_out, k_out, v_out
 
 
 def qkv_split_f32(qkv: torch.Tensor, seq: int, q_sp: int, k_sp: int, v_sp: int,

@@ -1,6 +1,9 @@
 """Build libqgemv_q4.so for gfx950 with hipcc (in-tree, no JIT cache).
 
-    python -m gemm_qgemv_q4_amd.build          # builds gemm_qgemv_q4_amd/lib/libqgemv_q4.so
+    python gemm_qgemv_q4_amd/build.py          # builds gemm_qgemv_q4_amd/lib/libqgemv_q4.so
+
+(Run it as a script: importing it through the package would first load the
+library that it is about to replace.)
 """
 from __future__ import annotations
 

@@ -1,5 +1,13 @@
 // C ABI of libqgemv_q4 (declared in include/qgemv_q4.h): argument checks,
 // kernel-variant choice and launches on the caller's stream.
+//
+// Every product entry point reduces to a list of "parts": weight tensors of
+// one format that share x, each with its rows and its output slice.  A part
+// list runs either on the GEMV kernel (small M) or, from qg_get_mfma_min_m()
+// rows of x on, on the matrix-core kernel.  Which of the two runs depends only
+// on the format, M, K, the group size and pointer alignment, never on how the
+// rows are split into parts, so single, dual, multi-part and fused-split calls
+// agree bit for bit.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -38,34 +46,67 @@ qg_status launch_status(const char* op) {
   return QG_OK;
 }
 
+qg_status launch_error(const char* op, const char* what, hipError_t e) {
+  snprintf(g_err, sizeof(g_err), "%s: %s: %s", op, what, hipGetErrorString(e));
+  return QG_ELAUNCH;
+}
+
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;  // keeps every in-kernel 32-bit index in range
+constexpr int64_t k2G = (int64_t)1 << 31;
 constexpr size_t kLdsBudget = 64 * 1024;       // per-workgroup x tile when K is tiled
 constexpr size_t kLdsPersistent = 150 * 1024;  // whole-K x tile of a persistent workgroup
 constexpr size_t kLdsMax = 160 * 1024;
 
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return 256;
+  if (dev >= 0 && dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+// One weight tensor of a product (host side).  Stream 1 is used by the dual
+// Q4_0 projection only.
+struct HostPart {
+  const void* w[2];
+  const float* scales;
+  const float* biases;
+  float* y[2];
+  int64_t ldy;
+  int64_t n;
+};
+
+// Bytes per weight row of each format.
+template <int FMT> int64_t row_bytes_of(int64_t k);
+template <> int64_t row_bytes_of<FMT_Q40>(int64_t k) { return k / 32 * 18; }
+template <> int64_t row_bytes_of<FMT_Q4K>(int64_t k) { return k / 256 * 144; }
+template <> int64_t row_bytes_of<FMT_AFF>(int64_t k) { return k; }
+template <> int64_t row_bytes_of<FMT_AFF4>(int64_t k) { return k / 2; }
+
 // ------------------------------------------------------------------ GEMV
 struct GemvPlan {
-  int mt, l, r, waves, kt, grid;
+  int mt, l, r, waves, kt, bpc;
   size_t lds;
   bool persistent;
 };
 
-int device_cus() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-    return 256;
-  return cus;
-}
-
 // Launch shape of the chunked GEMV kernel.  x of one m-tile is staged in LDS
 // once per workgroup when it fits (persistent workgroups walk several row
 // groups); otherwise each workgroup owns one row group and stages x in K tiles.
+// The shape depends on M and K only, so the arithmetic of an output never
+// depends on N or on the part list.
 template <int FMT>
-GemvPlan plan_gemv(int64_t m, int64_t n, int64_t k, int nw) {
+GemvPlan plan_gemv(int64_t m, int64_t k, int nw) {
   constexpr int CH = FmtTraits<FMT>::CH;
   constexpr bool SUMS = FmtTraits<FMT>::SUMS;
   GemvPlan pl{};
@@ -88,8 +129,6 @@ GemvPlan plan_gemv(int64_t m, int64_t n, int64_t k, int nw) {
     if (sscanf(env, "%d,%d,%d,%d", &el, &er, &ew, &eb) < 1) el = er = ew = eb = 0;
   }
   if (el == 8 || el == 16 || el == 32 || el == 64) pl.l = el;
-  const int p_rows = 64 / pl.l;
-  const int64_t mtiles = cdiv(m, pl.mt);
   int r = (pl.mt * nw <= 2 && chunks >= 64) ? 2 : 1;
   if (er == 1 || (er == 2 && pl.mt * nw <= 2) || (er == 4 && pl.mt * nw == 1)) r = er;
   pl.r = r;
@@ -98,15 +137,13 @@ GemvPlan plan_gemv(int64_t m, int64_t n, int64_t k, int nw) {
   if (pl.persistent) {
     pl.kt = (int)k;
     pl.lds = lds_for(k);
-    pl.waves = (FMT == FMT_AFF && pl.mt <= 2) ? 4 : 8;
+    pl.waves = ((FMT == FMT_AFF || FMT == FMT_AFF4) && pl.mt <= 2) ? 4 : 8;
     if (ew == 1 || ew == 2 || ew == 4 || ew == 8) pl.waves = ew;
     int bpc = (int)(kLdsMax / (pl.lds ? pl.lds : 1));
     const int bpc_max = pl.waves == 8 ? 1 : 4;
     bpc = bpc < 1 ? 1 : bpc > bpc_max ? bpc_max : bpc;
     if (eb >= 1 && eb <= 8 && (size_t)eb * pl.lds <= kLdsMax) bpc = eb;
-    const int64_t groups = cdiv(n, (int64_t)pl.waves * p_rows * r);
-    const int64_t cap = (int64_t)device_cus() * bpc;
-    pl.grid = (int)(groups < cap ? groups : cap);
+    pl.bpc = bpc;
   } else {
     pl.waves = 4;
     if (ew == 1 || ew == 2 || ew == 4) pl.waves = ew;
@@ -115,15 +152,33 @@ GemvPlan plan_gemv(int64_t m, int64_t n, int64_t k, int nw) {
     while (kt + step <= k && lds_for(kt + step) <= kLdsBudget) kt += step;
     pl.kt = (int)kt;
     pl.lds = lds_for(kt);
-    pl.grid = (int)cdiv(n, (int64_t)pl.waves * p_rows * r);
+    pl.bpc = 0;
   }
-  (void)mtiles;
   return pl;
 }
 
 template <int FMT, int MT, int NW, int L, int R>
 hipError_t launch_gemv_t(const GemvParams& p, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
-  auto kern = gemv_kernel<FMT, MT, NW, L, R>;
+  // multi-part variants exist for the formats whose entry points take parts
+  constexpr bool kHasMulti = NW == 1 && (FMT == FMT_Q4K || FMT == FMT_AFF);
+  if constexpr (kHasMulti) {
+    if (p.parts > 1) {
+      auto kern = gemv_kernel<FMT, MT, NW, L, R, true>;
+      if (lds > 64 * 1024) {
+        static std::atomic<bool> raised{false};
+        if (!raised.load()) {
+          hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax);
+          if (e != hipSuccess) return e;
+          raised.store(true);
+        }
+      }
+      hipLaunchKernelGGL(kern, grid, block, lds, s, p);
+      return hipSuccess;
+    }
+  }
+  if (p.parts != 1) return hipErrorInvalidValue;
+  auto kern = gemv_kernel<FMT, MT, NW, L, R, false>;
   if (lds > 64 * 1024) {
     static std::atomic<bool> raised{false};
     if (!raised.load()) {
@@ -174,42 +229,162 @@ hipError_t launch_gemv_mt(const GemvPlan& pl, const GemvParams& p, dim3 g, dim3 
   return hipErrorInvalidValue;
 }
 
-// Runs the chunked kernel (or the plain one when `plain`) over all m-tiles.
+// Runs a part list on the chunked GEMV kernel (or on the plain one when
+// `plain`), over all m-tiles of x.
 template <int FMT, int NW>
-qg_status run_gemv(const char* op, GemvParams p, int64_t m, bool plain, hipStream_t s) {
+qg_status run_gemv(const char* op, const HostPart* parts, int nparts, const float* x, int64_t m, int64_t k,
+                   int gs, bool plain, hipStream_t s) {
   (void)hipGetLastError();
+  const int64_t rb = row_bytes_of<FMT>(k);
   if (plain) {
     const dim3 block(256);
-    for (int64_t m0 = 0; m0 < m; m0 += 65535) {
-      const int64_t mc = m - m0 < 65535 ? m - m0 : 65535;
-      GemvParams q = p;
-      q.x = p.x + m0 * p.k;
-      q.y0 = p.y0 + m0 * p.n;
-      if (NW == 2) q.y1 = p.y1 + m0 * p.n;
-      const dim3 grid((unsigned)cdiv(p.n, 256), (unsigned)mc);
-      hipLaunchKernelGGL((gemv_plain_kernel<FMT, NW>), grid, block, 0, s, q, (int)mc);
+    for (int pi = 0; pi < nparts; ++pi) {
+      const HostPart& hp = parts[pi];
+      for (int64_t m0 = 0; m0 < m; m0 += 65535) {
+        const int64_t mc = m - m0 < 65535 ? m - m0 : 65535;
+        PlainParams q{};
+        for (int st = 0; st < 2; ++st) {
+          q.w[st] = static_cast<const uint8_t*>(hp.w[st] ? hp.w[st] : hp.w[0]);
+          q.y[st] = (hp.y[st] ? hp.y[st] : hp.y[0]) + m0 * hp.ldy;
+        }
+        q.scales = hp.scales;
+        q.biases = hp.biases;
+        q.x = x + m0 * k;
+        q.ldy = hp.ldy;
+        q.row_bytes = rb;
+        q.n = (int)hp.n;
+        q.k = (int)k;
+        q.gs = gs;
+        const dim3 grid((unsigned)cdiv(hp.n, 256), (unsigned)mc);
+        hipLaunchKernelGGL((gemv_plain_kernel<FMT, NW>), grid, block, 0, s, q, (int)mc);
+      }
     }
     return launch_status(op);
   }
-  const GemvPlan pl = plan_gemv<FMT>(m, p.n, p.k, NW);
-  const int p_rows = 64 / pl.l;
+  const GemvPlan pl = plan_gemv<FMT>(m, k, NW);
+  const int rows_per_group = pl.waves * (64 / pl.l) * pl.r;
+  GemvParams p{};
+  int64_t groups = 0;
+  for (int pi = 0; pi < nparts; ++pi) {
+    GemvPart& gp = p.part[pi];
+    for (int st = 0; st < 2; ++st) {
+      gp.w[st] = static_cast<const uint8_t*>(parts[pi].w[st] ? parts[pi].w[st] : parts[pi].w[0]);
+      gp.y[st] = parts[pi].y[st] ? parts[pi].y[st] : parts[pi].y[0];
+    }
+    gp.scales = parts[pi].scales;
+    gp.biases = parts[pi].biases;
+    gp.ldy = parts[pi].ldy;
+    gp.n = (int)parts[pi].n;
+    gp.group0 = (int)groups;
+    groups += cdiv(parts[pi].n, rows_per_group);
+  }
+  p.parts = nparts;
+  p.n_groups = (int)groups;
+  p.row_bytes = rb;
+  p.k = (int)k;
+  p.gs = gs;
   p.kt = pl.kt;
-  p.rows_per_block = pl.waves * p_rows * pl.r;
+  p.rows_per_block = rows_per_group;
+  int64_t grid = groups;
+  if (pl.persistent) {
+    const int64_t cap = (int64_t)device_cus() * pl.bpc;
+    grid = groups < cap ? groups : cap;
+  }
   const dim3 block(64 * pl.waves);
-  const int64_t blocks_x = pl.grid;
   for (int64_t m0 = 0; m0 < m; m0 += pl.mt) {
     GemvParams q = p;
-    q.x = p.x + m0 * p.k;
-    q.y0 = p.y0 + m0 * p.n;
-    if (NW == 2) q.y1 = p.y1 + m0 * p.n;
+    q.x = x + m0 * k;
+    for (int pi = 0; pi < nparts; ++pi)
+      for (int st = 0; st < 2; ++st) q.part[pi].y[st] = p.part[pi].y[st] + m0 * p.part[pi].ldy;
     q.m_rows = (int)(m - m0 < pl.mt ? m - m0 : pl.mt);
-    const hipError_t e = launch_gemv_mt<FMT, NW>(pl, q, dim3((unsigned)blocks_x), block, s);
-    if (e != hipSuccess) {
-      snprintf(g_err, sizeof(g_err), "%s: launch setup failed: %s", op, hipGetErrorString(e));
-      return QG_ELAUNCH;
-    }
+    const hipError_t e = launch_gemv_mt<FMT, NW>(pl, q, dim3((unsigned)grid), block, s);
+    if (e != hipSuccess) return launch_error(op, "launch setup failed", e);
   }
   return launch_status(op);
+}
+
+// ------------------------------------------------------------------ MFMA
+// The matrix-core path takes a part list when M reaches the threshold, K is a
+// whole number of 64-column stages, the group size is 32..512 and the weights
+// are aligned for its vector loads.
+template <int FMT>
+bool mfma_ok(const HostPart* parts, int nparts, int64_t m, int64_t k, int64_t gs) {
+  if (m < g_mfma_min_m.load() || k % 64 != 0 || gs < 32 || gs > 512) return false;
+  if (m * k >= k2G) return false;
+  const uintptr_t al = FMT == FMT_AFF || FMT == FMT_Q4K ? 16 : FMT == FMT_AFF4 ? 8 : 4;
+  for (int pi = 0; pi < nparts; ++pi) {
+    if (!aligned(parts[pi].w[0], al)) return false;
+    if (parts[pi].n * row_bytes_of<FMT>(k) >= k2G) return false;
+  }
+  return true;
+}
+
+// x -> (x_hi, x_lo, group sums) in stream-ordered scratch, then one launch of
+// the matrix-core kernel over every part's column tiles.
+template <int FMT>
+qg_status run_mfma(const char* op, const HostPart* parts, int nparts, const float* x, int64_t m, int64_t k,
+                   int gs, hipStream_t s) {
+  const int64_t groups = k / gs;
+  const size_t bytes_x = (size_t)m * k * sizeof(__bf16);
+  const size_t bytes_s = (size_t)m * groups * sizeof(__bf16);
+  const size_t bytes = 2 * bytes_x + 2 * bytes_s + 512;
+  (void)hipGetLastError();
+  void* scratch = nullptr;
+  hipError_t e = hipMallocAsync(&scratch, bytes, s);
+  if (e != hipSuccess) {
+    snprintf(g_err, sizeof(g_err), "%s: scratch allocation of %zu bytes failed: %s", op, bytes,
+             hipGetErrorString(e));
+    return QG_ELAUNCH;
+  }
+  auto align256 = [](void* p) {
+    return reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(p) + 255) & ~(uintptr_t)255);
+  };
+  __bf16* xh = static_cast<__bf16*>(scratch);
+  __bf16* xl = xh + (size_t)m * k;
+  __bf16* sh = static_cast<__bf16*>(align256(xl + (size_t)m * k));
+  __bf16* sl = static_cast<__bf16*>(align256(sh + (size_t)m * groups));
+  const int64_t items = m * (k / 8);
+  hipLaunchKernelGGL(affine_prep_kernel, dim3((unsigned)cdiv(items, 256)), dim3(256), 0, s, x, xh, xl, sh, sl,
+                     (int)m, (int)k, gs);
+  MfmaParams mp{};
+  mp.xh = xh;
+  mp.xl = xl;
+  mp.sh = sh;
+  mp.sl = sl;
+  int64_t tiles_n = 0;
+  for (int pi = 0; pi < nparts; ++pi) {
+    MfmaPart& q = mp.part[pi];
+    q.w = static_cast<const uint8_t*>(parts[pi].w[0]);
+    q.scales = parts[pi].scales;
+    q.biases = parts[pi].biases;
+    q.y = parts[pi].y[0];
+    q.ldy = parts[pi].ldy;
+    q.n = (int)parts[pi].n;
+    q.tile0 = (int)tiles_n;
+    tiles_n += cdiv(parts[pi].n, kBN);
+  }
+  mp.parts = nparts;
+  mp.row_bytes = row_bytes_of<FMT>(k);
+  mp.m = (int)m;
+  mp.k = (int)k;
+  mp.gs = gs;
+  mp.tiles_m = (int)cdiv(m, kBM);
+  mp.tiles_n = (int)tiles_n;
+  const dim3 grid((unsigned)(mp.tiles_m * mp.tiles_n));
+  if (nparts > 1) hipLaunchKernelGGL((qmm_mfma_kernel<FMT, true>), grid, dim3(512), 0, s, mp);
+  else hipLaunchKernelGGL((qmm_mfma_kernel<FMT, false>), grid, dim3(512), 0, s, mp);
+  const qg_status ls = launch_status(op);
+  e = hipFreeAsync(scratch, s);
+  if (ls == QG_OK && e != hipSuccess) return launch_error(op, "scratch release failed", e);
+  return ls;
+}
+
+// ------------------------------------------------------------------ checks
+qg_status check_mk(const char* op, int64_t m, int64_t k) {
+  if (m < 1 || k < 1) return fail("%s: M and K must be > 0; got (%lld, %lld)", op, (long long)m, (long long)k);
+  if (m > kMaxDim || k > kMaxDim)
+    return fail("%s: M and K must each be <= 2^30; got (%lld, %lld)", op, (long long)m, (long long)k);
+  return QG_OK;
 }
 
 qg_status check_mnk(const char* op, int64_t m, int64_t n, int64_t k) {
@@ -229,6 +404,14 @@ qg_status check_xy(const char* op, const float* x, const float* y) {
   return QG_OK;
 }
 
+qg_status check_group(const char* op, int64_t k, int64_t group_size) {
+  if (group_size < 2 || group_size > 1024 || (group_size & (group_size - 1)) != 0)
+    return fail("%s: group_size must be a power of two in [2, 1024]; got %lld", op, (long long)group_size);
+  if (k % group_size != 0)
+    return fail("%s: K (%lld) must be divisible by group_size (%lld)", op, (long long)k, (long long)group_size);
+  return QG_OK;
+}
+
 qg_status q40_common(const char* op, const void* w, const float* x, float* y, int64_t m, int64_t n,
                      int64_t k) {
   qg_status st = check_mnk(op, m, n, k);
@@ -237,6 +420,28 @@ qg_status q40_common(const char* op, const void* w, const float* x, float* y, in
   if (!w) return fail("%s: null weight pointer", op);
   if (!aligned(w, 4)) return fail("%s: Q4_0 weights must be 4-byte aligned", op);
   return check_xy(op, x, y);
+}
+
+HostPart single_part(const void* w, const float* scales, const float* biases, float* y, int64_t ldy, int64_t n) {
+  HostPart hp{};
+  hp.w[0] = w;
+  hp.scales = scales;
+  hp.biases = biases;
+  hp.y[0] = y;
+  hp.ldy = ldy;
+  hp.n = n;
+  return hp;
+}
+
+// The affine product over a part list (u8 or packed codes).
+template <int FMT>
+qg_status run_affine(const char* op, const HostPart* parts, int nparts, const float* x, int64_t m, int64_t k,
+                     int64_t gs, hipStream_t s) {
+  if (mfma_ok<FMT>(parts, nparts, m, k, gs)) return run_mfma<FMT>(op, parts, nparts, x, m, k, (int)gs, s);
+  bool plain = (k % 16 != 0) || gs < 16;
+  const uintptr_t al = FMT == FMT_AFF ? 16 : 8;
+  for (int pi = 0; pi < nparts; ++pi) plain = plain || !aligned(parts[pi].w[0], al);
+  return run_gemv<FMT, 1>(op, parts, nparts, x, m, k, (int)gs, plain, s);
 }
 
 }  // namespace
@@ -258,14 +463,10 @@ qg_status qgemv_q4_0(const void* w, const float* x, float* y, int64_t M, int64_t
   const char* op = "qgemv_q4_0";
   qg_status st = q40_common(op, w, x, y, M, N, K);
   if (st != QG_OK) return st;
-  GemvParams p{};
-  p.w0 = static_cast<const uint8_t*>(w);
-  p.x = x;
-  p.y0 = y;
-  p.row_bytes = K / 32 * 18;
-  p.n = (int)N;
-  p.k = (int)K;
-  return run_gemv<FMT_Q40, 1>(op, p, M, K % 64 != 0, static_cast<hipStream_t>(stream));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const HostPart hp = single_part(w, nullptr, nullptr, y, N, N);
+  if (mfma_ok<FMT_Q40>(&hp, 1, M, K, 32)) return run_mfma<FMT_Q40>(op, &hp, 1, x, M, K, 32, s);
+  return run_gemv<FMT_Q40, 1>(op, &hp, 1, x, M, K, 32, K % 64 != 0, s);
 }
 
 qg_status qgemv_dual_q4_0(const void* w_a, const void* w_b, const float* x, float* y_a, float* y_b,
@@ -276,16 +477,15 @@ qg_status qgemv_dual_q4_0(const void* w_a, const void* w_b, const float* x, floa
   st = q40_common(op, w_b, x, y_b, M, N, K);
   if (st != QG_OK) return st;
   if (y_a == y_b) return fail("%s: dst_a and dst_b must be different buffers", op);
-  GemvParams p{};
-  p.w0 = static_cast<const uint8_t*>(w_a);
-  p.w1 = static_cast<const uint8_t*>(w_b);
-  p.x = x;
-  p.y0 = y_a;
-  p.y1 = y_b;
-  p.row_bytes = K / 32 * 18;
-  p.n = (int)N;
-  p.k = (int)K;
-  return run_gemv<FMT_Q40, 2>(op, p, M, K % 64 != 0, static_cast<hipStream_t>(stream));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const HostPart two[2] = {single_part(w_a, nullptr, nullptr, y_a, N, N),
+                           single_part(w_b, nullptr, nullptr, y_b, N, N)};
+  // matrix cores: both weights as two parts of one launch (one x preparation)
+  if (mfma_ok<FMT_Q40>(two, 2, M, K, 32)) return run_mfma<FMT_Q40>(op, two, 2, x, M, K, 32, s);
+  HostPart hp = two[0];
+  hp.w[1] = w_b;
+  hp.y[1] = y_b;
+  return run_gemv<FMT_Q40, 2>(op, &hp, 1, x, M, K, 32, K % 64 != 0, s);
 }
 
 qg_status qgemv_q4_k(const void* w, const float* x, float* y, int64_t M, int64_t N, int64_t K,
@@ -297,14 +497,40 @@ qg_status qgemv_q4_k(const void* w, const float* x, float* y, int64_t M, int64_t
   if (!w) return fail("%s: null weight pointer", op);
   st = check_xy(op, x, y);
   if (st != QG_OK) return st;
-  GemvParams p{};
-  p.w0 = static_cast<const uint8_t*>(w);
-  p.x = x;
-  p.y0 = y;
-  p.row_bytes = K / 256 * 144;
-  p.n = (int)N;
-  p.k = (int)K;
-  return run_gemv<FMT_Q4K, 1>(op, p, M, !aligned(w, 16), static_cast<hipStream_t>(stream));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const HostPart hp = single_part(w, nullptr, nullptr, y, N, N);
+  if (mfma_ok<FMT_Q4K>(&hp, 1, M, K, 32)) return run_mfma<FMT_Q4K>(op, &hp, 1, x, M, K, 32, s);
+  return run_gemv<FMT_Q4K, 1>(op, &hp, 1, x, M, K, 32, !aligned(w, 16), s);
+}
+
+qg_status qgemv_q4_k_multi(const void* const* w, float* const* y, const int64_t* n, const int64_t* ldy,
+                           int64_t parts, const float* x, int64_t M, int64_t K, void* stream) {
+  const char* op = "qgemv_q4_k_multi";
+  if (parts < 1 || parts > kMaxParts)
+    return fail("%s: parts must be in [1, %d]; got %lld", op, kMaxParts, (long long)parts);
+  if (!w || !y || !n || !ldy) return fail("%s: null pointer", op);
+  qg_status st = check_mk(op, M, K);
+  if (st != QG_OK) return st;
+  if (K % 256 != 0) return fail("%s: K (%lld) must be a multiple of 256", op, (long long)K);
+  if (!x || !aligned(x, 4)) return fail("%s: x must be a non-null 4-byte aligned pointer", op);
+  HostPart hp[kMaxParts];
+  bool misaligned = false;
+  for (int64_t p = 0; p < parts; ++p) {
+    if (n[p] < 1 || n[p] > kMaxDim)
+      return fail("%s: part %lld: rows must be in [1, 2^30]; got %lld", op, (long long)p, (long long)n[p]);
+    if (ldy[p] < n[p] || ldy[p] > kMaxDim)
+      return fail("%s: part %lld: ldy (%lld) must be in [rows (%lld), 2^30]", op, (long long)p,
+                  (long long)ldy[p], (long long)n[p]);
+    if (!w[p]) return fail("%s: part %lld: null weight pointer", op, (long long)p);
+    st = check_xy(op, x, y[p]);
+    if (st != QG_OK) return st;
+    misaligned = misaligned || !aligned(w[p], 16);
+    hp[p] = single_part(w[p], nullptr, nullptr, y[p], ldy[p], n[p]);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int np = (int)parts;
+  if (mfma_ok<FMT_Q4K>(hp, np, M, K, 32)) return run_mfma<FMT_Q4K>(op, hp, np, x, M, K, 32, s);
+  return run_gemv<FMT_Q4K, 1>(op, hp, np, x, M, K, 32, misaligned, s);
 }
 
 qg_status qmm_affine_t(const float* x, const uint8_t* q, const float* scales, const float* biases,
@@ -312,80 +538,62 @@ qg_status qmm_affine_t(const float* x, const uint8_t* q, const float* scales, co
   const char* op = "qmm_affine_t";
   qg_status st = check_mnk(op, M, N, K);
   if (st != QG_OK) return st;
-  if (group_size < 2 || group_size > 1024 || (group_size & (group_size - 1)) != 0)
-    return fail("%s: group_size must be a power of two in [2, 1024]; got %lld", op, (long long)group_size);
-  if (K % group_size != 0)
-    return fail("%s: K (%lld) must be divisible by group_size (%lld)", op, (long long)K,
-                (long long)group_size);
+  st = check_group(op, K, group_size);
+  if (st != QG_OK) return st;
   if (!q || !scales || !biases) return fail("%s: null pointer", op);
   if (!aligned(scales, 4) || !aligned(biases, 4)) return fail("%s: scales/biases must be 4-byte aligned", op);
   st = check_xy(op, x, y);
   if (st != QG_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int gs = (int)group_size;
+  const HostPart hp = single_part(q, scales, biases, y, N, N);
+  return run_affine<FMT_AFF>(op, &hp, 1, x, M, K, group_size, static_cast<hipStream_t>(stream));
+}
 
-  if (M >= g_mfma_min_m.load() && gs >= 32 && gs <= 512 && K % 64 == 0 && aligned(q, 16) &&
-      M * K < ((int64_t)1 << 31) && N * K < ((int64_t)1 << 31)) {
-    // ---- matrix-core path: prepare x (bf16 hi/lo + group sums), then GEMM
-    const int64_t groups = K / gs;
-    const size_t bytes_x = (size_t)M * K * sizeof(__bf16);
-    const size_t bytes_s = (size_t)M * groups * sizeof(__bf16);
-    const size_t bytes = 2 * bytes_x + 2 * bytes_s + 512;
-    (void)hipGetLastError();
-    void* scratch = nullptr;
-    hipError_t e = hipMallocAsync(&scratch, bytes, s);
-    if (e != hipSuccess) {
-      snprintf(g_err, sizeof(g_err), "%s: scratch allocation of %zu bytes failed: %s", op, bytes,
-               hipGetErrorString(e));
-      return QG_ELAUNCH;
-    }
-    auto align256 = [](void* p) {
-      return reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(p) + 255) & ~(uintptr_t)255);
-    };
-    __bf16* xh = static_cast<__bf16*>(scratch);
-    __bf16* xl = xh + (size_t)M * K;
-    __bf16* sh = static_cast<__bf16*>(align256(xl + (size_t)M * K));
-    __bf16* sl = static_cast<__bf16*>(align256(sh + (size_t)M * groups));
-    const int64_t items = M * (K / 8);
-    hipLaunchKernelGGL(affine_prep_kernel, dim3((unsigned)cdiv(items, 256)), dim3(256), 0, s, x, xh, xl, sh, sl,
-                       (int)M, (int)K, gs);
-    MfmaParams mp{};
-    mp.xh = xh;
-    mp.xl = xl;
-    mp.sh = sh;
-    mp.sl = sl;
-    mp.q = q;
-    mp.scales = scales;
-    mp.biases = biases;
-    mp.y = y;
-    mp.m = (int)M;
-    mp.n = (int)N;
-    mp.k = (int)K;
-    mp.gs = gs;
-    mp.tiles_m = (int)cdiv(M, kBM);
-    mp.tiles_n = (int)cdiv(N, kBN);
-    hipLaunchKernelGGL(affine_mfma_kernel, dim3((unsigned)(mp.tiles_m * mp.tiles_n)), dim3(512), 0, s, mp);
-    const qg_status ls = launch_status(op);
-    e = hipFreeAsync(scratch, s);
-    if (ls == QG_OK && e != hipSuccess) {
-      snprintf(g_err, sizeof(g_err), "%s: scratch release failed: %s", op, hipGetErrorString(e));
-      return QG_ELAUNCH;
-    }
-    return ls;
+qg_status qmm_affine_t_packed(const float* x, const uint32_t* w_packed, const float* scales,
+                              const float* biases, float* y, int64_t M, int64_t N, int64_t K,
+                              int64_t group_size, void* stream) {
+  const char* op = "qmm_affine_t_packed";
+  qg_status st = check_mnk(op, M, N, K);
+  if (st != QG_OK) return st;
+  if (K % 8 != 0) return fail("%s: K (%lld) must be divisible by the pack factor (8)", op, (long long)K);
+  st = check_group(op, K, group_size);
+  if (st != QG_OK) return st;
+  if (!w_packed || !scales || !biases) return fail("%s: null pointer", op);
+  if (!aligned(w_packed, 4)) return fail("%s: w_packed must be 4-byte aligned", op);
+  if (!aligned(scales, 4) || !aligned(biases, 4)) return fail("%s: scales/biases must be 4-byte aligned", op);
+  st = check_xy(op, x, y);
+  if (st != QG_OK) return st;
+  const HostPart hp = single_part(w_packed, scales, biases, y, N, N);
+  return run_affine<FMT_AFF4>(op, &hp, 1, x, M, K, group_size, static_cast<hipStream_t>(stream));
+}
+
+qg_status qmm_affine_t_qkv(const float* x, const uint8_t* q, const float* scales, const float* biases,
+                           float* q_out, float* k_out, float* v_out, int64_t M, int64_t K,
+                           int64_t group_size, int64_t q_sp, int64_t k_sp, int64_t v_sp, void* stream) {
+  const char* op = "qmm_affine_t_qkv";
+  if (q_sp < 1 || k_sp < 1 || v_sp < 1) return fail("%s: q_sp, k_sp, v_sp must all be > 0", op);
+  if (q_sp > kMaxDim || k_sp > kMaxDim || v_sp > kMaxDim) return fail("%s: spans must be <= 2^30", op);
+  const int64_t N = q_sp + k_sp + v_sp;
+  qg_status st = check_mnk(op, M, N, K);
+  if (st != QG_OK) return st;
+  st = check_group(op, K, group_size);
+  if (st != QG_OK) return st;
+  if (!q || !scales || !biases) return fail("%s: null pointer", op);
+  if (!aligned(scales, 4) || !aligned(biases, 4)) return fail("%s: scales/biases must be 4-byte aligned", op);
+  float* outs[3] = {q_out, k_out, v_out};
+  for (int i = 0; i < 3; ++i) {
+    st = check_xy(op, x, outs[i]);
+    if (st != QG_OK) return st;
   }
-
-  GemvParams p{};
-  p.w0 = q;
-  p.scales = scales;
-  p.biases = biases;
-  p.x = x;
-  p.y0 = y;
-  p.row_bytes = K;
-  p.n = (int)N;
-  p.k = (int)K;
-  p.gs = gs;
-  const bool plain = (K % 16 != 0) || gs < 16 || !aligned(q, 16);
-  return run_gemv<FMT_AFF, 1>(op, p, M, plain, s);
+  if (q_out == k_out || q_out == v_out || k_out == v_out) return fail("%s: outputs must not alias each other", op);
+  const int64_t groups = K / group_size;
+  const int64_t span[3] = {q_sp, k_sp, v_sp};
+  HostPart hp[3];
+  int64_t row0 = 0;
+  for (int i = 0; i < 3; ++i) {
+    hp[i] = single_part(q + row0 * K, scales + row0 * groups, biases + row0 * groups, outs[i], span[i], span[i]);
+    row0 += span[i];
+  }
+  return run_affine<FMT_AFF>(op, hp, 3, x, M, K, group_size, static_cast<hipStream_t>(stream));
 }
 
 qg_status qkv_split_f32(const float* qkv, float* q, float* k, float* v, int64_t seq, int64_t q_sp,

@@ -7,6 +7,13 @@ namespace qg {
 
 constexpr int kWave = 64;
 
+// Weight formats: GGML block_q4_0, GGML block_q4_K, MLX-style affine groups
+// with u8 codes, and the same with codes packed eight per u32.
+enum { FMT_Q40 = 0, FMT_Q4K = 1, FMT_AFF = 2, FMT_AFF4 = 3 };
+
+// Most weight tensors (parts) one product may have.
+constexpr int kMaxParts = 8;
+
 typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -51,6 +58,19 @@ __device__ __forceinline__ float group_sum(float v, int width) {
   if (width >= 32) v += __shfl_xor(v, 16, kWave);
   if (width >= 64) v += __shfl_xor(v, 32, kWave);
   return v;
+}
+
+// Scale and min of sub-block j (0..7) of a block_q4_K from its 12 packed
+// scale bytes s12: 6 bits each; for j >= 4 the top two bits live in bits 6..7
+// of bytes j-4 (scale) and j (min).
+__device__ __forceinline__ void q4k_sc_m(const uint8_t* s12, int j, int& sc, int& mn) {
+  if (j < 4) {
+    sc = s12[j] & 63;
+    mn = s12[j + 4] & 63;
+  } else {
+    sc = (s12[j + 4] & 0x0F) | ((s12[j - 4] >> 6) << 4);
+    mn = (s12[j + 4] >> 4) | ((s12[j] >> 6) << 4);
+  }
 }
 
 // Sum over the 64 lanes of a wave (xor butterfly; fixed order).

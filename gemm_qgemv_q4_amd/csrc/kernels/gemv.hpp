@@ -9,6 +9,8 @@
 //           value d*sc*q - dmin*m              [ferrum-kernels q4_k_gemv_v2.rs]
 //   affine: u8 codes, f32 scale and bias per group, value s*q + b
 //                                              [mlx-native qmm_affine.rs]
+//   affine b4: the same with the codes packed eight per u32 word (element
+//           8*kp + j in bits 4j..4j+3 of word kp)   [same page, packed kernel]
 //
 // Work decomposition (chosen for wave64 and HBM streaming, not taken from the
 // pages' Metal kernels):
@@ -27,27 +29,38 @@
 //     x are staged too, which lets the block offset (-8*d, -dmin*m) be applied
 //     once per 32 weights instead of once per weight.
 //   * The lanes of a row are summed with a fixed xor butterfly: no atomics,
-//     and the arithmetic of one output does not depend on R, NW, MT or the
-//     number of waves, which makes the dual kernel bitwise equal to two
-//     single calls.
+//     and the arithmetic of one output does not depend on R, NW, MT, the
+//     number of waves or which part a row belongs to, which makes the dual
+//     kernel bitwise equal to two single calls, the multi-part product equal
+//     to one call per part, and the packed affine format equal to the u8 one.
+//   * A product may have up to kMaxParts parts: weight tensors of one format
+//     that share x, each with its own rows and output slice.  Row groups are
+//     numbered part after part, so the part of a workgroup's group is uniform
+//     and its pointers live in scalar registers.
 #pragma once
 #include "common.hpp"
 
 namespace qg {
 
-enum { FMT_Q40 = 0, FMT_Q4K = 1, FMT_AFF = 2 };
+// One weight tensor of a product and where its outputs go.
+struct GemvPart {
+  const uint8_t* w[2];    // weights of stream 0 and (dual only) stream 1
+  const float* scales;    // affine: [n, K/gs]
+  const float* biases;    // affine: [n, K/gs]
+  float* y[2];            // output (m, r) of stream s at y[s][m * ldy + r]
+  long long ldy;
+  int n;                  // rows
+  int group0;             // first row group of this part
+};
 
 struct GemvParams {
-  const uint8_t* w0;      // weights (stream 0)
-  const uint8_t* w1;      // weights (stream 1, dual only)
-  const float* scales;    // affine: [N, K/gs]
-  const float* biases;    // affine: [N, K/gs]
+  GemvPart part[kMaxParts];
+  int parts;
+  int n_groups;           // row groups over all parts
   const float* x;         // [m_rows, K] of this m-tile
-  float* y0;              // [m_rows, N] of this m-tile (stream 0)
-  float* y1;              // stream 1 (dual only)
   long long row_bytes;    // bytes per weight row
   int m_rows;             // valid x rows in this tile (<= MT)
-  int n, k;
+  int k;
   int gs;                 // affine group size
   int kt;                 // K elements staged per LDS tile (multiple of L*CH, or == k)
   int rows_per_block;     // waves_per_block * P * R
@@ -57,39 +70,75 @@ template <int FMT> struct FmtTraits;
 template <> struct FmtTraits<FMT_Q40> { static constexpr int CH = 64; static constexpr bool SUMS = true; };
 template <> struct FmtTraits<FMT_Q4K> { static constexpr int CH = 64; static constexpr bool SUMS = true; };
 template <> struct FmtTraits<FMT_AFF> { static constexpr int CH = 16; static constexpr bool SUMS = false; };
+template <> struct FmtTraits<FMT_AFF4> { static constexpr int CH = 16; static constexpr bool SUMS = false; };
 
 // Raw bytes of one chunk of one row.
 struct ChunkQ40 { u32x4a4 a; u32x4a4 b; uint32_t c; };   // 36 bytes: blocks 2t, 2t+1
 struct ChunkQ4K { u32x4 h; u32x4 qa; u32x4 qb; };         // header + 32 nibble bytes
 struct ChunkAff { u32x4 q; float s; float b; };           // 16 codes + their group's s, b
+struct ChunkAff4 { uint32_t q0, q1; float s; float b; };  // 16 packed codes + s, b
 
 template <int FMT> struct ChunkOf;
 template <> struct ChunkOf<FMT_Q40> { using T = ChunkQ40; };
 template <> struct ChunkOf<FMT_Q4K> { using T = ChunkQ4K; };
 template <> struct ChunkOf<FMT_AFF> { using T = ChunkAff; };
+template <> struct ChunkOf<FMT_AFF4> { using T = ChunkAff4; };
 
+// Chunk tg of row `row` of a weight tensor starting at w (affine: its scales
+// and biases start at sc, bi).
 template <int FMT>
 __device__ __forceinline__ typename ChunkOf<FMT>::T load_chunk(const GemvParams& p, const uint8_t* w,
-                                                               int row, int tg) {
+                                                               const float* sc, const float* bi, int row,
+                                                               int tg) {
   typename ChunkOf<FMT>::T c;
+  const uint8_t* rw = w + (size_t)row * (size_t)p.row_bytes;
   if constexpr (FMT == FMT_Q40) {
-    const uint8_t* base = w + (size_t)row * (size_t)p.row_bytes + 36 * (size_t)tg;
+    const uint8_t* base = rw + 36 * (size_t)tg;
     c.a = *(const u32x4a4*)(base);
     c.b = *(const u32x4a4*)(base + 16);
     c.c = *(const uint32_t*)(base + 32);
   } else if constexpr (FMT == FMT_Q4K) {
-    const uint8_t* base = w + (size_t)row * (size_t)p.row_bytes + 144 * (size_t)(tg >> 2);
+    const uint8_t* base = rw + 144 * (size_t)(tg >> 2);
     c.h = *(const u32x4*)(base);
     c.qa = *(const u32x4*)(base + 16 + 32 * (tg & 3));
     c.qb = *(const u32x4*)(base + 32 + 32 * (tg & 3));
   } else {
-    c.q = *(const u32x4*)(w + (size_t)row * (size_t)p.k + 16 * (size_t)tg);
+    if constexpr (FMT == FMT_AFF) {
+      c.q = *(const u32x4*)(rw + 16 * (size_t)tg);
+    } else {
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      const u32x2 v = *(const u32x2*)(rw + 8 * (size_t)tg);
+      c.q0 = v.x;
+      c.q1 = v.y;
+    }
     const int groups = p.k / p.gs;
     const size_t gi = (size_t)row * groups + (16 * tg) / p.gs;
-    c.s = p.scales[gi];
-    c.b = p.biases[gi];
+    c.s = sc[gi];
+    c.b = bi[gi];
   }
   return c;
+}
+
+// The four u32 words of byte codes (element order, one code per byte) of an
+// affine chunk.  Packed codes: word q0 holds elements 0..7 as nibbles; the
+// even elements are its low nibbles, the odd ones its high nibbles, and a
+// byte permute interleaves them back into element order.
+__device__ __forceinline__ void aff_words(const ChunkAff& c, uint32_t (&qd)[4]) {
+  qd[0] = c.q.x;
+  qd[1] = c.q.y;
+  qd[2] = c.q.z;
+  qd[3] = c.q.w;
+}
+__device__ __forceinline__ void aff_words(const ChunkAff4& c, uint32_t (&qd)[4]) {
+  const uint32_t w2[2] = {c.q0, c.q1};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t ev = w2[i] & 0x0F0F0F0Fu;         // elements 0, 2, 4, 6 of the word
+    const uint32_t od = (w2[i] >> 4) & 0x0F0F0F0Fu;  // elements 1, 3, 5, 7
+    // v_perm_b32(od, ev, sel): byte selector 0..3 = ev bytes, 4..7 = od bytes
+    qd[2 * i] = __builtin_amdgcn_perm(od, ev, 0x05010400u);
+    qd[2 * i + 1] = __builtin_amdgcn_perm(od, ev, 0x07030602u);
+  }
 }
 
 // Per-half (32-weight) scale factors of a chunk: y += A0*dot0 + B0*sumx0 + A1*dot1 + B1*sumx1
@@ -153,7 +202,12 @@ __device__ __forceinline__ void compute_chunk(const typename ChunkOf<FMT>::T (&c
                                               float (&acc)[NW][R][MT]) {
   constexpr int CH = FmtTraits<FMT>::CH;
   constexpr int NE4 = CH / 4;
-  if constexpr (FMT == FMT_AFF) {
+  if constexpr (FMT == FMT_AFF || FMT == FMT_AFF4) {
+    uint32_t words[NW][R][4];
+#pragma unroll
+    for (int s = 0; s < NW; ++s)
+#pragma unroll
+      for (int r = 0; r < R; ++r) aff_words(ch[s][r], words[s][r]);
 #pragma unroll
     for (int e4 = 0; e4 < NE4; ++e4) {
       f32x4 xv[MT];
@@ -163,7 +217,7 @@ __device__ __forceinline__ void compute_chunk(const typename ChunkOf<FMT>::T (&c
       for (int s = 0; s < NW; ++s)
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          const uint32_t qd = opaque(ch[s][r].q[e4]);
+          const uint32_t qd = opaque(words[s][r][e4]);
           const float sc = ch[s][r].s, bi = ch[s][r].b;
           const float w0 = __builtin_fmaf(sc, ubyte_f32<0>(qd), bi);
           const float w1 = __builtin_fmaf(sc, ubyte_f32<1>(qd), bi);
@@ -254,7 +308,7 @@ __device__ __forceinline__ void compute_chunk(const typename ChunkOf<FMT>::T (&c
 // otherwise it owns one group and stages x tile by tile.  The lane's weight
 // loads run one step ahead of its arithmetic across chunk, tile and group
 // boundaries.
-template <int FMT, int MT, int NW, int L, int R>
+template <int FMT, int MT, int NW, int L, int R, bool MULTI>
 __global__ void __launch_bounds__(512) gemv_kernel(GemvParams p) {
   constexpr int CH = FmtTraits<FMT>::CH;
   constexpr int NE4 = CH / 4;
@@ -271,30 +325,66 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams p) {
   const int lc = lane % L;
   const int rp = lane / L;
   const int rows_per_group = p.rows_per_block;
-  const int n_groups = (p.n + rows_per_group - 1) / rows_per_group;
+  const int n_groups = p.n_groups;
   const int n_chunks = p.k / CH;
   const int ct_max = p.kt / CH;
   const int ctp = ct_max + 1;  // LDS pitch in float4s (odd: spreads banks on the staging writes)
   f32x4* xs = smem;                                              // [MT][NE4][ctp]
   float* xsum = reinterpret_cast<float*>(smem + MT * NE4 * ctp);  // [MT][ct_max][2]
   const bool x_vec = (reinterpret_cast<uintptr_t>(p.x) & 15u) == 0;
-  const uint8_t* wptr[2] = {p.w0, NW == 2 ? p.w1 : p.w0};
-  float* yptr[2] = {p.y0, NW == 2 ? p.y1 : p.y0};
-
-  auto group_rows = [&](int g, int (&rows)[R], bool (&valid)[R]) {
-    const int row0 = g * rows_per_group + wv * (P * R) + rp;
+  // Part of row group g (uniform across the workgroup), copied out of the
+  // kernel arguments once per group, and this lane's rows in it, counted from
+  // the part's first row.
+  struct View {
+    const uint8_t* w[NW];
+    const float* sc;
+    const float* bi;
+    float* y[NW];
+    long long ldy;
+  };
+  struct Span {
+    int n, group0;
+  };
+  auto view_of = [&](const GemvPart& pt, View& v, Span& sp) {
+#pragma unroll
+    for (int s = 0; s < NW; ++s) {
+      v.w[s] = pt.w[s];
+      v.y[s] = pt.y[s];
+    }
+    v.sc = pt.scales;
+    v.bi = pt.biases;
+    v.ldy = pt.ldy;
+    sp.n = pt.n;
+    sp.group0 = pt.group0;
+  };
+  // A single-part launch (MULTI false) reads part 0 at fixed argument
+  // offsets together with the other arguments; only multi-part launches look
+  // the part of each group up.
+  auto group_rows = [&](int g, View& v, int (&rows)[R], bool (&valid)[R]) {
+    Span sp;
+    if constexpr (MULTI) {
+      int pi = 0;
+      for (int i = 1; i < p.parts; ++i)
+        if (g >= p.part[i].group0) pi = i;
+      pi = __builtin_amdgcn_readfirstlane(pi);
+      view_of(p.part[pi], v, sp);
+    } else {
+      view_of(p.part[0], v, sp);
+    }
+    const int n = sp.n;
+    const int row0 = (g - sp.group0) * rows_per_group + wv * (P * R) + rp;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int rr = row0 + r * P;
-      valid[r] = rr < p.n;
-      rows[r] = valid[r] ? rr : p.n - 1;  // clamp: loads stay in bounds, the store is skipped
+      valid[r] = rr < n;
+      rows[r] = valid[r] ? rr : n - 1;  // clamp: loads stay in bounds, the store is skipped
     }
   };
-  auto fetch = [&](Chunk (&dst)[NW][R], const int (&rows)[R], int tg) {
+  auto fetch = [&](Chunk (&dst)[NW][R], const View& v, const int (&rows)[R], int tg) {
 #pragma unroll
     for (int s = 0; s < NW; ++s)
 #pragma unroll
-      for (int r = 0; r < R; ++r) dst[s][r] = load_chunk<FMT>(p, wptr[s], rows[r], tg);
+      for (int r = 0; r < R; ++r) dst[s][r] = load_chunk<FMT>(p, v.w[s], v.sc, v.bi, rows[r], tg);
   };
 
   // Stage x[:, k0:k0+ktile] as [m][e4][chunk] float4 columns plus the sums of
@@ -339,14 +429,14 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams p) {
   // writing x to LDS waits only for x (loads retire in order) and the weights
   // stay in flight.  (For MT > 1 the extra registers cost more than it saves.)
   constexpr int XU = XPRE / MT > 0 ? XPRE / MT : 1;
-  auto stage_x_first = [&](int ktile, Chunk (&dst)[NW][R], const int (&rws)[R], int tg) {
+  auto stage_x_first = [&](int ktile, Chunk (&dst)[NW][R], const View& pv, const int (&rws)[R], int tg) {
     const int n4 = ktile >> 2;
     f32x4 v[MT][XU];
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
       for (int u = 0; u < XU; ++u) v[m][u] = xload(m, u * (int)blockDim.x + tid, 0, n4);
-    fetch(dst, rws, tg);
+    fetch(dst, pv, rws, tg);
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -357,9 +447,10 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams p) {
 
   const bool persistent = p.kt >= p.k;
   int g = blockIdx.x;
+  View cv;
   int rows[R];
   bool rvalid[R];
-  group_rows(g, rows, rvalid);
+  group_rows(g, cv, rows, rvalid);
   Chunk cur[NW][R];
   const int tg0 = lc < n_chunks ? lc : 0;
   bool staged = false;
@@ -373,19 +464,20 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams p) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) acc[s][r][m] = 0.0f;
     const int g_next = g + gridDim.x;
+    View nv;
     int rows_next[R];
     bool valid_next[R];
-    group_rows(g_next < n_groups ? g_next : g, rows_next, valid_next);
+    group_rows(g_next < n_groups ? g_next : g, nv, rows_next, valid_next);
 
     for (int k0 = 0; k0 < p.k; k0 += p.kt) {
       const int ktile = min(p.kt, p.k - k0);
       const int ct = ktile / CH;
       if (!persistent || !staged) {
         if (MT == 1 && !staged && k0 == 0 && (ktile >> 2) <= XU * (int)blockDim.x) {
-          if constexpr (MT == 1) stage_x_first(ktile, cur, rows, tg0);
+          if constexpr (MT == 1) stage_x_first(ktile, cur, cv, rows, tg0);
         } else {
-          if (staged) __syncthreads();  // the previous tile's readers are done
-          else fetch(cur, rows, tg0);   // first weights in flight while x is staged
+          if (staged) __syncthreads();     // the previous tile's readers are done
+          else fetch(cur, cv, rows, tg0);  // first weights in flight while x is staged
           stage(k0, ktile);
         }
         staged = true;
@@ -393,8 +485,8 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams p) {
       for (int t = lc; t < ct; t += L) {
         const int tg = k0 / CH + t;
         Chunk nxt[NW][R];
-        if (tg + L < n_chunks) fetch(nxt, rows, tg + L);
-        else if (g_next < n_groups) fetch(nxt, rows_next, tg0);
+        if (tg + L < n_chunks) fetch(nxt, cv, rows, tg + L);
+        else if (g_next < n_groups) fetch(nxt, nv, rows_next, tg0);
         compute_chunk<FMT, MT, NW, R>(cur, xs, xsum, ctp, ct_max, t, tg, acc);
 #pragma unroll
         for (int s = 0; s < NW; ++s)
@@ -411,9 +503,10 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams p) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           const float v = group_sum(acc[s][r][m], L);
-          if (lc == 0 && rvalid[r] && m < p.m_rows) yptr[s][(size_t)m * p.n + rows[r]] = v;
+          if (lc == 0 && rvalid[r] && m < p.m_rows) cv.y[s][(size_t)m * cv.ldy + rows[r]] = v;
         }
     g = g_next;
+    cv = nv;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       rows[r] = rows_next[r];
@@ -425,19 +518,29 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams p) {
 
 // ---------------------------------------------------------------------------
 // Plain kernel for shapes and alignments the chunked kernel does not take
-// (K not a multiple of 64 for Q4_0, misaligned Q4_K rows, affine K % 16 != 0
-// or group_size < 16): one thread per output, sequential f32 sum over K.
+// (K not a multiple of 64 for Q4_0, misaligned Q4_K rows, affine K % 16 != 0,
+// group_size < 16 or misaligned codes): one thread per output, sequential f32
+// sum over K.  Launched once per part.
+struct PlainParams {
+  const uint8_t* w[2];
+  const float* scales;
+  const float* biases;
+  const float* x;
+  float* y[2];
+  long long ldy;
+  long long row_bytes;
+  int n, k, gs;
+};
+
 template <int FMT, int NW>
-__global__ void __launch_bounds__(256) gemv_plain_kernel(GemvParams p, int m_count) {
+__global__ void __launch_bounds__(256) gemv_plain_kernel(PlainParams p, int m_count) {
   const int n = blockIdx.x * blockDim.x + threadIdx.x;
   const int m = blockIdx.y;
   if (n >= p.n || m >= m_count) return;
   const float* xr = p.x + (size_t)m * p.k;
-  const uint8_t* wptr[2] = {p.w0, NW == 2 ? p.w1 : p.w0};
-  float* yptr[2] = {p.y0, NW == 2 ? p.y1 : p.y0};
 #pragma unroll
   for (int s = 0; s < NW; ++s) {
-    const uint8_t* row = wptr[s] + (size_t)n * (size_t)p.row_bytes;
+    const uint8_t* row = p.w[s] + (size_t)n * (size_t)p.row_bytes;
     float a = 0.0f;
     for (int k = 0; k < p.k; ++k) {
       float w;
@@ -454,26 +557,22 @@ __global__ void __launch_bounds__(256) gemv_plain_kernel(GemvParams p, int m_cou
         const int j = e / 32;
         const float d = f16_bits_to_f32(sb[0] | ((uint32_t)sb[1] << 8));
         const float dmin = f16_bits_to_f32(sb[2] | ((uint32_t)sb[3] << 8));
-        const uint8_t* s12 = sb + 4;
         int sc, mn;
-        if (j < 4) {
-          sc = s12[j] & 63;
-          mn = s12[j + 4] & 63;
-        } else {
-          sc = (s12[j + 4] & 0x0F) | ((s12[j - 4] >> 6) << 4);
-          mn = (s12[j + 4] >> 4) | ((s12[j] >> 6) << 4);
-        }
+        q4k_sc_m(sb + 4, j, sc, mn);
         const uint32_t byte = sb[16 + 32 * (e / 64) + (e % 32)];
         const int q = (e % 64) < 32 ? (int)(byte & 15u) : (int)(byte >> 4);
         w = __builtin_fmaf(d * (float)sc, (float)q, -(dmin * (float)mn));
       } else {
         const int groups = p.k / p.gs;
         const size_t gi = (size_t)n * groups + k / p.gs;
-        w = __builtin_fmaf(p.scales[gi], (float)row[k], p.biases[gi]);
+        uint32_t code;
+        if constexpr (FMT == FMT_AFF) code = row[k];
+        else code = (row[k >> 1] >> (4 * (k & 1))) & 15u;
+        w = __builtin_fmaf(p.scales[gi], (float)code, p.biases[gi]);
       }
       a = __builtin_fmaf(xr[k], w, a);
     }
-    yptr[s][(size_t)m * p.n + n] = a;
+    p.y[s][(size_t)m * p.ldy + n] = a;
   }
 }
 

@@ -1,10 +1,15 @@
-// Prefill-M affine product on the gfx950 matrix cores.
+// Prefill-M products on the gfx950 matrix cores, for every weight format
+// whose values are a per-group affine map of small integer codes:
 //
 // y[m, n] = sum_g s[n,g] * sum_{k in g} x[m,k] q[n,k]  +  sum_g b[n,g] * X_g[m]
-// with X_g[m] = sum_{k in g} x[m,k]  (the affine value s*q + b of
-// mlx-native qmm_affine.rs, regrouped per group g of group_size columns).
+// with X_g[m] = sum_{k in g} x[m,k]:
+//   affine (u8 or packed codes): s, b from the scale and bias tensors
+//                                         [mlx-native qmm_affine.rs]
+//   Q4_0: groups of 32, s = d, b = -8 d   [mlx-native fused_dual_proj_q4_0.rs]
+//   Q4_K: groups of 32 (sub-blocks), s = d * sc_j, b = -dmin * m_j
+//                                         [ferrum-kernels q4_k_gemv_v2.rs]
 //
-// Precision: the codes q (0..255) are exact in bf16.  x is split once into
+// Precision: the codes (0..255) are exact in bf16.  x is split once into
 // x_hi = bf16(x) and x_lo = bf16(x - x_hi), so x_hi + x_lo carries 16
 // significant bits (relative error <= 2^-18); bf16 x bf16 products are exact
 // in the f32 MFMA accumulator.  Each group's partial product P_g = (x_hi +
@@ -17,9 +22,12 @@
 // Kernels:
 //   affine_prep_kernel : x [M,K] f32 -> x_hi, x_lo [M,K] bf16 and X [M, K/gs]
 //                        as bf16 hi, lo.
-//   affine_mfma_kernel : 128x128 output tile per 512-thread workgroup (eight
+//   qmm_mfma_kernel<F> : 128x128 output tile per 512-thread workgroup (eight
 //                        waves: 2x2 sub-tiles of 64x64, each shared by two
-//                        waves that split every 64-wide K stage).
+//                        waves that split every 64-wide K stage).  Column
+//                        tiles are numbered part after part (up to kMaxParts
+//                        weight tensors sharing x), so a tile's part is
+//                        uniform.
 #pragma once
 #include "common.hpp"
 
@@ -78,24 +86,67 @@ __global__ void __launch_bounds__(256) affine_prep_kernel(const float* __restric
   }
 }
 
+// One weight tensor of a product and where its outputs go.
+struct MfmaPart {
+  const uint8_t* w;       // row r at w + r * row_bytes
+  const float* scales;    // affine formats: [n, K/gs]
+  const float* biases;    // affine formats: [n, K/gs]
+  float* y;               // output (m, r) at y[m * ldy + r]
+  long long ldy;
+  int n;                  // rows
+  int tile0;              // first column tile of this part
+};
+
 struct MfmaParams {
   const __bf16* xh;      // [M, K]
   const __bf16* xl;      // [M, K]
   const __bf16* sh;      // [M, K/gs] group sums of x, hi
   const __bf16* sl;      // [M, K/gs] group sums of x, lo
-  const uint8_t* q;      // [N, K]
-  const float* scales;   // [N, K/gs]
-  const float* biases;   // [N, K/gs]
-  float* y;              // [M, N]
-  int m, n, k, gs;
-  int tiles_m, tiles_n;
+  MfmaPart part[kMaxParts];
+  int parts;
+  long long row_bytes;   // bytes per weight row
+  int m, k, gs;
+  int tiles_m, tiles_n;  // tiles_n over all parts
 };
 
 constexpr int kBM = 128, kBN = 128, kBK = 64;
 constexpr int kPitch = kBK + 8;  // bf16 elements per LDS row (144 bytes)
 constexpr int kTileElems = kBM * kPitch;
 
-struct StageRegs { u32x4 ah[2], al[2], b; };
+struct StageRegs { u32x4 ah[2], al[2], b; uint32_t b4; };
+
+// Scale s[row, g] and bias b[row, g] of group g (group size 32 for the block
+// formats) of weight row `row` of part `pt`.
+template <int F>
+__device__ __forceinline__ float group_scale(const MfmaPart& pt, long long row_bytes, int groups, int row,
+                                             int g) {
+  if constexpr (F == FMT_AFF || F == FMT_AFF4) {
+    return pt.scales[(size_t)row * groups + g];
+  } else if constexpr (F == FMT_Q40) {
+    const uint16_t d = *(const uint16_t*)(pt.w + (size_t)row * row_bytes + 18 * (size_t)g);
+    return f16_bits_to_f32(d);
+  } else {
+    const uint8_t* sb = pt.w + (size_t)row * row_bytes + 144 * (size_t)(g >> 3);
+    int sc, mn;
+    q4k_sc_m(sb + 4, g & 7, sc, mn);
+    return f16_bits_to_f32(*(const uint16_t*)sb) * (float)sc;  // exact: 11 x 6 bits
+  }
+}
+template <int F>
+__device__ __forceinline__ float group_bias(const MfmaPart& pt, long long row_bytes, int groups, int row,
+                                            int g) {
+  if constexpr (F == FMT_AFF || F == FMT_AFF4) {
+    return pt.biases[(size_t)row * groups + g];
+  } else if constexpr (F == FMT_Q40) {
+    const uint16_t d = *(const uint16_t*)(pt.w + (size_t)row * row_bytes + 18 * (size_t)g);
+    return -8.0f * f16_bits_to_f32(d);
+  } else {
+    const uint8_t* sb = pt.w + (size_t)row * row_bytes + 144 * (size_t)(g >> 3);
+    int sc, mn;
+    q4k_sc_m(sb + 4, g & 7, sc, mn);
+    return -(f16_bits_to_f32(*(const uint16_t*)(sb + 2)) * (float)mn);
+  }
+}
 
 // One 32-wide K step of the wave's 64x64 sub-tile: P += (A_hi + A_lo) * B.
 // All 16 hi products are issued before the 16 lo products, so consecutive
@@ -140,7 +191,8 @@ __device__ __forceinline__ void mfma_substep(const __bf16* sAh, const __bf16* sA
 // a wave scales its partial product: acc += s[n, g] * P.  The bias term
 // sum_g b[n,g] * X_g[m] is one more small matrix product at the end, with
 // both factors split into bf16 hi + lo (three MFMAs per 32 groups).
-__global__ void __launch_bounds__(512) affine_mfma_kernel(MfmaParams p) {
+template <int F, bool MULTI>
+__global__ void __launch_bounds__(512) qmm_mfma_kernel(MfmaParams p) {
   __shared__ __attribute__((aligned(16))) __bf16 sA[2][2 * kTileElems];  // [buf][hi | lo]
   __shared__ __attribute__((aligned(16))) __bf16 sB[2][kTileElems];
   __shared__ float sS[2][2][kBN];  // [buf][group in stage][n]
@@ -158,8 +210,18 @@ __global__ void __launch_bounds__(512) affine_mfma_kernel(MfmaParams p) {
   int tile = blockIdx.x;
   if ((total & 7) == 0) tile = (tile & 7) * (total >> 3) + (tile >> 3);
   const int tm = tile % p.tiles_m;
-  const int tn = tile / p.tiles_m;
-  const int m0 = tm * kBM, n0 = tn * kBN;
+  const int tn = tile / p.tiles_m;  // column tile over all parts
+  // a single-part launch (MULTI false) reads part 0 at fixed argument offsets
+  MfmaPart pt = p.part[0];
+  if constexpr (MULTI) {
+    int pi = 0;
+    for (int i = 1; i < p.parts; ++i)
+      if (tn >= p.part[i].tile0) pi = i;
+    pi = __builtin_amdgcn_readfirstlane(pi);
+    pt = p.part[pi];
+  }
+  const int n_rows = pt.n;
+  const int m0 = tm * kBM, n0 = (tn - pt.tile0) * kBN;  // n0: row of the part
   const int groups = p.k / p.gs;
   const int stages = p.k / kBK;
   const int ng = p.gs < kBK ? kBK / p.gs : 1;  // groups per stage: 2 when gs == 32
@@ -174,17 +236,19 @@ __global__ void __launch_bounds__(512) affine_mfma_kernel(MfmaParams p) {
     }
 
   // Chunks this thread moves per stage: 8-element pieces of x_hi/x_lo rows
-  // a_row0 and a_row0 + 64, and 16 codes of weight row b_n.  Offsets are 32-bit
-  // element offsets from the uniform base pointers (M*K and N*K are below 2^31,
-  // checked on the host).  Rows past M or N read nothing (zeros).
+  // a_row0 and a_row0 + 64, and 16 codes of weight row b_n (codes
+  // 16*b_kc .. 16*b_kc+15 of the stage's 64 columns).  Offsets are 32-bit
+  // offsets from the uniform base pointers (M*K elements and the part's
+  // weight bytes are below 2^31, checked on the host).  Rows past M or the
+  // part's rows read nothing (zeros).
   const int a_row0 = tid >> 3, a_kc = tid & 7;
   const int b_n = tid >> 2, b_kc = tid & 3;
   const bool a_ok0 = m0 + a_row0 < p.m, a_ok1 = m0 + a_row0 + 64 < p.m;
-  const bool b_ok = n0 + b_n < p.n;
+  const bool b_ok = n0 + b_n < n_rows;
   const uint32_t a_off0 = (uint32_t)(a_ok0 ? m0 + a_row0 : 0) * (uint32_t)p.k + (uint32_t)(a_kc * 8);
   const uint32_t a_off1 = (uint32_t)(a_ok1 ? m0 + a_row0 + 64 : 0) * (uint32_t)p.k + (uint32_t)(a_kc * 8);
-  const uint32_t b_off = (uint32_t)(b_ok ? n0 + b_n : 0) * (uint32_t)p.k + (uint32_t)(b_kc * 16);
-  const uint32_t s_off = (uint32_t)(n0 + (tid & 127) < p.n ? n0 + (tid & 127) : 0) * (uint32_t)groups;
+  const uint32_t b_row = (uint32_t)(b_ok ? n0 + b_n : 0) * (uint32_t)p.row_bytes;
+  const int s_row = n0 + (tid & 127) < n_rows ? n0 + (tid & 127) : n_rows - 1;
 
   auto load = [&](int st, StageRegs& r) {
     const uint32_t k0 = (uint32_t)(st * kBK);
@@ -193,7 +257,57 @@ __global__ void __launch_bounds__(512) affine_mfma_kernel(MfmaParams p) {
     r.al[0] = a_ok0 ? *(const u32x4*)(p.xl + (a_off0 + k0)) : z;
     r.ah[1] = a_ok1 ? *(const u32x4*)(p.xh + (a_off1 + k0)) : z;
     r.al[1] = a_ok1 ? *(const u32x4*)(p.xl + (a_off1 + k0)) : z;
-    r.b = b_ok ? *(const u32x4*)(p.q + (b_off + k0)) : z;
+    r.b = z;
+    r.b4 = 0u;
+    if (b_ok) {
+      if constexpr (F == FMT_AFF) {
+        r.b = *(const u32x4*)(pt.w + (b_row + k0 + 16u * b_kc));
+      } else if constexpr (F == FMT_AFF4) {
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 v = *(const u32x2*)(pt.w + (b_row + k0 / 2u + 8u * b_kc));
+        r.b.x = v.x;
+        r.b.y = v.y;
+      } else if constexpr (F == FMT_Q40) {
+        // the stage's two blocks are 36 contiguous bytes at 36*st; block
+        // b_kc/2 has its 16 nibble bytes at 2 (block 0) or 20 (block 1): read
+        // the 20 bytes from 16*(b_kc/2) (4-byte aligned, inside the 36)
+        const uint8_t* base = pt.w + (b_row + 36u * st + 16u * (b_kc >> 1));
+        r.b = *(const u32x4a4*)base;
+        r.b4 = *(const uint32_t*)(base + 16);
+      } else {
+        // Q4_K: stage st is 64-column chunk (st & 3) of super-block st / 4;
+        // its 32 nibble bytes sit at 16 + 32*(st & 3); b_kc & 1 picks the half
+        r.b = *(const u32x4*)(pt.w + (b_row + 144u * (st >> 2) + 16u + 32u * (st & 3) + 16u * (b_kc & 1)));
+      }
+    }
+  };
+  // The 16 codes of the thread's B chunk as bytes in element order.
+  auto code_words = [&](const StageRegs& r, uint32_t (&cw)[4]) {
+    if constexpr (F == FMT_AFF) {
+      cw[0] = r.b.x; cw[1] = r.b.y; cw[2] = r.b.z; cw[3] = r.b.w;
+    } else if constexpr (F == FMT_AFF4) {
+      const uint32_t w2[2] = {r.b.x, r.b.y};
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint32_t ev = w2[i] & 0x0F0F0F0Fu, od = (w2[i] >> 4) & 0x0F0F0F0Fu;
+        cw[2 * i] = __builtin_amdgcn_perm(od, ev, 0x05010400u);
+        cw[2 * i + 1] = __builtin_amdgcn_perm(od, ev, 0x07030602u);
+      }
+    } else {
+      uint32_t nb[4];
+      if constexpr (F == FMT_Q40) {
+        const uint32_t d[5] = {r.b.x, r.b.y, r.b.z, r.b.w, r.b4};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) nb[i] = (b_kc >> 1) ? d[i + 1] : __builtin_amdgcn_alignbyte(d[i + 1], d[i], 2);
+      } else {
+        nb[0] = r.b.x; nb[1] = r.b.y; nb[2] = r.b.z; nb[3] = r.b.w;
+      }
+      // Q4_0: low nibbles are elements 0..15 of the block, high ones 16..31;
+      // Q4_K: low nibbles are the first sub-block of the chunk, high the second
+      const bool high = F == FMT_Q40 ? (b_kc & 1) : (b_kc >> 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cw[i] = high ? (nb[i] >> 4) & 0x0F0F0F0Fu : nb[i] & 0x0F0F0F0Fu;
+    }
   };
   auto store = [&](int st, const StageRegs& r, int buf) {
     __bf16* ah = sA[buf];
@@ -203,17 +317,19 @@ __global__ void __launch_bounds__(512) affine_mfma_kernel(MfmaParams p) {
     *(u32x4*)(ah + (a_row0 + 64) * kPitch + a_kc * 8) = r.ah[1];
     *(u32x4*)(al + (a_row0 + 64) * kPitch + a_kc * 8) = r.al[1];
     // 16 codes -> 16 bf16 (exact: integers below 256)
+    uint32_t cw[4];
+    code_words(r, cw);
     bf16x8 lo, hi;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const uint32_t wlo = r.b[e >> 2], whi = r.b[2 + (e >> 2)];
+      const uint32_t wlo = cw[e >> 2], whi = cw[2 + (e >> 2)];
       lo[e] = (__bf16)(float)((wlo >> (8 * (e & 3))) & 0xFFu);
       hi[e] = (__bf16)(float)((whi >> (8 * (e & 3))) & 0xFFu);
     }
     *(bf16x8*)(sB[buf] + b_n * kPitch + b_kc * 16) = lo;
     *(bf16x8*)(sB[buf] + b_n * kPitch + b_kc * 16 + 8) = hi;
     const int g0 = st * kBK / p.gs;
-    if (tid < ng * kBN) sS[buf][tid >> 7][tid & 127] = p.scales[s_off + (uint32_t)(g0 + (tid >> 7))];
+    if (tid < ng * kBN) sS[buf][tid >> 7][tid & 127] = group_scale<F>(pt, p.row_bytes, groups, s_row, g0 + (tid >> 7));
   };
   auto scale_into_acc = [&](int buf, int gi) {
 #pragma unroll
@@ -289,8 +405,8 @@ __global__ void __launch_bounds__(512) affine_mfma_kernel(MfmaParams p) {
           xhv = p.sh[(size_t)gm * groups + gg];
           xlv = p.sl[(size_t)gm * groups + gg];
         }
-        if (gn < p.n) {
-          const float b = p.biases[(size_t)gn * groups + gg];
+        if (gn < n_rows) {
+          const float b = group_bias<F>(pt, p.row_bytes, groups, gn, gg);
           bhv = (__bf16)b;
           blv = (__bf16)(b - (float)bhv);
         }
@@ -335,7 +451,7 @@ __global__ void __launch_bounds__(512) affine_mfma_kernel(MfmaParams p) {
         for (int e = 0; e < 4; ++e) {
           const int gm = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + e;
           const int gn = n0 + wn * 64 + j * 16 + (lane & 15);
-          if (gm < p.m && gn < p.n) p.y[(size_t)gm * p.n + gn] = acc[i][j][e];
+          if (gm < p.m && gn < n_rows) pt.y[(size_t)gm * pt.ldy + gn] = acc[i][j][e];
         }
   }
 }

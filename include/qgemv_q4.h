@@ -5,9 +5,9 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
- *    keeps no pointer after a call returns.  qmm_affine_t allocates and frees
- *    stream-ordered scratch for its prefill path (see below); nothing else
- *    allocates.
+ *    keeps no pointer after a call returns.  The product calls allocate and
+ *    free stream-ordered scratch for their matrix-core path (see "Prefill
+ *    rows" below); nothing else allocates.
  *  - Row-major, contiguous.  x is [M, K] f32, y is [M, N] f32:
  *        y[m, n] = sum_k x[m, k] * w[n, k]
  *    where w is the dequantized weight.
@@ -26,6 +26,17 @@
  *  - Results are deterministic: the same call on the same data gives the same
  *    bits.  Floating-point results match the exact product within
  *    max |y - y_exact| <= 1e-5 * sum_k |x[m,k] * w[n,k]|.
+ *  - Prefill rows: from M >= qg_get_mfma_min_m() rows of x on (and K % 64 ==
+ *    0, the weights aligned for 16-byte loads -- 8 for packed codes, 4 for
+ *    Q4_0 -- and for the affine formats 32 <= group_size <= 512) a product
+ *    runs on the matrix cores.  x is split into two bf16 terms so the f32
+ *    tolerance above still holds.  That path takes stream-ordered scratch
+ *    (hipMallocAsync / hipFreeAsync on `stream`) of M*K*4 + M*(K/gs)*4 bytes
+ *    plus alignment (gs = 32 for Q4_0 and Q4_K).  The choice of path depends
+ *    on the format, M, K, the group size and alignment only, so the
+ *    equalities stated below (dual = two singles, multi-part = one call per
+ *    part, packed = unpacked, fused split = product then split) hold bit for
+ *    bit on both paths.
  */
 #ifndef QGEMV_Q4_H
 #define QGEMV_Q4_H
@@ -93,11 +104,6 @@ qg_status qgemv_dual_q4_0(const void* w_a, const void* w_b, const float* x,
  *   x : [M, K] f32;  q : [N, K] u8 codes (any value 0..255);
  *   scales, biases : [N, K/group_size] f32;  y : [M, N] f32.
  *   group_size : power of two in [2, 1024], K % group_size == 0.
- * For M >= qg_get_mfma_min_m() (and 32 <= group_size <= 512, K % 64 == 0,
- * q 16-byte aligned) the product runs on the matrix cores; x is split into
- * two bf16 terms so the f32 tolerance above still holds.  That path takes
- * stream-ordered scratch (hipMallocAsync / hipFreeAsync on `stream`) of
- * M*K*4 + M*(K/group_size)*4 bytes (plus alignment).
  * Errors: M, N, K < 1; bad group_size; K % group_size != 0; null pointers;
  *         misaligned f32 pointers.
  */
@@ -105,6 +111,64 @@ qg_status qmm_affine_t(const float* x, const uint8_t* q, const float* scales,
                        const float* biases, float* y,
                        int64_t M, int64_t N, int64_t K, int64_t group_size,
                        void* stream);
+
+/*
+ * qgemv_q4_k_multi -- the parts of a fused projection in one launch.
+ * Defined by: ferrum-kernels `q4_k_gemv_v2.rs` (doc of
+ * dispatch_gemv_q4k_v2_offset: each part of a fused projection has its own
+ * weights and writes a disjoint slice of a shared output buffer).
+ *   parts      : number of parts, 1..8.
+ *   w[p]       : Q4_K weights of part p, [n[p]][K/256] super-blocks as for
+ *                qgemv_q4_k.
+ *   y[p], ldy[p] : output of part p: y[p][m*ldy[p] + j] = sum_k x[m,k] *
+ *                W_p[j,k] for j < n[p].  For one shared output Y[M, N_total]
+ *                pass y[p] = Y + (first column of part p), ldy[p] = N_total.
+ *   x : [M, K] f32 shared by all parts.
+ * Each part's result is bitwise equal to qgemv_q4_k on that part alone.
+ * Output slices must not overlap each other or x.
+ * Errors: parts outside 1..8; M, K, n[p] < 1; K % 256 != 0; ldy[p] < n[p];
+ *         null pointers; x or y[p] not 4-byte aligned.
+ */
+qg_status qgemv_q4_k_multi(const void* const* w, float* const* y, const int64_t* n,
+                           const int64_t* ldy, int64_t parts, const float* x,
+                           int64_t M, int64_t K, void* stream);
+
+/*
+ * qmm_affine_t_packed -- qmm_affine_t with 4-bit codes packed eight per word.
+ * Defined by: mlx-native `qmm_affine.rs` (dispatch_qmm_affine_t_packed_simd4_b4
+ * and the pack_b4_to_u32 helper of its tests: the code of element 8*kp + j
+ * sits in bits 4j..4j+3 of u32 word kp; the packed product is byte-identical
+ * to the unpacked one).
+ *   w_packed : [N, K/8] u32, 4-byte aligned;  scales, biases : [N, K/gs] f32;
+ *   x : [M, K] f32;  y : [M, N] f32.
+ *   group_size : power of two in [2, 1024], K % group_size == 0, K % 8 == 0.
+ *   (The page's kernel takes group_size 32 only; any group size is taken here.)
+ * Bitwise equal to qmm_affine_t on the unpacked u8 codes when w_packed is
+ * 8-byte aligned and the u8 codes 16-byte aligned.  Half the weight bytes.
+ * Errors: as qmm_affine_t; K % 8 != 0.
+ */
+qg_status qmm_affine_t_packed(const float* x, const uint32_t* w_packed, const float* scales,
+                              const float* biases, float* y,
+                              int64_t M, int64_t N, int64_t K, int64_t group_size,
+                              void* stream);
+
+/*
+ * qmm_affine_t_qkv -- fused QKV projection with the split in its epilogue.
+ * Defined by: mlx-native `qkv_split.rs` (module doc: the fused projection's
+ * output [seq, q|k|v] is split into contiguous q, k, v) over the product of
+ * mlx-native `qmm_affine.rs`.
+ *   q : [N, K] u8 codes with N = q_sp + k_sp + v_sp (rows 0..q_sp-1 give q,
+ *       the next k_sp rows k, the last v_sp rows v); scales, biases:
+ *       [N, K/gs] f32;  x : [M, K] f32.
+ *   q_out : [M, q_sp], k_out : [M, k_sp], v_out : [M, v_sp] f32.
+ * Bitwise equal to qmm_affine_t into a [M, N] buffer followed by
+ * qkv_split_f32; the [M, N] intermediate is never written.
+ * Errors: as qmm_affine_t; a span < 1; outputs aliasing each other.
+ */
+qg_status qmm_affine_t_qkv(const float* x, const uint8_t* q, const float* scales,
+                           const float* biases, float* q_out, float* k_out, float* v_out,
+                           int64_t M, int64_t K, int64_t group_size,
+                           int64_t q_sp, int64_t k_sp, int64_t v_sp, void* stream);
 
 /*
  * qkv_split_f32 -- split a fused QKV activation into contiguous q, k, v.
@@ -121,7 +185,7 @@ qg_status qkv_split_f32(const float* qkv, float* q, float* k, float* v,
                         void* stream);
 
 /*
- * Tuning knob: smallest M at which qmm_affine_t uses the matrix-core path
+ * Tuning knob: smallest M at which the product calls use the matrix-core path
  * (default 64).  Process-wide.  qg_set_mfma_min_m returns QG_EINVAL for m < 1.
  */
 qg_status qg_set_mfma_min_m(int64_t m);

@@ -22,15 +22,15 @@ def declared_functions():
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
         for m in re.finditer(r"\b([A-Za-z_][A-Za-z0-9_]*)\s*\(", text):
             name = m.group(1)
-            if name.startswith("qg") or name in ("qmm_affine_t", "qkv_split_f32"):
+            if name.startswith(("qg", "qmm_", "qkv_")):
                 names.add(name)
     return names
 
 
-def test_header_declares_the_five_entry_points():
+def test_header_declares_the_entry_points():
     names = declared_functions()
     for fn in ("qgemv_q4_0", "qgemv_q4_k", "qgemv_dual_q4_0", "qmm_affine_t", "qkv_split_f32",
-               "qg_last_error"):
+               "qgemv_q4_k_multi", "qmm_affine_t_packed", "qmm_affine_t_qkv", "qg_last_error"):
         assert fn in names
 
 
@@ -120,3 +120,39 @@ def test_error_message_is_per_call():
     assert "QK4_0" in qg.last_error()
     _err(qg.raw.qgemv_q4_k(A, B, C, 1, 4, 384, None))
     assert "256" in qg.last_error()
+
+
+def _multi(ws, ys, ns, ldys, parts, x, m, k):
+    n_arr = (ctypes.c_int64 * max(1, len(ns)))(*ns)
+    l_arr = (ctypes.c_int64 * max(1, len(ldys)))(*ldys)
+    w_arr = (ctypes.c_void_p * max(1, len(ws)))(*ws)
+    y_arr = (ctypes.c_void_p * max(1, len(ys)))(*ys)
+    return qg.raw.qgemv_q4_k_multi(w_arr, y_arr, n_arr, l_arr, parts, x, m, k, None)
+
+
+def test_multi_rejects_bad_part_lists():
+    assert "parts" in _err(_multi([A], [C], [4], [4], 0, B, 1, 256))
+    assert "parts" in _err(_multi([A] * 9, [C] * 9, [4] * 9, [4] * 9, 9, B, 1, 256))
+    assert "ldy" in _err(_multi([A, D], [C, E], [4, 8], [4, 7], 2, B, 1, 256))
+    assert "rows" in _err(_multi([A, D], [C, E], [4, 0], [4, 4], 2, B, 1, 256))
+    assert "256" in _err(_multi([A], [C], [4], [4], 1, B, 1, 384))
+    assert "null" in _err(_multi([A, None], [C, E], [4, 4], [4, 4], 2, B, 1, 256))
+    assert "M and K" in _err(_multi([A], [C], [4], [4], 1, B, 0, 256))
+    assert "null" in _err(qg.raw.qgemv_q4_k_multi(None, None, None, None, 1, B, 1, 256, None))
+
+
+def test_packed_rejects_bad_shapes():
+    assert "pack factor" in _err(qg.raw.qmm_affine_t_packed(A, B, C, D, E, 1, 1, 36, 4, None))
+    assert "group_size" in _err(qg.raw.qmm_affine_t_packed(A, B, C, D, E, 1, 1, 64, 48, None))
+    assert "divisible" in _err(qg.raw.qmm_affine_t_packed(A, B, C, D, E, 1, 1, 96, 64, None))
+    assert "aligned" in _err(qg.raw.qmm_affine_t_packed(A, P(8194), C, D, E, 1, 1, 64, 32, None))
+    assert "must all be > 0" in _err(qg.raw.qmm_affine_t_packed(A, B, C, D, E, 1, 0, 64, 32, None))
+
+
+def test_qkv_fused_rejects_bad_spans_and_aliasing():
+    F = P(1 << 17)
+    G = P(1 << 18)
+    assert "> 0" in _err(qg.raw.qmm_affine_t_qkv(A, B, C, D, E, F, G, 1, 64, 32, 0, 4, 4, None))
+    assert "alias" in _err(qg.raw.qmm_affine_t_qkv(A, B, C, D, E, E, G, 1, 64, 32, 4, 4, 4, None))
+    assert "group_size" in _err(qg.raw.qmm_affine_t_qkv(A, B, C, D, E, F, G, 1, 64, 3, 4, 4, 4, None))
+    assert "null" in _err(qg.raw.qmm_affine_t_qkv(A, None, C, D, E, F, G, 1, 64, 32, 4, 4, 4, None))
