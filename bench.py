@@ -8,9 +8,12 @@ with the weights rotated over >= 1 GiB of distinct device copies so that the
 256 MB Infinity Cache cannot serve them, and the K timed calls captured in a
 HIP graph and replayed (the per-call launch cost of Python is not timed).
 
-The other four workloads (Q4_0 GEMV 1024^2, dual Q4_0 at M = 1/4/8, affine
-12288x4096 at M = 1/8, prefill affine GEMM 512x8192x2048 + qkv split) are
-measured the same way and reported under "per_config".
+The other workloads (Q4_0 GEMV 1024^2, dual Q4_0 at M = 1/4/8, affine
+12288x4096 at M = 1/8, prefill affine GEMM 512x8192x2048 + qkv split, and the
+follow-on paths: multi-part Q4_K, packed 4-bit affine, Q4_0 prefill on the
+matrix cores, the fused projection + split) are measured the same way and
+reported under "per_config": the first of five timed replays, the median,
+p10 and p90 over the five, and one cold call after a 512 MiB cache flush.
 
 `cpu_baseline` times the f64 CPU oracle on a bounded sample of the same
 workload on the host; `roofline.traffic` comes from the committed rocprofv3
@@ -35,6 +38,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
 ROTATE_BYTES = 1 << 30
+REPS = 5  # timed replays of the K-call graph per workload
 HEADLINE = "q4_k_gemv_4096"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q4_k_gemv_4096_traffic.json")
 
@@ -152,6 +156,77 @@ def build_cases(qg, torch, only=None):
                           lambda i, qkv_r=qkv_r, rr=rr, c=c, qo=qo, ko=ko, vo=vo:
                           qg.qkv_split_f32(qkv_r[i % rr], c["m"], c["q_sp"], c["k_sp"], c["v_sp"],
                                            q=qo, k=ko, v=vo)))
+    # ---- follow-on paths
+    nxt = synth.NEXT_CONFIGS
+    # multi-part Q4_K: a q|k|v decode projection (4096 + 1024 + 1024 rows) in one
+    # launch, and the same three products as three separate calls
+    if want("q4_k_qkv_multi_4096"):
+        c = nxt["q4_k_qkv_multi_4096"]
+        ws, x = synth.q4_k_multi_case(c["seed"], c["m"], c["ns"], c["k"])
+        wbytes = sum(w.nbytes for w in ws)
+        r = n_copies(wbytes)
+        wss = [rot(dev(w), r) for w in ws]
+        dx = dev(x)
+        ntot = sum(c["ns"])
+        y = torch.empty((c["m"], ntot), dtype=torch.float32, device="cuda")
+        nb = wbytes + x.nbytes + y.numel() * 4
+        ns, k = list(c["ns"]), c["k"]
+        cases.append(Case("q4_k_qkv_multi_4096", "Q4_K multi-part 4096+1024+1024 x 4096, M=1, one launch", nb,
+                          2 * ntot * k, r,
+                          lambda i, wss=wss, dx=dx, y=y, r=r, ns=ns, k=k:
+                          qg.qgemv_q4_k_multi([wl[i % r] for wl in wss], dx, ns, k, y=y)))
+        ys = [y[:, sum(ns[:j]):sum(ns[:j + 1])] for j in range(len(ns))]
+        outs = [torch.empty((c["m"], n), dtype=torch.float32, device="cuda") for n in ns]
+        cases.append(Case("q4_k_qkv_separate_4096", "the same three Q4_K products as three calls", nb,
+                          2 * ntot * k, r,
+                          lambda i, wss=wss, dx=dx, outs=outs, r=r, ns=ns, k=k:
+                          [qg.qgemv_q4_k(wl[i % r], dx, n, k, y=o) for wl, n, o in zip(wss, ns, outs)]))
+    # packed 4-bit affine codes, 12288 x 4096 gs 64, M = 1 and 8
+    if want("affine_b4_12288x4096_gs64"):
+        c = nxt["affine_b4_12288x4096_gs64"]
+        x8, q, s, b = synth.affine_case(c["seed"], c["m"], c["n"], c["k"], c["gs"])
+        wp = synth.pack_b4_u32(q).view(np.int32)
+        wbytes = wp.nbytes + s.nbytes + b.nbytes
+        r = n_copies(wbytes)
+        wps, ss_, bs_ = rot(dev(wp), r), rot(dev(s), r), rot(dev(b), r)
+        for m in (1, 8):
+            dx = dev(x8[:m])
+            y = torch.empty((m, c["n"]), dtype=torch.float32, device="cuda")
+            nb = wbytes + m * c["k"] * 4 + m * c["n"] * 4
+            cases.append(Case(f"affine_b4_12288x4096_gs64_m{m}", f"packed affine gs64 M={m} N=12288 K=4096", nb,
+                              2 * m * c["n"] * c["k"], r,
+                              lambda i, wps=wps, ss_=ss_, bs_=bs_, dx=dx, y=y, r=r, gs=c["gs"]:
+                              qg.qmm_affine_t_packed(dx, wps[i % r], ss_[i % r], bs_[i % r], gs, y=y)))
+    # Q4_0 prefill on the matrix cores, 512 x 4096 x 4096
+    if want("q4_0_prefill_512x4096"):
+        c = nxt["q4_0_prefill_512x4096"]
+        w, x = synth.q4_0_case(c["seed"], c["m"], c["n"], c["k"])
+        r = n_copies(w.nbytes)
+        ws, dx = rot(dev(w), r), dev(x)
+        y = torch.empty((c["m"], c["n"]), dtype=torch.float32, device="cuda")
+        nb = w.nbytes + x.nbytes + y.numel() * 4
+        cases.append(Case("q4_0_prefill_512x4096", "Q4_0 M=512 N=4096 K=4096 (MFMA)", nb,
+                          2 * c["m"] * c["n"] * c["k"], r,
+                          lambda i, ws=ws, dx=dx, y=y, r=r, n=c["n"], k=c["k"]:
+                          qg.qgemv_q4_0(ws[i % r], dx, n, k, y=y), bound="mfma"))
+    # fused projection + q|k|v split on the prefill workload
+    if want("prefill_qkv_fused_512x2048"):
+        c = cfg["prefill_qkv_512x2048"]
+        x, q, s, b = synth.affine_case(c["seed"], c["m"], c["n"], c["k"], c["gs"])
+        wbytes = q.nbytes + s.nbytes + b.nbytes
+        r = n_copies(wbytes)
+        qs_, ss_, bs_ = rot(dev(q), r), rot(dev(s), r), rot(dev(b), r)
+        dx = dev(x)
+        qo = torch.empty((c["m"], c["q_sp"]), dtype=torch.float32, device="cuda")
+        ko = torch.empty((c["m"], c["k_sp"]), dtype=torch.float32, device="cuda")
+        vo = torch.empty((c["m"], c["v_sp"]), dtype=torch.float32, device="cuda")
+        nb = wbytes + x.nbytes + c["m"] * c["n"] * 4
+        cases.append(Case("prefill_qkv_fused_512x2048", "affine gs64 M=512 N=8192 K=2048 -> q|k|v (MFMA, split epilogue)",
+                          nb, 2 * c["m"] * c["n"] * c["k"], r,
+                          lambda i, qs_=qs_, ss_=ss_, bs_=bs_, dx=dx, qo=qo, ko=ko, vo=vo, r=r, c=c:
+                          qg.qmm_affine_t_qkv(dx, qs_[i % r], ss_[i % r], bs_[i % r], c["gs"], c["q_sp"],
+                                              c["k_sp"], c["v_sp"], q_out=qo, k_out=ko, v_out=vo),
+                          bound="mfma"))
     return cases
 
 
@@ -177,17 +252,35 @@ def time_case(torch, case, steps, warmup):
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     reps = []
-    for _ in range(3):
+    for _ in range(REPS):
         torch.cuda.synchronize()
         e0.record(s)
         run()
         e1.record(s)
         torch.cuda.synchronize()
         reps.append(e0.elapsed_time(e1))
-    ms = reps[0]
+    ms = reps[0]  # the first timed replay is the figure reported; the others give the spread
     us = ms * 1e3 / steps
+    per_call = sorted(r * 1e3 / steps for r in reps)
+    # single cold call: write a 512 MiB buffer to push the operands out of the
+    # caches, then time one eager call
+    flush = torch.empty(128 << 20, dtype=torch.float32, device="cuda")
+    cold = []
+    for i in range(3):
+        flush.fill_(float(i))
+        torch.cuda.synchronize()
+        e0.record(s)
+        case.launch(i)
+        e1.record(s)
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1) * 1e3)
+    del flush
     out = {
         "desc": case.desc, "us_per_call": round(us, 3), "us_per_call_reps": [round(r * 1e3 / steps, 3) for r in reps],
+        "us_median": round(float(np.median(per_call)), 3),
+        "us_p10": round(float(np.percentile(per_call, 10)), 3),
+        "us_p90": round(float(np.percentile(per_call, 90)), 3),
+        "us_cold_single_call": round(float(np.median(cold)), 3),
         "bytes": case.nbytes, "GBps": round(case.nbytes / (us * 1e-6) / 1e9, 1),
         "frac_hbm_peak": round(case.nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "graph": graph is not None, "rotation_copies": case.copies, "steps": steps,

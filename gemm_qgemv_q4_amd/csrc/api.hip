@@ -95,66 +95,114 @@ template <> int64_t row_bytes_of<FMT_AFF4>(int64_t k) { return k / 2; }
 
 // ------------------------------------------------------------------ GEMV
 struct GemvPlan {
-  int mt, l, r, waves, kt, bpc;
+  int mt, l, r, kt;
   size_t lds;
   bool persistent;
+  int waves_env, bpc_env;  // tuning override (0: automatic)
 };
 
-// Launch shape of the chunked GEMV kernel.  x of one m-tile is staged in LDS
+// Launch shape of the chunked GEMV kernel that fixes its arithmetic: rows of
+// x per tile (MT), lanes per row (L), row sets per wave (R) and the x tile.
+// It depends on the format, M and K only, so the arithmetic of an output
+// never depends on N or on the part list.  x of one m-tile is staged in LDS
 // once per workgroup when it fits (persistent workgroups walk several row
-// groups); otherwise each workgroup owns one row group and stages x in K tiles.
-// The shape depends on M and K only, so the arithmetic of an output never
-// depends on N or on the part list.
+// groups); otherwise each workgroup owns one row group and stages x in K
+// tiles.  Measured on MI355X (graph replay of the 4096^2 Q4 and 12288x4096
+// affine decode shapes): Q4 formats are fastest with 32 lanes per row and
+// one row set at every M; affine codes with 64 lanes and two row sets.
 template <int FMT>
 GemvPlan plan_gemv(int64_t m, int64_t k, int nw) {
   constexpr int CH = FmtTraits<FMT>::CH;
   constexpr bool SUMS = FmtTraits<FMT>::SUMS;
+  constexpr bool Q4 = FMT == FMT_Q40 || FMT == FMT_Q4K;
   GemvPlan pl{};
   const int64_t chunks = k / CH;
   pl.mt = m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : 8;
-  // Measured on MI355X: at MT >= 4 two rows per wave side by side (L = 32) and
-  // one 512-thread workgroup per CU are best; at MT <= 2 a full wave per row.
-  // Rows shorter than 32 chunks still get 32 lanes (two rows per wave; the
-  // lanes past the row's end idle), which measured faster than narrower groups.
-  const int lmax = pl.mt >= 4 ? 32 : 64;
-  pl.l = chunks >= lmax ? lmax : 32;
+  pl.l = Q4 ? 32 : (chunks >= 64 ? 64 : 32);
+  int r = 1;
+  if (!Q4 && chunks >= 64 && (pl.mt * nw <= 2 || (nw == 1 && pl.mt == 8))) r = 2;
   auto lds_for = [&](int64_t kt) {
     const int64_t ct = kt / CH;
     return (size_t)(pl.mt * (CH / 4) * (ct + 1) * 16 + (SUMS ? pl.mt * ct * 8 : 0));
   };
-  // Tuning override "L,R,W,B" (0 keeps the automatic choice; B = workgroups per CU
-  // of the persistent grid), e.g. QG_GEMV_PLAN=32,2,4,2
+  // Tuning override "L,R,W,B" (0 keeps the automatic choice; W = waves per
+  // workgroup, B = workgroups per CU of the persistent grid), e.g.
+  // QG_GEMV_PLAN=32,1,8,0
   int el = 0, er = 0, ew = 0, eb = 0;
   if (const char* env = getenv("QG_GEMV_PLAN")) {
     if (sscanf(env, "%d,%d,%d,%d", &el, &er, &ew, &eb) < 1) el = er = ew = eb = 0;
   }
   if (el == 8 || el == 16 || el == 32 || el == 64) pl.l = el;
-  int r = (pl.mt * nw <= 2 && chunks >= 64) ? 2 : 1;
-  if (er == 1 || (er == 2 && pl.mt * nw <= 2) || (er == 4 && pl.mt * nw == 1)) r = er;
+  if (er == 1 || (er == 2 && (pl.mt * nw <= 2 || (nw == 1 && pl.mt == 8))) || (er == 4 && pl.mt * nw == 1)) r = er;
   pl.r = r;
-
+  pl.waves_env = (ew == 1 || ew == 2 || ew == 4 || ew == 8) ? ew : 0;
+  pl.bpc_env = (eb >= 1 && eb <= 8) ? eb : 0;
   pl.persistent = lds_for(k) <= kLdsPersistent;
   if (pl.persistent) {
     pl.kt = (int)k;
     pl.lds = lds_for(k);
-    pl.waves = ((FMT == FMT_AFF || FMT == FMT_AFF4) && pl.mt <= 2) ? 4 : 8;
-    if (ew == 1 || ew == 2 || ew == 4 || ew == 8) pl.waves = ew;
-    int bpc = (int)(kLdsMax / (pl.lds ? pl.lds : 1));
-    const int bpc_max = pl.waves == 8 ? 1 : 4;
-    bpc = bpc < 1 ? 1 : bpc > bpc_max ? bpc_max : bpc;
-    if (eb >= 1 && eb <= 8 && (size_t)eb * pl.lds <= kLdsMax) bpc = eb;
-    pl.bpc = bpc;
   } else {
-    pl.waves = 4;
-    if (ew == 1 || ew == 2 || ew == 4) pl.waves = ew;
     const int64_t step = (int64_t)pl.l * CH;
     int64_t kt = step;
     while (kt + step <= k && lds_for(kt + step) <= kLdsBudget) kt += step;
     pl.kt = (int)kt;
     pl.lds = lds_for(kt);
-    pl.bpc = 0;
   }
   return pl;
+}
+
+// Waves per workgroup and the grid, which do not change the arithmetic.  A
+// persistent workgroup stages x once and walks row groups; every workgroup
+// should walk the same number of them (a partly filled last round leaves CUs
+// idle), so the shape with the best balance wins, then the preferred one:
+// 8 waves (one workgroup per CU) except for affine codes at M <= 2.
+struct GemvGrid {
+  int waves;
+  int64_t groups_rows;  // rows per group
+  int64_t grid;
+};
+
+template <int FMT>
+GemvGrid grid_gemv(const GemvPlan& pl, const HostPart* parts, int nparts) {
+  const int64_t cus = device_cus();
+  auto groups_for = [&](int64_t rpg) {
+    int64_t g = 0;
+    for (int pi = 0; pi < nparts; ++pi) g += cdiv(parts[pi].n, rpg);
+    return g;
+  };
+  const int pref = ((FMT == FMT_AFF || FMT == FMT_AFF4) && pl.mt <= 2) ? 4 : 8;
+  GemvGrid best{};
+  if (!pl.persistent) {
+    best.waves = pl.waves_env ? pl.waves_env : 4;
+    best.groups_rows = (int64_t)best.waves * (64 / pl.l) * pl.r;
+    best.grid = groups_for(best.groups_rows);
+    return best;
+  }
+  double best_eff = -1.0;
+  const int cand[2] = {pref, pref == 8 ? 4 : 8};
+  for (int ci = 0; ci < 2; ++ci) {
+    const int w = pl.waves_env ? pl.waves_env : cand[ci];
+    if (ci == 1 && pl.waves_env) break;
+    const int64_t rpg = (int64_t)w * (64 / pl.l) * pl.r;
+    const int64_t groups = groups_for(rpg);
+    int fit = (int)(kLdsMax / (pl.lds ? pl.lds : 1));
+    const int cap_b = w == 8 ? 1 : 4;
+    fit = fit < 1 ? 1 : fit > cap_b ? cap_b : fit;
+    int b_lo = 1, b_hi = fit;
+    if (pl.bpc_env && (size_t)pl.bpc_env * pl.lds <= kLdsMax) b_lo = b_hi = pl.bpc_env;
+    for (int b = b_hi; b >= b_lo; --b) {
+      const int64_t slots = cus * b;
+      const int64_t used = groups < slots ? groups : slots;
+      const double eff = (double)groups / (double)(cdiv(groups, slots) * used);
+      if (eff > best_eff + 1e-9) {
+        best_eff = eff;
+        best.waves = w;
+        best.groups_rows = rpg;
+        best.grid = used;
+      }
+    }
+  }
+  return best;
 }
 
 template <int FMT, int MT, int NW, int L, int R>
@@ -200,7 +248,7 @@ hipError_t launch_gemv_r(int r, const GemvParams& p, dim3 g, dim3 b, size_t lds,
       if constexpr (MT * NW == 1) return launch_gemv_t<FMT, MT, NW, L, 4>(p, g, b, lds, s);
       break;
     case 2:
-      if constexpr (MT * NW <= 2) return launch_gemv_t<FMT, MT, NW, L, 2>(p, g, b, lds, s);
+      if constexpr (MT * NW <= 2 || (NW == 1 && MT == 8)) return launch_gemv_t<FMT, MT, NW, L, 2>(p, g, b, lds, s);
       break;
     case 1: return launch_gemv_t<FMT, MT, NW, L, 1>(p, g, b, lds, s);
   }
@@ -262,7 +310,8 @@ qg_status run_gemv(const char* op, const HostPart* parts, int nparts, const floa
     return launch_status(op);
   }
   const GemvPlan pl = plan_gemv<FMT>(m, k, NW);
-  const int rows_per_group = pl.waves * (64 / pl.l) * pl.r;
+  const GemvGrid gg = grid_gemv<FMT>(pl, parts, nparts);
+  const int rows_per_group = (int)gg.groups_rows;
   GemvParams p{};
   int64_t groups = 0;
   for (int pi = 0; pi < nparts; ++pi) {
@@ -285,12 +334,8 @@ qg_status run_gemv(const char* op, const HostPart* parts, int nparts, const floa
   p.gs = gs;
   p.kt = pl.kt;
   p.rows_per_block = rows_per_group;
-  int64_t grid = groups;
-  if (pl.persistent) {
-    const int64_t cap = (int64_t)device_cus() * pl.bpc;
-    grid = groups < cap ? groups : cap;
-  }
-  const dim3 block(64 * pl.waves);
+  const int64_t grid = gg.grid;
+  const dim3 block(64 * gg.waves);
   for (int64_t m0 = 0; m0 < m; m0 += pl.mt) {
     GemvParams q = p;
     q.x = x + m0 * k;
@@ -438,9 +483,9 @@ template <int FMT>
 qg_status run_affine(const char* op, const HostPart* parts, int nparts, const float* x, int64_t m, int64_t k,
                      int64_t gs, hipStream_t s) {
   if (mfma_ok<FMT>(parts, nparts, m, k, gs)) return run_mfma<FMT>(op, parts, nparts, x, m, k, (int)gs, s);
-  bool plain = (k % 16 != 0) || gs < 16;
-  const uintptr_t al = FMT == FMT_AFF ? 16 : 8;
-  for (int pi = 0; pi < nparts; ++pi) plain = plain || !aligned(parts[pi].w[0], al);
+  // the chunked kernel takes 32-code chunks inside one group
+  bool plain = (k % 32 != 0) || gs < 32;
+  for (int pi = 0; pi < nparts; ++pi) plain = plain || !aligned(parts[pi].w[0], 16);
   return run_gemv<FMT, 1>(op, parts, nparts, x, m, k, (int)gs, plain, s);
 }
 

@@ -16,18 +16,20 @@
 // pages' Metal kernels):
 //   * A row of weights is cut into "chunks" of CH weights (64 for Q4_0 = two
 //     blocks = 36 contiguous bytes; 64 for Q4_K = one 32-byte nibble run of a
-//     super-block plus its 16-byte header; 16 for affine = one 16-byte code
-//     load).  Consecutive lanes take consecutive chunks, so every wave-wide
-//     load instruction covers contiguous memory of one row.
+//     super-block plus its 16-byte header; 32 for affine = 32 u8 codes or 16
+//     bytes of packed codes, inside one group since group sizes of 32 and up
+//     take this kernel).  Consecutive lanes take consecutive chunks, so every
+//     wave-wide load instruction covers contiguous memory of one row.
 //   * L lanes serve one row; a wave serves P = 64/L rows side by side and R
 //     such row sets one after the other; each lane keeps NW*R*MT f32
 //     accumulators (NW = 1, or 2 for the dual projection).
 //   * x (MT rows of the activation) is staged once per workgroup in LDS as
 //     float4 columns [m][e4][chunk] (e4 = which 4 elements of the chunk), so
 //     the lanes of a wave read consecutive 16-byte words (no bank conflicts)
-//     and every x word read feeds R*NW rows.  For Q4_0/Q4_K the per-32 sums of
-//     x are staged too, which lets the block offset (-8*d, -dmin*m) be applied
-//     once per 32 weights instead of once per weight.
+//     and every x word read feeds R*NW rows.  The per-32 sums of x are staged
+//     too, which lets the block offset (-8*d, -dmin*m, or the affine bias b)
+//     and the affine scale be applied once per 32 weights instead of once per
+//     weight: the inner loop is one code conversion and one FMA per weight.
 //   * The lanes of a row are summed with a fixed xor butterfly: no atomics,
 //     and the arithmetic of one output does not depend on R, NW, MT, the
 //     number of waves or which part a row belongs to, which makes the dual
@@ -69,14 +71,14 @@ struct GemvParams {
 template <int FMT> struct FmtTraits;
 template <> struct FmtTraits<FMT_Q40> { static constexpr int CH = 64; static constexpr bool SUMS = true; };
 template <> struct FmtTraits<FMT_Q4K> { static constexpr int CH = 64; static constexpr bool SUMS = true; };
-template <> struct FmtTraits<FMT_AFF> { static constexpr int CH = 16; static constexpr bool SUMS = false; };
-template <> struct FmtTraits<FMT_AFF4> { static constexpr int CH = 16; static constexpr bool SUMS = false; };
+template <> struct FmtTraits<FMT_AFF> { static constexpr int CH = 32; static constexpr bool SUMS = true; };
+template <> struct FmtTraits<FMT_AFF4> { static constexpr int CH = 32; static constexpr bool SUMS = true; };
 
 // Raw bytes of one chunk of one row.
 struct ChunkQ40 { u32x4a4 a; u32x4a4 b; uint32_t c; };   // 36 bytes: blocks 2t, 2t+1
 struct ChunkQ4K { u32x4 h; u32x4 qa; u32x4 qb; };         // header + 32 nibble bytes
-struct ChunkAff { u32x4 q; float s; float b; };           // 16 codes + their group's s, b
-struct ChunkAff4 { uint32_t q0, q1; float s; float b; };  // 16 packed codes + s, b
+struct ChunkAff { u32x4 qa, qb; float s; float b; };     // 32 codes + their group's s, b
+struct ChunkAff4 { u32x4 q; float s; float b; };          // 32 packed codes + s, b
 
 template <int FMT> struct ChunkOf;
 template <> struct ChunkOf<FMT_Q40> { using T = ChunkQ40; };
@@ -104,37 +106,36 @@ __device__ __forceinline__ typename ChunkOf<FMT>::T load_chunk(const GemvParams&
     c.qb = *(const u32x4*)(base + 32 + 32 * (tg & 3));
   } else {
     if constexpr (FMT == FMT_AFF) {
-      c.q = *(const u32x4*)(rw + 16 * (size_t)tg);
+      c.qa = *(const u32x4*)(rw + 32 * (size_t)tg);
+      c.qb = *(const u32x4*)(rw + 32 * (size_t)tg + 16);
     } else {
-      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-      const u32x2 v = *(const u32x2*)(rw + 8 * (size_t)tg);
-      c.q0 = v.x;
-      c.q1 = v.y;
+      c.q = *(const u32x4*)(rw + 16 * (size_t)tg);
     }
     const int groups = p.k / p.gs;
-    const size_t gi = (size_t)row * groups + (16 * tg) / p.gs;
+    const size_t gi = (size_t)row * groups + (32 * tg) / p.gs;
     c.s = sc[gi];
     c.b = bi[gi];
   }
   return c;
 }
 
-// The four u32 words of byte codes (element order, one code per byte) of an
-// affine chunk.  Packed codes: word q0 holds elements 0..7 as nibbles; the
+// The eight u32 words of byte codes (element order, one code per byte) of an
+// affine chunk.  Packed codes: each word holds eight elements as nibbles; the
 // even elements are its low nibbles, the odd ones its high nibbles, and a
 // byte permute interleaves them back into element order.
-__device__ __forceinline__ void aff_words(const ChunkAff& c, uint32_t (&qd)[4]) {
-  qd[0] = c.q.x;
-  qd[1] = c.q.y;
-  qd[2] = c.q.z;
-  qd[3] = c.q.w;
-}
-__device__ __forceinline__ void aff_words(const ChunkAff4& c, uint32_t (&qd)[4]) {
-  const uint32_t w2[2] = {c.q0, c.q1};
+__device__ __forceinline__ void aff_words(const ChunkAff& c, uint32_t (&qd)[8]) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const uint32_t ev = w2[i] & 0x0F0F0F0Fu;         // elements 0, 2, 4, 6 of the word
-    const uint32_t od = (w2[i] >> 4) & 0x0F0F0F0Fu;  // elements 1, 3, 5, 7
+  for (int i = 0; i < 4; ++i) {
+    qd[i] = c.qa[i];
+    qd[4 + i] = c.qb[i];
+  }
+}
+__device__ __forceinline__ void aff_words(const ChunkAff4& c, uint32_t (&qd)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = c.q[i];
+    const uint32_t ev = w & 0x0F0F0F0Fu;         // elements 0, 2, 4, 6 of the word
+    const uint32_t od = (w >> 4) & 0x0F0F0F0Fu;  // elements 1, 3, 5, 7
     // v_perm_b32(od, ev, sel): byte selector 0..3 = ev bytes, 4..7 = od bytes
     qd[2 * i] = __builtin_amdgcn_perm(od, ev, 0x05010400u);
     qd[2 * i + 1] = __builtin_amdgcn_perm(od, ev, 0x07030602u);
@@ -170,29 +171,27 @@ __device__ __forceinline__ HalfScales q4k_scales(const ChunkQ4K& c, int cc) {
   return {d * ubyte_f32<0>(scp), -(dmin * ubyte_f32<0>(mp)), d * ubyte_f32<1>(scp), -(dmin * ubyte_f32<1>(mp))};
 }
 
-// The 16 dwords of nibble values (each byte 0..15) of a 64-weight chunk, in
-// element order: dword e4 holds elements 4*e4 .. 4*e4+3.
-__device__ __forceinline__ void unpack_q40(const ChunkQ40& c, uint32_t (&v)[16]) {
-  // block 2t: nibble bytes start at byte 2 -> realign across dwords 0..4
+// The 8 dwords of nibble values (each byte 0..15) of half h (32 weights) of a
+// 64-weight chunk, in element order: dword i holds elements 4i .. 4i+3 of the
+// half.  Unpacking one half at a time keeps half the nibble registers live.
+__device__ __forceinline__ void unpack_q40(const ChunkQ40& c, int h, uint32_t (&v)[8]) {
   const uint32_t d[9] = {c.a.x, c.a.y, c.a.z, c.a.w, c.b.x, c.b.y, c.b.z, c.b.w, c.c};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t qa = __builtin_amdgcn_alignbyte(d[i + 1], d[i], 2);
-    v[i] = opaque(qa & 0x0F0F0F0Fu);             // elements 4i..4i+3 of block 2t
-    v[4 + i] = opaque((qa >> 4) & 0x0F0F0F0Fu);  // elements 16+4i.. of block 2t
-    const uint32_t qb = d[5 + i];                // block 2t+1: nibbles at bytes 20..35
-    v[8 + i] = opaque(qb & 0x0F0F0F0Fu);
-    v[12 + i] = opaque((qb >> 4) & 0x0F0F0F0Fu);
+    // block 2t: nibble bytes start at byte 2 -> realign across dwords 0..4;
+    // block 2t+1: nibbles at bytes 20..35 = dwords 5..8
+    const uint32_t q = h == 0 ? __builtin_amdgcn_alignbyte(d[i + 1], d[i], 2) : d[5 + i];
+    v[i] = opaque(q & 0x0F0F0F0Fu);             // elements 4i..4i+3 of the block
+    v[4 + i] = opaque((q >> 4) & 0x0F0F0F0Fu);  // elements 16+4i.. of the block
   }
 }
 
-__device__ __forceinline__ void unpack_q4k(const ChunkQ4K& c, uint32_t (&v)[16]) {
+__device__ __forceinline__ void unpack_q4k(const ChunkQ4K& c, int h, uint32_t (&v)[8]) {
   const uint32_t q[8] = {c.qa.x, c.qa.y, c.qa.z, c.qa.w, c.qb.x, c.qb.y, c.qb.z, c.qb.w};
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    v[i] = opaque(q[i] & 0x0F0F0F0Fu);             // sub-block 2c: low nibbles
-    v[8 + i] = opaque((q[i] >> 4) & 0x0F0F0F0Fu);  // sub-block 2c+1: high nibbles
-  }
+  for (int i = 0; i < 8; ++i)
+    v[i] = opaque(h == 0 ? q[i] & 0x0F0F0F0Fu            // sub-block 2c: low nibbles
+                         : (q[i] >> 4) & 0x0F0F0F0Fu);   // sub-block 2c+1: high nibbles
 }
 
 // Decode one chunk of every (stream, row) and accumulate it.
@@ -203,11 +202,19 @@ __device__ __forceinline__ void compute_chunk(const typename ChunkOf<FMT>::T (&c
   constexpr int CH = FmtTraits<FMT>::CH;
   constexpr int NE4 = CH / 4;
   if constexpr (FMT == FMT_AFF || FMT == FMT_AFF4) {
-    uint32_t words[NW][R][4];
+    // the chunk lies in one group: acc += s * sum(x q) + b * sum(x)
+    uint32_t words[NW][R][8];
 #pragma unroll
     for (int s = 0; s < NW; ++s)
 #pragma unroll
       for (int r = 0; r < R; ++r) aff_words(ch[s][r], words[s][r]);
+    float sub[NW][R][MT];
+#pragma unroll
+    for (int s = 0; s < NW; ++s)
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) sub[s][r][m] = 0.0f;
 #pragma unroll
     for (int e4 = 0; e4 < NE4; ++e4) {
       f32x4 xv[MT];
@@ -218,39 +225,51 @@ __device__ __forceinline__ void compute_chunk(const typename ChunkOf<FMT>::T (&c
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           const uint32_t qd = opaque(words[s][r][e4]);
-          const float sc = ch[s][r].s, bi = ch[s][r].b;
-          const float w0 = __builtin_fmaf(sc, ubyte_f32<0>(qd), bi);
-          const float w1 = __builtin_fmaf(sc, ubyte_f32<1>(qd), bi);
-          const float w2 = __builtin_fmaf(sc, ubyte_f32<2>(qd), bi);
-          const float w3 = __builtin_fmaf(sc, ubyte_f32<3>(qd), bi);
+          const float q0 = ubyte_f32<0>(qd), q1 = ubyte_f32<1>(qd);
+          const float q2 = ubyte_f32<2>(qd), q3 = ubyte_f32<3>(qd);
 #pragma unroll
           for (int m = 0; m < MT; ++m) {
-            float a = acc[s][r][m];
-            a = __builtin_fmaf(xv[m].x, w0, a);
-            a = __builtin_fmaf(xv[m].y, w1, a);
-            a = __builtin_fmaf(xv[m].z, w2, a);
-            a = __builtin_fmaf(xv[m].w, w3, a);
-            acc[s][r][m] = a;
+            float a = sub[s][r][m];
+            a = __builtin_fmaf(xv[m].x, q0, a);
+            a = __builtin_fmaf(xv[m].y, q1, a);
+            a = __builtin_fmaf(xv[m].z, q2, a);
+            a = __builtin_fmaf(xv[m].w, q3, a);
+            sub[s][r][m] = a;
           }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const float sx = xsum[(m * ct_max + t) * 2];
+#pragma unroll
+      for (int s = 0; s < NW; ++s)
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          float a = acc[s][r][m];
+          a = __builtin_fmaf(ch[s][r].s, sub[s][r][m], a);
+          a = __builtin_fmaf(ch[s][r].b, sx, a);
+          acc[s][r][m] = a;
         }
     }
   } else {
     HalfScales hs[NW][R];
-    uint32_t nib[NW][R][16];
 #pragma unroll
     for (int s = 0; s < NW; ++s)
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        if constexpr (FMT == FMT_Q40) {
-          hs[s][r] = q40_scales(ch[s][r]);
-          unpack_q40(ch[s][r], nib[s][r]);
-        } else {
-          hs[s][r] = q4k_scales(ch[s][r], tg & 3);
-          unpack_q4k(ch[s][r], nib[s][r]);
-        }
+        if constexpr (FMT == FMT_Q40) hs[s][r] = q40_scales(ch[s][r]);
+        else hs[s][r] = q4k_scales(ch[s][r], tg & 3);
       }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+      uint32_t nib[NW][R][8];
+#pragma unroll
+      for (int s = 0; s < NW; ++s)
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          if constexpr (FMT == FMT_Q40) unpack_q40(ch[s][r], h, nib[s][r]);
+          else unpack_q4k(ch[s][r], h, nib[s][r]);
+        }
       float sub[NW][R][MT];
 #pragma unroll
       for (int s = 0; s < NW; ++s)
@@ -268,7 +287,7 @@ __device__ __forceinline__ void compute_chunk(const typename ChunkOf<FMT>::T (&c
         for (int s = 0; s < NW; ++s)
 #pragma unroll
           for (int r = 0; r < R; ++r) {
-            const uint32_t v = nib[s][r][e4];
+            const uint32_t v = nib[s][r][e];
             const float q0 = ubyte_f32<0>(v), q1 = ubyte_f32<1>(v);
             const float q2 = ubyte_f32<2>(v), q3 = ubyte_f32<3>(v);
 #pragma unroll
@@ -518,8 +537,8 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams p) {
 
 // ---------------------------------------------------------------------------
 // Plain kernel for shapes and alignments the chunked kernel does not take
-// (K not a multiple of 64 for Q4_0, misaligned Q4_K rows, affine K % 16 != 0,
-// group_size < 16 or misaligned codes): one thread per output, sequential f32
+// (K not a multiple of 64 for Q4_0, misaligned Q4_K rows, affine K % 32 != 0,
+// group_size < 32 or misaligned codes): one thread per output, sequential f32
 // sum over K.  Launched once per part.
 struct PlainParams {
   const uint8_t* w[2];

@@ -143,8 +143,8 @@ qg_status qgemv_q4_k_multi(const void* const* w, float* const* y, const int64_t*
  *   x : [M, K] f32;  y : [M, N] f32.
  *   group_size : power of two in [2, 1024], K % group_size == 0, K % 8 == 0.
  *   (The page's kernel takes group_size 32 only; any group size is taken here.)
- * Bitwise equal to qmm_affine_t on the unpacked u8 codes when w_packed is
- * 8-byte aligned and the u8 codes 16-byte aligned.  Half the weight bytes.
+ * Bitwise equal to qmm_affine_t on the unpacked u8 codes when w_packed and
+ * the u8 codes are both 16-byte aligned.  Half the weight bytes.
  * Errors: as qmm_affine_t; K % 8 != 0.
  */
 qg_status qmm_affine_t_packed(const float* x, const uint32_t* w_packed, const float* scales,

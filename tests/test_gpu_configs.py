@@ -1,4 +1,4 @@
-"""Full-size parity on the five benchmark workloads, in the launch configuration
+"""Full-size parity on the benchmark workloads, in the launch configuration
 bench.py times (same entry points, same shapes, default variant choice).
 The oracle finishes every one of these in seconds on the host, so every output
 element is compared, not a sample."""
@@ -64,3 +64,56 @@ def test_config_prefill_qkv_512x2048(lib):
     rq, rk, rv = oracle.qkv_split_f32(qkv_h, c["m"], c["q_sp"], c["k_sp"], c["v_sp"])
     for got, ref in ((qo, rq), (ko, rk), (vo, rv)):
         assert np.array_equal(host(got).view(np.uint32), ref.view(np.uint32))
+
+
+# ------------------------------------------------------------------ follow-on paths, full size
+NXT = synth.NEXT_CONFIGS
+
+
+def test_config_q4_k_qkv_multi_4096(lib):
+    c = NXT["q4_k_qkv_multi_4096"]
+    ns, k = list(c["ns"]), c["k"]
+    ws, x = synth.q4_k_multi_case(c["seed"], c["m"], ns, k)
+    dws, dx = [dev(w) for w in ws], dev(x)
+    y = host(lib.qgemv_q4_k_multi(dws, dx, ns, k))
+    col = 0
+    for w, dw, n in zip(ws, dws, ns):
+        single = host(lib.qgemv_q4_k(dw, dx, n, k))
+        assert np.array_equal(y[:, col:col + n].view(np.uint32), single.view(np.uint32))
+        assert_close(y[:, col:col + n], oracle.decode_q4_k(w, n, k), x, f"C multi col {col}")
+        col += n
+
+
+@pytest.mark.parametrize("m", [1, 8])
+def test_config_affine_b4_12288x4096(lib, m):
+    import torch
+    c = NXT["affine_b4_12288x4096_gs64"]
+    x8, q, s, b = synth.affine_case(c["seed"], c["m"], c["n"], c["k"], c["gs"])
+    x = np.ascontiguousarray(x8[:m])
+    wp = synth.pack_b4_u32(q)
+    dx, ds, db = dev(x), dev(s), dev(b)
+    y = host(lib.qmm_affine_t_packed(dx, torch.from_numpy(wp.view(np.int32)).cuda(), ds, db, c["gs"]))
+    y8 = host(lib.qmm_affine_t(dx, dev(q), ds, db, c["gs"]))
+    assert np.array_equal(y.view(np.uint32), y8.view(np.uint32))
+    assert_close(y, oracle.decode_affine_b4(wp, s, b, c["n"], c["k"], c["gs"]), x, f"C packed m{m}")
+
+
+def test_config_q4_0_prefill_512x4096(lib):
+    c = NXT["q4_0_prefill_512x4096"]
+    assert c["m"] >= lib.qg_get_mfma_min_m()  # the matrix-core path is the one timed
+    w, x = synth.q4_0_case(c["seed"], c["m"], c["n"], c["k"])
+    y = host(lib.qgemv_q4_0(dev(w), dev(x), c["n"], c["k"]))
+    assert_close(y, oracle.decode_q4_0(w, c["n"], c["k"]), x, "C q4_0 prefill")
+
+
+def test_config_prefill_qkv_fused_512x2048(lib):
+    c = CFG["prefill_qkv_512x2048"]
+    x, q, s, b = synth.affine_case(c["seed"], c["m"], c["n"], c["k"], c["gs"])
+    dx, dq, ds, db = dev(x), dev(q), dev(s), dev(b)
+    outs = lib.qmm_affine_t_qkv(dx, dq, ds, db, c["gs"], c["q_sp"], c["k_sp"], c["v_sp"])
+    qkv = lib.qmm_affine_t(dx, dq, ds, db, c["gs"])
+    refs = lib.qkv_split_f32(qkv, c["m"], c["q_sp"], c["k_sp"], c["v_sp"])
+    for got, ref in zip(outs, refs):
+        assert np.array_equal(host(got).view(np.uint32), host(ref).view(np.uint32))
+    y = np.concatenate([host(t) for t in outs], axis=1)
+    assert_close(y, oracle.decode_affine(q, s, b, c["n"], c["k"], c["gs"]), x, "C fused qkv")
