@@ -263,12 +263,13 @@ def time_case(torch, case, steps, warmup):
     us = ms * 1e3 / steps
     per_call = sorted(r * 1e3 / steps for r in reps)
     # single cold call: write a 512 MiB buffer to push the operands out of the
-    # caches, then time one eager call
+    # caches, then time one call.  The events and the call are queued while the
+    # fill still runs, so the events bracket GPU time only (no host launch gap).
     flush = torch.empty(128 << 20, dtype=torch.float32, device="cuda")
     cold = []
     for i in range(3):
-        flush.fill_(float(i))
         torch.cuda.synchronize()
+        flush.fill_(float(i))
         e0.record(s)
         case.launch(i)
         e1.record(s)

@@ -22,12 +22,12 @@
 // Kernels:
 //   affine_prep_kernel : x [M,K] f32 -> x_hi, x_lo [M,K] bf16 and X [M, K/gs]
 //                        as bf16 hi, lo.
-//   qmm_mfma_kernel<F> : 128x128 output tile per 512-thread workgroup (eight
-//                        waves: 2x2 sub-tiles of 64x64, each shared by two
-//                        waves that split every 64-wide K stage).  Column
-//                        tiles are numbered part after part (up to kMaxParts
-//                        weight tensors sharing x), so a tile's part is
-//                        uniform.
+//   qmm_mfma_kernel<F, MULTI, SM, SN> : a (64 SM) x (64 SN) output tile per
+//                        workgroup of 2*SM*SN waves: SM x SN sub-tiles of
+//                        64x64, each shared by two waves that split every
+//                        64-wide K stage.  Column tiles are numbered part after
+//                        part (up to kMaxParts weight tensors sharing x), so a
+//                        tile's part is uniform.
 #pragma once
 #include "common.hpp"
 
@@ -109,11 +109,8 @@ struct MfmaParams {
   int tiles_m, tiles_n;  // tiles_n over all parts
 };
 
-constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kBK = 64;
 constexpr int kPitch = kBK + 8;  // bf16 elements per LDS row (144 bytes)
-constexpr int kTileElems = kBM * kPitch;
-
-struct StageRegs { u32x4 ah[2], al[2], b; uint32_t b4; };
 
 // Scale s[row, g] and bias b[row, g] of group g (group size 32 for the block
 // formats) of weight row `row` of part `pt`.
@@ -182,26 +179,36 @@ __device__ __forceinline__ void mfma_substep(const __bf16* sAh, const __bf16* sA
   }
 }
 
-// 128x128 output tile per 512-thread workgroup: 8 waves, two per SIMD.  Waves
-// w and w+4 own the same 64x64 sub-tile (2x2 sub-tiles, 4x4 MFMA tiles each)
-// and split every 64-wide K stage: wave half 0 takes columns 0..31, half 1
-// columns 32..63.  Their partial sums meet in LDS at the end.  K runs through
-// two LDS buffers; each stage's global loads are issued one stage ahead into
-// registers (one barrier per stage).  When a group of gs columns is complete,
-// a wave scales its partial product: acc += s[n, g] * P.  The bias term
-// sum_g b[n,g] * X_g[m] is one more small matrix product at the end, with
-// both factors split into bf16 hi + lo (three MFMAs per 32 groups).
-template <int F, bool MULTI>
-__global__ void __launch_bounds__(512) qmm_mfma_kernel(MfmaParams p) {
-  __shared__ __attribute__((aligned(16))) __bf16 sA[2][2 * kTileElems];  // [buf][hi | lo]
-  __shared__ __attribute__((aligned(16))) __bf16 sB[2][kTileElems];
-  __shared__ float sS[2][2][kBN];  // [buf][group in stage][n]
+// One workgroup computes a (64*SM) x (64*SN) output tile: SM x SN sub-tiles
+// of 64 x 64, each owned by a pair of waves (4 x 4 MFMA tiles each), so the
+// workgroup has 2*SM*SN waves and the CU runs two waves per SIMD.  The two
+// waves of a pair split every 64-wide K stage: wave half 0 takes columns
+// 0..31, half 1 columns 32..63; their partial sums meet in LDS at the end.  K
+// runs through two LDS buffers; each stage's global loads are issued one stage
+// ahead into registers (one barrier per stage).  When a group of gs columns is
+// complete, a wave scales its partial product: acc += s[n, g] * P.  The bias
+// term sum_g b[n,g] * X_g[m] is one more small matrix product at the end,
+// with both factors split into bf16 hi + lo (three MFMAs per 32 groups).
+// The arithmetic of one output element is the same for every (SM, SN), so
+// the host picks the tile shape from the tile count alone.
+template <int F, bool MULTI, int SM, int SN>
+__global__ void __launch_bounds__(128 * SM * SN, 4 / (SM * SN)) qmm_mfma_kernel(MfmaParams p) {
+  constexpr int T = 128 * SM * SN;  // threads
+  constexpr int NSUB = SM * SN;
+  constexpr int BM = 64 * SM, BN = 64 * SN;
+  constexpr int A_ELEMS = BM * kPitch, B_ELEMS = BN * kPitch;
+  constexpr int RA = 4 / SN;  // x rows each thread moves per stage (8 elements each, hi and lo)
+  constexpr int IB = 2 / SM;  // 16-code pieces of weights each thread moves per stage
+  __shared__ __attribute__((aligned(16))) __bf16 sA[2][2 * A_ELEMS];  // [buf][hi | lo]
+  __shared__ __attribute__((aligned(16))) __bf16 sB[2][B_ELEMS];
+  __shared__ float sS[2][2][BN];  // [buf][group in stage][n]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
-  const int kh = wid >> 2;            // which 32-column half of each stage
-  const int wm = (wid >> 1) & 1, wn = wid & 1;
+  const int kh = wid / NSUB;  // which 32-column half of each stage
+  const int sub = wid % NSUB;
+  const int wm = sub / SN, wn = sub % SN;
 
   // Tiles of one column block (same weights) are consecutive and the
   // dispatcher spreads consecutive ids over the 8 XCDs, so give each XCD a
@@ -221,7 +228,7 @@ __global__ void __launch_bounds__(512) qmm_mfma_kernel(MfmaParams p) {
     pt = p.part[pi];
   }
   const int n_rows = pt.n;
-  const int m0 = tm * kBM, n0 = (tn - pt.tile0) * kBN;  // n0: row of the part
+  const int m0 = tm * BM, n0 = (tn - pt.tile0) * BN;  // n0: row of the part
   const int groups = p.k / p.gs;
   const int stages = p.k / kBK;
   const int ng = p.gs < kBK ? kBK / p.gs : 1;  // groups per stage: 2 when gs == 32
@@ -235,58 +242,76 @@ __global__ void __launch_bounds__(512) qmm_mfma_kernel(MfmaParams p) {
       P[i][j] = acc[i][j];
     }
 
-  // Chunks this thread moves per stage: 8-element pieces of x_hi/x_lo rows
-  // a_row0 and a_row0 + 64, and 16 codes of weight row b_n (codes
-  // 16*b_kc .. 16*b_kc+15 of the stage's 64 columns).  Offsets are 32-bit
-  // offsets from the uniform base pointers (M*K elements and the part's
-  // weight bytes are below 2^31, checked on the host).  Rows past M or the
-  // part's rows read nothing (zeros).
+  // Pieces this thread moves per stage: 8-element pieces of x_hi/x_lo rows
+  // a_row0 + i*(T/8), and 16 codes of weight rows b_n[i] (codes 16*b_kc[i] ..
+  // 16*b_kc[i]+15 of the stage's 64 columns).  Offsets are 32-bit offsets
+  // from the uniform base pointers (M*K elements and the part's weight bytes
+  // are below 2^31, checked on the host).  Rows past M or the part's rows read
+  // nothing (zeros).
   const int a_row0 = tid >> 3, a_kc = tid & 7;
-  const int b_n = tid >> 2, b_kc = tid & 3;
-  const bool a_ok0 = m0 + a_row0 < p.m, a_ok1 = m0 + a_row0 + 64 < p.m;
-  const bool b_ok = n0 + b_n < n_rows;
-  const uint32_t a_off0 = (uint32_t)(a_ok0 ? m0 + a_row0 : 0) * (uint32_t)p.k + (uint32_t)(a_kc * 8);
-  const uint32_t a_off1 = (uint32_t)(a_ok1 ? m0 + a_row0 + 64 : 0) * (uint32_t)p.k + (uint32_t)(a_kc * 8);
-  const uint32_t b_row = (uint32_t)(b_ok ? n0 + b_n : 0) * (uint32_t)p.row_bytes;
-  const int s_row = n0 + (tid & 127) < n_rows ? n0 + (tid & 127) : n_rows - 1;
+  bool a_ok[RA];
+  uint32_t a_off[RA];
+#pragma unroll
+  for (int i = 0; i < RA; ++i) {
+    const int r = m0 + a_row0 + i * (T / 8);
+    a_ok[i] = r < p.m;
+    a_off[i] = (uint32_t)(a_ok[i] ? r : 0) * (uint32_t)p.k + (uint32_t)(a_kc * 8);
+  }
+  int b_n[IB], b_kc[IB];
+  bool b_ok[IB];
+  uint32_t b_row[IB];
+#pragma unroll
+  for (int i = 0; i < IB; ++i) {
+    const int it = tid + i * T;
+    b_n[i] = it >> 2;
+    b_kc[i] = it & 3;
+    b_ok[i] = n0 + b_n[i] < n_rows;
+    b_row[i] = (uint32_t)(b_ok[i] ? n0 + b_n[i] : 0) * (uint32_t)p.row_bytes;
+  }
+  const int s_row = n0 + (tid % BN) < n_rows ? n0 + (tid % BN) : n_rows - 1;
 
-  auto load = [&](int st, StageRegs& r) {
+  struct Regs { u32x4 ah[RA], al[RA], b[IB]; uint32_t b4[IB]; };
+  auto load = [&](int st, Regs& r) {
     const uint32_t k0 = (uint32_t)(st * kBK);
     const u32x4 z = {0u, 0u, 0u, 0u};
-    r.ah[0] = a_ok0 ? *(const u32x4*)(p.xh + (a_off0 + k0)) : z;
-    r.al[0] = a_ok0 ? *(const u32x4*)(p.xl + (a_off0 + k0)) : z;
-    r.ah[1] = a_ok1 ? *(const u32x4*)(p.xh + (a_off1 + k0)) : z;
-    r.al[1] = a_ok1 ? *(const u32x4*)(p.xl + (a_off1 + k0)) : z;
-    r.b = z;
-    r.b4 = 0u;
-    if (b_ok) {
-      if constexpr (F == FMT_AFF) {
-        r.b = *(const u32x4*)(pt.w + (b_row + k0 + 16u * b_kc));
-      } else if constexpr (F == FMT_AFF4) {
-        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-        const u32x2 v = *(const u32x2*)(pt.w + (b_row + k0 / 2u + 8u * b_kc));
-        r.b.x = v.x;
-        r.b.y = v.y;
-      } else if constexpr (F == FMT_Q40) {
-        // the stage's two blocks are 36 contiguous bytes at 36*st; block
-        // b_kc/2 has its 16 nibble bytes at 2 (block 0) or 20 (block 1): read
-        // the 20 bytes from 16*(b_kc/2) (4-byte aligned, inside the 36)
-        const uint8_t* base = pt.w + (b_row + 36u * st + 16u * (b_kc >> 1));
-        r.b = *(const u32x4a4*)base;
-        r.b4 = *(const uint32_t*)(base + 16);
-      } else {
-        // Q4_K: stage st is 64-column chunk (st & 3) of super-block st / 4;
-        // its 32 nibble bytes sit at 16 + 32*(st & 3); b_kc & 1 picks the half
-        r.b = *(const u32x4*)(pt.w + (b_row + 144u * (st >> 2) + 16u + 32u * (st & 3) + 16u * (b_kc & 1)));
+#pragma unroll
+    for (int i = 0; i < RA; ++i) {
+      r.ah[i] = a_ok[i] ? *(const u32x4*)(p.xh + (a_off[i] + k0)) : z;
+      r.al[i] = a_ok[i] ? *(const u32x4*)(p.xl + (a_off[i] + k0)) : z;
+    }
+#pragma unroll
+    for (int i = 0; i < IB; ++i) {
+      r.b[i] = z;
+      r.b4[i] = 0u;
+      if (b_ok[i]) {
+        if constexpr (F == FMT_AFF) {
+          r.b[i] = *(const u32x4*)(pt.w + (b_row[i] + k0 + 16u * b_kc[i]));
+        } else if constexpr (F == FMT_AFF4) {
+          typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+          const u32x2 v = *(const u32x2*)(pt.w + (b_row[i] + k0 / 2u + 8u * b_kc[i]));
+          r.b[i].x = v.x;
+          r.b[i].y = v.y;
+        } else if constexpr (F == FMT_Q40) {
+          // the stage's two blocks are 36 contiguous bytes at 36*st; block
+          // b_kc/2 has its 16 nibble bytes at 2 (block 0) or 20 (block 1): read
+          // the 20 bytes from 16*(b_kc/2) (4-byte aligned, inside the 36)
+          const uint8_t* base = pt.w + (b_row[i] + 36u * st + 16u * (b_kc[i] >> 1));
+          r.b[i] = *(const u32x4a4*)base;
+          r.b4[i] = *(const uint32_t*)(base + 16);
+        } else {
+          // Q4_K: stage st is 64-column chunk (st & 3) of super-block st / 4;
+          // its 32 nibble bytes sit at 16 + 32*(st & 3); b_kc & 1 picks the half
+          r.b[i] = *(const u32x4*)(pt.w + (b_row[i] + 144u * (st >> 2) + 16u + 32u * (st & 3) + 16u * (b_kc[i] & 1)));
+        }
       }
     }
   };
-  // The 16 codes of the thread's B chunk as bytes in element order.
-  auto code_words = [&](const StageRegs& r, uint32_t (&cw)[4]) {
+  // The 16 codes of a B piece as bytes in element order.
+  auto code_words = [&](const u32x4& b, uint32_t b4, int kc, uint32_t (&cw)[4]) {
     if constexpr (F == FMT_AFF) {
-      cw[0] = r.b.x; cw[1] = r.b.y; cw[2] = r.b.z; cw[3] = r.b.w;
+      cw[0] = b.x; cw[1] = b.y; cw[2] = b.z; cw[3] = b.w;
     } else if constexpr (F == FMT_AFF4) {
-      const uint32_t w2[2] = {r.b.x, r.b.y};
+      const uint32_t w2[2] = {b.x, b.y};
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const uint32_t ev = w2[i] & 0x0F0F0F0Fu, od = (w2[i] >> 4) & 0x0F0F0F0Fu;
@@ -296,40 +321,44 @@ __global__ void __launch_bounds__(512) qmm_mfma_kernel(MfmaParams p) {
     } else {
       uint32_t nb[4];
       if constexpr (F == FMT_Q40) {
-        const uint32_t d[5] = {r.b.x, r.b.y, r.b.z, r.b.w, r.b4};
+        const uint32_t d[5] = {b.x, b.y, b.z, b.w, b4};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) nb[i] = (b_kc >> 1) ? d[i + 1] : __builtin_amdgcn_alignbyte(d[i + 1], d[i], 2);
+        for (int i = 0; i < 4; ++i) nb[i] = (kc >> 1) ? d[i + 1] : __builtin_amdgcn_alignbyte(d[i + 1], d[i], 2);
       } else {
-        nb[0] = r.b.x; nb[1] = r.b.y; nb[2] = r.b.z; nb[3] = r.b.w;
+        nb[0] = b.x; nb[1] = b.y; nb[2] = b.z; nb[3] = b.w;
       }
       // Q4_0: low nibbles are elements 0..15 of the block, high ones 16..31;
       // Q4_K: low nibbles are the first sub-block of the chunk, high the second
-      const bool high = F == FMT_Q40 ? (b_kc & 1) : (b_kc >> 1);
+      const bool high = F == FMT_Q40 ? (kc & 1) : (kc >> 1);
 #pragma unroll
       for (int i = 0; i < 4; ++i) cw[i] = high ? (nb[i] >> 4) & 0x0F0F0F0Fu : nb[i] & 0x0F0F0F0Fu;
     }
   };
-  auto store = [&](int st, const StageRegs& r, int buf) {
+  auto store = [&](int st, const Regs& r, int buf) {
     __bf16* ah = sA[buf];
-    __bf16* al = sA[buf] + kTileElems;
-    *(u32x4*)(ah + a_row0 * kPitch + a_kc * 8) = r.ah[0];
-    *(u32x4*)(al + a_row0 * kPitch + a_kc * 8) = r.al[0];
-    *(u32x4*)(ah + (a_row0 + 64) * kPitch + a_kc * 8) = r.ah[1];
-    *(u32x4*)(al + (a_row0 + 64) * kPitch + a_kc * 8) = r.al[1];
-    // 16 codes -> 16 bf16 (exact: integers below 256)
-    uint32_t cw[4];
-    code_words(r, cw);
-    bf16x8 lo, hi;
+    __bf16* al = sA[buf] + A_ELEMS;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t wlo = cw[e >> 2], whi = cw[2 + (e >> 2)];
-      lo[e] = (__bf16)(float)((wlo >> (8 * (e & 3))) & 0xFFu);
-      hi[e] = (__bf16)(float)((whi >> (8 * (e & 3))) & 0xFFu);
+    for (int i = 0; i < RA; ++i) {
+      *(u32x4*)(ah + (a_row0 + i * (T / 8)) * kPitch + a_kc * 8) = r.ah[i];
+      *(u32x4*)(al + (a_row0 + i * (T / 8)) * kPitch + a_kc * 8) = r.al[i];
     }
-    *(bf16x8*)(sB[buf] + b_n * kPitch + b_kc * 16) = lo;
-    *(bf16x8*)(sB[buf] + b_n * kPitch + b_kc * 16 + 8) = hi;
+#pragma unroll
+    for (int i = 0; i < IB; ++i) {
+      // 16 codes -> 16 bf16 (exact: integers below 256)
+      uint32_t cw[4];
+      code_words(r.b[i], r.b4[i], b_kc[i], cw);
+      bf16x8 lo, hi;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t wlo = cw[e >> 2], whi = cw[2 + (e >> 2)];
+        lo[e] = (__bf16)(float)((wlo >> (8 * (e & 3))) & 0xFFu);
+        hi[e] = (__bf16)(float)((whi >> (8 * (e & 3))) & 0xFFu);
+      }
+      *(bf16x8*)(sB[buf] + b_n[i] * kPitch + b_kc[i] * 16) = lo;
+      *(bf16x8*)(sB[buf] + b_n[i] * kPitch + b_kc[i] * 16 + 8) = hi;
+    }
     const int g0 = st * kBK / p.gs;
-    if (tid < ng * kBN) sS[buf][tid >> 7][tid & 127] = group_scale<F>(pt, p.row_bytes, groups, s_row, g0 + (tid >> 7));
+    if (tid < ng * BN) sS[buf][tid / BN][tid % BN] = group_scale<F>(pt, p.row_bytes, groups, s_row, g0 + tid / BN);
   };
   auto scale_into_acc = [&](int buf, int gi) {
 #pragma unroll
@@ -344,7 +373,7 @@ __global__ void __launch_bounds__(512) qmm_mfma_kernel(MfmaParams p) {
   // this wave's 32-column half of stage st
   auto compute = [&](int st, int buf) {
     const __bf16* ah = sA[buf];
-    const __bf16* al = sA[buf] + kTileElems;
+    const __bf16* al = sA[buf] + A_ELEMS;
     if (p.gs == 32) {  // the half is a whole group
       mfma_substep<true>(ah, al, sB[buf], kh * 32, wm, wn, lane, P);
       scale_into_acc(buf, kh);
@@ -356,7 +385,7 @@ __global__ void __launch_bounds__(512) qmm_mfma_kernel(MfmaParams p) {
     if ((c0 + kBK) % p.gs == 0) scale_into_acc(buf, 0);
   };
 
-  StageRegs rg;
+  Regs rg;
   load(0, rg);
   store(0, rg, 0);
   __syncthreads();
@@ -369,8 +398,8 @@ __global__ void __launch_bounds__(512) qmm_mfma_kernel(MfmaParams p) {
   }
 
   // ---- combine the two K halves: half 1 hands its partial sums to half 0
-  float* red = reinterpret_cast<float*>(&sA[0][0]);  // 4 sub-tiles x 64 x 64 floats = 64 KB
-  float* mine = red + (size_t)(wm * 2 + wn) * 4096;
+  float* red = reinterpret_cast<float*>(&sA[0][0]);  // NSUB sub-tiles x 64 x 64 floats
+  float* mine = red + (size_t)sub * 4096;
   if (kh == 1) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -391,30 +420,34 @@ __global__ void __launch_bounds__(512) qmm_mfma_kernel(MfmaParams p) {
 
   // ---- bias term: acc += X[m, g] * b[n, g] over all groups, as a K = groups
   // product on the matrix cores with X and b split into bf16 hi + lo
+  constexpr int BR = BM > BN ? BM : BN;
   for (int g0 = 0; g0 < groups; g0 += 32) {
-    __bf16* xh_s = sA[1];                // [128 m][32 g], pitch kPitch
-    __bf16* xl_s = sA[1] + kTileElems;
-    __bf16* bh_s = sB[0];                // [128 n][32 g]
+    __bf16* xh_s = sA[1];  // [BM m][32 g], pitch kPitch
+    __bf16* xl_s = sA[1] + A_ELEMS;
+    __bf16* bh_s = sB[0];  // [BN n][32 g]
     __bf16* bl_s = sB[1];
-    for (int i = tid; i < kBM * 32; i += 512) {
+    for (int i = tid; i < BR * 32; i += T) {
       const int r = i >> 5, g = i & 31;
       const int gm = m0 + r, gn = n0 + r, gg = g0 + g;
-      __bf16 xhv = (__bf16)0.0f, xlv = (__bf16)0.0f, bhv = (__bf16)0.0f, blv = (__bf16)0.0f;
-      if (gg < groups) {
-        if (gm < p.m) {
+      if (r < BM) {
+        __bf16 xhv = (__bf16)0.0f, xlv = (__bf16)0.0f;
+        if (gg < groups && gm < p.m) {
           xhv = p.sh[(size_t)gm * groups + gg];
           xlv = p.sl[(size_t)gm * groups + gg];
         }
-        if (gn < n_rows) {
+        xh_s[r * kPitch + g] = xhv;
+        xl_s[r * kPitch + g] = xlv;
+      }
+      if (r < BN) {
+        __bf16 bhv = (__bf16)0.0f, blv = (__bf16)0.0f;
+        if (gg < groups && gn < n_rows) {
           const float b = group_bias<F>(pt, p.row_bytes, groups, gn, gg);
           bhv = (__bf16)b;
           blv = (__bf16)(b - (float)bhv);
         }
+        bh_s[r * kPitch + g] = bhv;
+        bl_s[r * kPitch + g] = blv;
       }
-      xh_s[r * kPitch + g] = xhv;
-      xl_s[r * kPitch + g] = xlv;
-      bh_s[r * kPitch + g] = bhv;
-      bl_s[r * kPitch + g] = blv;
     }
     __syncthreads();
     if (kh == 0) {

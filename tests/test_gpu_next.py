@@ -221,3 +221,21 @@ def test_qkv_fused_hand(lib):
     assert np.array_equal(host(qo), np.array(fx["q_out"], np.float32))
     assert np.array_equal(host(ko), np.array(fx["k_out"], np.float32))
     assert np.array_equal(host(vo), np.array(fx["v_out"], np.float32))
+
+
+# ------------------------------------------------------------------ matrix-core tile shapes
+def test_mfma_tile_shape_does_not_change_bits(lib, force_mfma):
+    """Four 2048-row parts at M = 256 give the launch 4x the column tiles of one
+    part alone, so the multi-part launch and the single calls take different
+    tile shapes (128x128 vs 64x128 on a 256-CU part); each part must still
+    equal its single call bit for bit."""
+    m, ns, k = 256, (2048, 2048, 2048, 2048), 256
+    ws, x = synth.q4_k_multi_case(6900, m, ns, k)
+    dws, dx = [dev(w) for w in ws], dev(x)
+    y = host(lib.qgemv_q4_k_multi(dws, dx, list(ns), k))
+    col = 0
+    for w, dw, n in zip(ws, dws, ns):
+        single = host(lib.qgemv_q4_k(dw, dx, n, k))
+        assert np.array_equal(bits(y[:, col:col + n]), bits(single)), f"part at column {col}"
+        col += n
+    assert_close(y[:, :2048], oracle.decode_q4_k(ws[0], 2048, k), x, "tile shapes")
