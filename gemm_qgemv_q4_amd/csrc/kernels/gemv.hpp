@@ -333,7 +333,7 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams p) {
   constexpr int NE4 = CH / 4;
   constexpr int P = kWave / L;
   constexpr bool SUMS = FmtTraits<FMT>::SUMS;
-  constexpr int SB = 4;     // float4s of x per thread per staging batch
+  constexpr int SB = 16 / MT > 4 ? 4 : 16 / MT;  // float4s of x per row and thread per staging batch
   constexpr int XPRE = 4;   // float4 registers for x loaded ahead of the first weights
   using Chunk = typename ChunkOf<FMT>::T;
 
@@ -428,18 +428,21 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams p) {
       if (j < n4 && (e4 & 7) == 0) xsum[(m * ct_max + t) * 2 + (e4 >> 3)] = sm;
     }
   };
+  // The loads of a batch cover every x row before any of them is written, so
+  // staging MT rows costs one memory round trip per batch, not one per row.
   auto stage = [&](int k0, int ktile) {
     const int n4 = ktile >> 2;
     const int step = SB * (int)blockDim.x;
+    for (int j0 = 0; j0 < n4; j0 += step) {
+      f32x4 v[MT][SB];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      for (int j0 = 0; j0 < n4; j0 += step) {
-        f32x4 v[SB];
+      for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int u = 0; u < SB; ++u) v[u] = xload(m, j0 + u * (int)blockDim.x + tid, k0, n4);
+        for (int u = 0; u < SB; ++u) v[m][u] = xload(m, j0 + u * (int)blockDim.x + tid, k0, n4);
 #pragma unroll
-        for (int u = 0; u < SB; ++u) xstore(m, j0 + u * (int)blockDim.x + tid, n4, v[u]);
-      }
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int u = 0; u < SB; ++u) xstore(m, j0 + u * (int)blockDim.x + tid, n4, v[m][u]);
     }
     __syncthreads();
   };
