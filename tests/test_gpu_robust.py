@@ -112,3 +112,53 @@ def test_two_streams_do_not_interfere(lib):
     torch.cuda.synchronize()
     for kind, t in outs:
         assert np.array_equal(bits(host(t)), bits(ref_a if kind == "a" else ref_q))
+
+
+# ------------------------------------------------------------------ K-tiled GEMV (x does not fit in LDS)
+@pytest.mark.parametrize("m,n,k", [(8, 70, 8192), (5, 33, 16384), (2, 40, 40960)])
+def test_q4_0_k_tiled(lib, m, n, k):
+    w, x = synth.q4_0_case(7400 + m + k, m, n, k)
+    y = host(lib.qgemv_q4_0(dev(w), dev(x), n, k))
+    assert_close(y, oracle.decode_q4_0(w, n, k), x, f"q4_0 k-tiled {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m,n,k", [(8, 33, 16384), (3, 20, 12288)])
+def test_q4_k_k_tiled(lib, m, n, k):
+    w, x = synth.q4_k_case(7500 + m + k, m, n, k)
+    y = host(lib.qgemv_q4_k(dev(w), dev(x), n, k))
+    assert_close(y, oracle.decode_q4_k(w, n, k), x, f"q4_k k-tiled {m}x{n}x{k}")
+
+
+def test_dual_k_tiled_bitwise(lib):
+    m, n, k = 8, 64, 8192
+    wa, wb, x = synth.dual_q4_0_case(7600, m, n, k)
+    dwa, dwb, dx = dev(wa), dev(wb), dev(x)
+    ya, yb = lib.qgemv_dual_q4_0(dwa, dwb, dx, n, k)
+    sa, sb = lib.qgemv_q4_0(dwa, dx, n, k), lib.qgemv_q4_0(dwb, dx, n, k)
+    assert np.array_equal(bits(host(ya)), bits(host(sa)))
+    assert np.array_equal(bits(host(yb)), bits(host(sb)))
+    assert_close(host(ya), oracle.decode_q4_0(wa, n, k), x, "dual k-tiled")
+
+
+@pytest.mark.parametrize("m,n,k,gs", [(8, 50, 8192, 64), (4, 31, 16384, 128)])
+def test_affine_and_packed_k_tiled(lib, m, n, k, gs):
+    import torch
+    x, q, s, b = synth.affine_case(7700 + m + k, m, n, k, gs)
+    dx, ds, db = dev(x), dev(s), dev(b)
+    y8 = host(lib.qmm_affine_t(dx, dev(q), ds, db, gs))
+    wp = synth.pack_b4_u32(q)
+    y4 = host(lib.qmm_affine_t_packed(dx, torch.from_numpy(wp.view(np.int32)).cuda(), ds, db, gs))
+    assert np.array_equal(bits(y8), bits(y4))
+    assert_close(y8, oracle.decode_affine(q, s, b, n, k, gs), x, f"affine k-tiled {m}x{n}x{k}")
+
+
+def test_multi_k_tiled(lib):
+    m, ns, k = 8, (40, 7), 16384
+    ws, x = synth.q4_k_multi_case(7800, m, ns, k)
+    dws, dx = [dev(w) for w in ws], dev(x)
+    y = host(lib.qgemv_q4_k_multi(dws, dx, list(ns), k))
+    col = 0
+    for w, dw, n in zip(ws, dws, ns):
+        assert np.array_equal(bits(y[:, col:col + n]), bits(host(lib.qgemv_q4_k(dw, dx, n, k))))
+        assert_close(y[:, col:col + n], oracle.decode_q4_k(w, n, k), x, f"multi k-tiled col {col}")
+        col += n
