@@ -44,16 +44,17 @@ __device__ __forceinline__ float dpp_mov(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 
-// Sum over aligned groups of `width` lanes (width = 8, 16, 32 or 64); every
-// lane of a group gets the group's sum.  Within a row of 16 lanes the partial
-// sums move by DPP (no LDS traffic): xor 1, xor 2, then the half-row and row
-// mirrors, which pair each quad (then each half-row) with its partner.  The
-// last one or two steps cross rows with a lane shuffle.  The order of the
-// additions is fixed, so results are reproducible bit for bit.
+// Sum over aligned groups of `width` lanes (width = 4, 8, 16, 32 or 64);
+// every lane of a group gets the group's sum.  Within a row of 16 lanes the
+// partial sums move by DPP (no LDS traffic): xor 1, xor 2, then the half-row
+// and row mirrors, which pair each quad (then each half-row) with its partner.
+// The last one or two steps cross rows with a lane shuffle.  The order of the
+// additions is fixed (the same as an xor butterfly), so results are
+// reproducible bit for bit.
 __device__ __forceinline__ float group_sum(float v, int width) {
   v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
   v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
-  v += dpp_mov<0x141>(v);  // row_half_mirror
+  if (width >= 8) v += dpp_mov<0x141>(v);   // row_half_mirror
   if (width >= 16) v += dpp_mov<0x140>(v);  // row_mirror
   if (width >= 32) v += __shfl_xor(v, 16, kWave);
   if (width >= 64) v += __shfl_xor(v, 32, kWave);

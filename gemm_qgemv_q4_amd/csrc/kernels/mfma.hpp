@@ -37,7 +37,7 @@ namespace qg {
 // x -> (x_hi, x_lo) bf16 and per-group sums X_g, the sums also split into
 // bf16 hi/lo (they feed the bias product on the matrix cores).  Each thread
 // converts 8 consecutive elements; the gs/8 threads of a group (gs <= 512)
-// combine their partial sums with a fixed xor butterfly.
+// combine their partial sums with a fixed-order DPP reduction.
 __global__ void __launch_bounds__(256) affine_prep_kernel(const float* __restrict__ x,
                                                           __bf16* __restrict__ xh,
                                                           __bf16* __restrict__ xl,
@@ -76,7 +76,7 @@ __global__ void __launch_bounds__(256) affine_prep_kernel(const float* __restric
     *reinterpret_cast<bf16x8*>(xl + base) = lv;
   }
   const int lanes = gs / 8;  // threads per group (4..64)
-  for (int off = 1; off < lanes; off <<= 1) s += __shfl_xor(s, off, kWave);
+  s = group_sum(s, lanes);
   if (ok && (c8 % lanes) == 0) {
     const int groups = k / gs;
     const size_t gi = (size_t)m * groups + c8 / lanes;
