@@ -322,12 +322,23 @@ def _time_oracle(budget_s, threads):
 def cpu_baseline(budget_s=10.0):
     """The oracle as it stands on the host: one BLAS thread (the reported
     value) and all the host's cores (reported beside it)."""
+    import oracle
+    import synth
     host_cores = len(os.sched_getaffinity(0))
     nb, calls, el = _time_oracle(budget_s, 1)
     per = el / calls
+    # one more call split into its two steps: f64 decode, then the f64 product
+    c = synth.CONFIGS[HEADLINE]
+    w, x = synth.q4_k_case(c["seed"], c["m"], c["n"], c["k"])
+    t0 = time.perf_counter()
+    w64 = oracle.decode_q4_k(w, c["n"], c["k"])
+    t1 = time.perf_counter()
+    oracle.gemv_f64(w64, x)
+    t2 = time.perf_counter()
     out = {"value": round(nb / per / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
            "sample": f"{calls} full Q4_K GEMV calls (M=1, N=K=4096) in {el:.1f}s, numpy f64 decode + matvec, "
-                     f"1 BLAS thread; {per * 1e6:.0f} us/call; host has {host_cores} cores"}
+                     f"1 BLAS thread; {per * 1e6:.0f} us/call (decode {(t1 - t0) * 1e6:.0f} us, "
+                     f"product {(t2 - t1) * 1e6:.0f} us); host has {host_cores} cores"}
     nb, calls, el = _time_oracle(budget_s, host_cores)
     per = el / calls
     out["all_cores"] = {"value": round(nb / per / 1e9, 4), "unit": "GB/s", "cores": host_cores,
