@@ -391,22 +391,23 @@ qg_status run_mfma(const char* op, const HostPart* parts, int nparts, const floa
   const int64_t items = m * (k / 8);
   hipLaunchKernelGGL(affine_prep_kernel, dim3((unsigned)cdiv(items, 256)), dim3(256), 0, s, x, xh, xl, sh, sl,
                      (int)m, (int)k, gs);
-  // Tile shape: 128x128 (two waves per SIMD) unless that leaves more than half
-  // of the CUs without a workgroup; then 64x128, then 64x64.  Measured on
-  // MI355X: Q4_0 512x4096x4096 runs 121 us on 128 tiles of 128x128 and 131 us
-  // on 256 tiles of 64x128 (one wave per SIMD), so smaller tiles only pay off
-  // below half occupancy.  The arithmetic of an output does not depend on the
-  // shape.
+  // Tile shape: 128x128 (16 waves) while that gives every other CU a tile,
+  // else 64x128 (8 waves, two workgroups per CU); both run four waves per
+  // SIMD.  Measured on MI355X: Q4_0 512x4096x4096 takes 107 us on 128 tiles
+  // of 128x128 and 100 us on 256 tiles of 64x128; the affine 512x8192x2048
+  // product 64 us on 256 tiles of 128x128 and 72 us on 512 of 64x128.  The
+  // arithmetic of an output does not depend on the shape.
   const int64_t cus = device_cus();
-  auto tiles_for = [&](int sm, int sn) {
+  auto tiles_for = [&](int sm) {
     int64_t tn = 0;
-    for (int pi = 0; pi < nparts; ++pi) tn += cdiv(parts[pi].n, 64 * sn);
+    for (int pi = 0; pi < nparts; ++pi) tn += cdiv(parts[pi].n, 128);
     return cdiv(m, 64 * sm) * tn;
   };
-  int sm = 2, sn = 2;
-  if (2 * tiles_for(2, 2) < cus) {
-    sm = 1;
-    sn = 2 * tiles_for(1, 2) >= cus ? 2 : 1;
+  int sm = 2 * tiles_for(2) > cus ? 2 : 1;
+  // tuning override (same results either way): QG_MFMA_TILE=0 (128x128) or 1 (64x128)
+  if (const char* env = getenv("QG_MFMA_TILE")) {
+    const int t = atoi(env);
+    if (t == 0 || t == 1) sm = 2 - t;
   }
   MfmaParams mp{};
   mp.xh = xh;
@@ -423,7 +424,7 @@ qg_status run_mfma(const char* op, const HostPart* parts, int nparts, const floa
     q.ldy = parts[pi].ldy;
     q.n = (int)parts[pi].n;
     q.tile0 = (int)tiles_n;
-    tiles_n += cdiv(parts[pi].n, 64 * sn);
+    tiles_n += cdiv(parts[pi].n, 128);
   }
   mp.parts = nparts;
   mp.row_bytes = row_bytes_of<FMT>(k);
@@ -433,17 +434,15 @@ qg_status run_mfma(const char* op, const HostPart* parts, int nparts, const floa
   mp.tiles_m = (int)cdiv(m, 64 * sm);
   mp.tiles_n = (int)tiles_n;
   const dim3 grid((unsigned)(mp.tiles_m * mp.tiles_n));
-  const dim3 block((unsigned)(128 * sm * sn));
+  // 128x128 runs as 4 x 2 wave pairs of 32x64 sub-tiles, 64x128 as 2 x 2
+  const dim3 block((unsigned)(512 * sm));
   const bool multi = nparts > 1;
   if (sm == 2) {
-    if (multi) hipLaunchKernelGGL((qmm_mfma_kernel<FMT, true, 2, 2>), grid, block, 0, s, mp);
-    else hipLaunchKernelGGL((qmm_mfma_kernel<FMT, false, 2, 2>), grid, block, 0, s, mp);
-  } else if (sn == 2) {
-    if (multi) hipLaunchKernelGGL((qmm_mfma_kernel<FMT, true, 1, 2>), grid, block, 0, s, mp);
-    else hipLaunchKernelGGL((qmm_mfma_kernel<FMT, false, 1, 2>), grid, block, 0, s, mp);
+    if (multi) hipLaunchKernelGGL((qmm_mfma_kernel<FMT, true, 4, 2, 2>), grid, block, 0, s, mp);
+    else hipLaunchKernelGGL((qmm_mfma_kernel<FMT, false, 4, 2, 2>), grid, block, 0, s, mp);
   } else {
-    if (multi) hipLaunchKernelGGL((qmm_mfma_kernel<FMT, true, 1, 1>), grid, block, 0, s, mp);
-    else hipLaunchKernelGGL((qmm_mfma_kernel<FMT, false, 1, 1>), grid, block, 0, s, mp);
+    if (multi) hipLaunchKernelGGL((qmm_mfma_kernel<FMT, true, 2, 2, 2>), grid, block, 0, s, mp);
+    else hipLaunchKernelGGL((qmm_mfma_kernel<FMT, false, 2, 2, 2>), grid, block, 0, s, mp);
   }
   const qg_status ls = launch_status(op);
   e = hipFreeAsync(scratch, s);

@@ -22,12 +22,12 @@
 // Kernels:
 //   affine_prep_kernel : x [M,K] f32 -> x_hi, x_lo [M,K] bf16 and X [M, K/gs]
 //                        as bf16 hi, lo.
-//   qmm_mfma_kernel<F, MULTI, SM, SN> : a (64 SM) x (64 SN) output tile per
-//                        workgroup of 2*SM*SN waves: SM x SN sub-tiles of
-//                        64x64, each shared by two waves that split every
-//                        64-wide K stage.  Column tiles are numbered part after
-//                        part (up to kMaxParts weight tensors sharing x), so a
-//                        tile's part is uniform.
+//   qmm_mfma_kernel<F, MULTI, SM, SN, TI> : a (16 TI SM) x (64 SN) output
+//                        tile per workgroup of 2*SM*SN waves: SM x SN
+//                        sub-tiles of (16 TI) x 64, each shared by two waves
+//                        that split every 64-wide K stage.  Column tiles are
+//                        numbered part after part (up to kMaxParts weight
+//                        tensors sharing x), so a tile's part is uniform.
 #pragma once
 #include "common.hpp"
 
@@ -145,12 +145,12 @@ __device__ __forceinline__ float group_bias(const MfmaPart& pt, long long row_by
   }
 }
 
-// One 32-wide K step of the wave's 64x64 sub-tile: P += (A_hi + A_lo) * B.
+// One 32-wide K step of the wave's (16 TI) x 64 sub-tile: P += (A_hi + A_lo) * B.
 // All 16 hi products are issued before the 16 lo products, so consecutive
 // MFMAs never wait on each other's accumulator.
-template <bool FIRST>
+template <bool FIRST, int TI>
 __device__ __forceinline__ void mfma_substep(const __bf16* sAh, const __bf16* sAl, const __bf16* sB,
-                                             int kq, int wm, int wn, int lane, f32x4 (&P)[4][4]) {
+                                             int kq, int wm, int wn, int lane, f32x4 (&P)[TI][4]) {
   const int r16 = lane & 15;
   const int kk = (lane >> 4) * 8 + kq;
   bf16x8 bfrag[4];
@@ -158,8 +158,8 @@ __device__ __forceinline__ void mfma_substep(const __bf16* sAh, const __bf16* sA
   for (int j = 0; j < 4; ++j)
     bfrag[j] = *(const bf16x8*)(sB + (wn * 64 + j * 16 + r16) * kPitch + kk);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const bf16x8 ah = *(const bf16x8*)(sAh + (wm * 64 + i * 16 + r16) * kPitch + kk);
+  for (int i = 0; i < TI; ++i) {
+    const bf16x8 ah = *(const bf16x8*)(sAh + (wm * 16 * TI + i * 16 + r16) * kPitch + kk);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if constexpr (FIRST) {
@@ -171,34 +171,40 @@ __device__ __forceinline__ void mfma_substep(const __bf16* sAh, const __bf16* sA
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const bf16x8 al = *(const bf16x8*)(sAl + (wm * 64 + i * 16 + r16) * kPitch + kk);
+  for (int i = 0; i < TI; ++i) {
+    const bf16x8 al = *(const bf16x8*)(sAl + (wm * 16 * TI + i * 16 + r16) * kPitch + kk);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       P[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bfrag[j], P[i][j], 0, 0, 0);
   }
 }
 
-// One workgroup computes a (64*SM) x (64*SN) output tile: SM x SN sub-tiles
-// of 64 x 64, each owned by a pair of waves (4 x 4 MFMA tiles each), so the
-// workgroup has 2*SM*SN waves and the CU runs two waves per SIMD.  The two
-// waves of a pair split every 64-wide K stage: wave half 0 takes columns
-// 0..31, half 1 columns 32..63; their partial sums meet in LDS at the end.  K
-// runs through two LDS buffers; each stage's global loads are issued one stage
-// ahead into registers (one barrier per stage).  When a group of gs columns is
-// complete, a wave scales its partial product: acc += s[n, g] * P.  The bias
-// term sum_g b[n,g] * X_g[m] is one more small matrix product at the end,
-// with both factors split into bf16 hi + lo (three MFMAs per 32 groups).
-// The arithmetic of one output element is the same for every (SM, SN), so
+// One workgroup computes a (16*TI*SM) x (64*SN) output tile: SM x SN
+// sub-tiles of (16*TI) x 64, each owned by a pair of waves (TI x 4 MFMA tiles
+// each), so the workgroup has 2*SM*SN waves.  With TI = 2 a wave holds 32
+// accumulator tiles' worth of registers (acc and P), which leaves room for
+// four waves per SIMD; the measured alternative, TI = 4 at two waves per
+// SIMD, is 10-20% slower on every workload.  The two waves of a pair split
+// every 64-wide K stage: wave half 0 takes columns 0..31, half 1 columns
+// 32..63; their partial sums meet in LDS at the end.  K runs through two LDS
+// buffers; each stage's global loads are issued one stage ahead into
+// registers (one barrier per stage).  When a group of gs columns is complete,
+// a wave scales its partial product: acc += s[n, g] * P.  The bias term
+// sum_g b[n,g] * X_g[m] is one more small matrix product at the end, with
+// both factors split into bf16 hi + lo (three MFMAs per 32 groups).  The
+// arithmetic of one output element is the same for every (SM, SN, TI), so
 // the host picks the tile shape from the tile count alone.
-template <int F, bool MULTI, int SM, int SN>
-__global__ void __launch_bounds__(128 * SM * SN, 4 / (SM * SN)) qmm_mfma_kernel(MfmaParams p) {
+template <int F, bool MULTI, int SM, int SN, int TI>
+__global__ void __launch_bounds__(128 * SM * SN, 8 / TI) qmm_mfma_kernel(MfmaParams p) {
   constexpr int T = 128 * SM * SN;  // threads
   constexpr int NSUB = SM * SN;
-  constexpr int BM = 64 * SM, BN = 64 * SN;
+  constexpr int SUBM = 16 * TI;     // rows of a wave pair's sub-tile
+  constexpr int BM = SUBM * SM, BN = 64 * SN;
   constexpr int A_ELEMS = BM * kPitch, B_ELEMS = BN * kPitch;
-  constexpr int RA = 4 / SN;  // x rows each thread moves per stage (8 elements each, hi and lo)
-  constexpr int IB = 2 / SM;  // 16-code pieces of weights each thread moves per stage
+  constexpr int RA = BM * 8 / T;    // x rows each thread moves per stage (8 elements each, hi and lo)
+  constexpr int NB = BN * 4;        // 16-code pieces of weights per stage
+  constexpr int IB = NB >= T ? NB / T : 1;  // pieces per thread (threads past NB move none)
+  static_assert(RA >= 1 && BM * 8 == RA * T, "x pieces must divide evenly over the threads");
   __shared__ __attribute__((aligned(16))) __bf16 sA[2][2 * A_ELEMS];  // [buf][hi | lo]
   __shared__ __attribute__((aligned(16))) __bf16 sB[2][B_ELEMS];
   __shared__ float sS[2][2][BN];  // [buf][group in stage][n]
@@ -233,9 +239,9 @@ __global__ void __launch_bounds__(128 * SM * SN, 4 / (SM * SN)) qmm_mfma_kernel(
   const int stages = p.k / kBK;
   const int ng = p.gs < kBK ? kBK / p.gs : 1;  // groups per stage: 2 when gs == 32
 
-  f32x4 acc[4][4], P[4][4];
+  f32x4 acc[TI][4], P[TI][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -260,12 +266,13 @@ __global__ void __launch_bounds__(128 * SM * SN, 4 / (SM * SN)) qmm_mfma_kernel(
   int b_n[IB], b_kc[IB];
   bool b_ok[IB];
   uint32_t b_row[IB];
+  const bool b_mine = NB >= T || tid < NB;  // threads past NB move no weight piece
 #pragma unroll
   for (int i = 0; i < IB; ++i) {
-    const int it = tid + i * T;
+    const int it = b_mine ? tid + i * T : 0;
     b_n[i] = it >> 2;
     b_kc[i] = it & 3;
-    b_ok[i] = n0 + b_n[i] < n_rows;
+    b_ok[i] = b_mine && n0 + b_n[i] < n_rows;
     b_row[i] = (uint32_t)(b_ok[i] ? n0 + b_n[i] : 0) * (uint32_t)p.row_bytes;
   }
   const int s_row = n0 + (tid % BN) < n_rows ? n0 + (tid % BN) : n_rows - 1;
@@ -344,6 +351,7 @@ __global__ void __launch_bounds__(128 * SM * SN, 4 / (SM * SN)) qmm_mfma_kernel(
     }
 #pragma unroll
     for (int i = 0; i < IB; ++i) {
+      if (!b_mine) break;
       // 16 codes -> 16 bf16 (exact: integers below 256)
       uint32_t cw[4];
       code_words(r.b[i], r.b4[i], b_kc[i], cw);
@@ -365,7 +373,7 @@ __global__ void __launch_bounds__(128 * SM * SN, 4 / (SM * SN)) qmm_mfma_kernel(
     for (int j = 0; j < 4; ++j) {
       const float sv = sS[buf][gi][wn * 64 + j * 16 + (lane & 15)];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < TI; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(sv, P[i][j][e], acc[i][j][e]);
     }
@@ -375,13 +383,13 @@ __global__ void __launch_bounds__(128 * SM * SN, 4 / (SM * SN)) qmm_mfma_kernel(
     const __bf16* ah = sA[buf];
     const __bf16* al = sA[buf] + A_ELEMS;
     if (p.gs == 32) {  // the half is a whole group
-      mfma_substep<true>(ah, al, sB[buf], kh * 32, wm, wn, lane, P);
+      mfma_substep<true, TI>(ah, al, sB[buf], kh * 32, wm, wn, lane, P);
       scale_into_acc(buf, kh);
       return;
     }
     const int c0 = st * kBK;
-    if (c0 % p.gs == 0) mfma_substep<true>(ah, al, sB[buf], kh * 32, wm, wn, lane, P);
-    else mfma_substep<false>(ah, al, sB[buf], kh * 32, wm, wn, lane, P);
+    if (c0 % p.gs == 0) mfma_substep<true, TI>(ah, al, sB[buf], kh * 32, wm, wn, lane, P);
+    else mfma_substep<false, TI>(ah, al, sB[buf], kh * 32, wm, wn, lane, P);
     if ((c0 + kBK) % p.gs == 0) scale_into_acc(buf, 0);
   };
 
@@ -399,17 +407,17 @@ __global__ void __launch_bounds__(128 * SM * SN, 4 / (SM * SN)) qmm_mfma_kernel(
 
   // ---- combine the two K halves: half 1 hands its partial sums to half 0
   float* red = reinterpret_cast<float*>(&sA[0][0]);  // NSUB sub-tiles x 64 x 64 floats
-  float* mine = red + (size_t)sub * 4096;
+  float* mine = red + (size_t)sub * (SUBM * 64);
   if (kh == 1) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) *(f32x4*)(mine + ((i * 4 + j) * 64 + lane) * 4) = acc[i][j];
   }
   __syncthreads();
   if (kh == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const f32x4 o = *(const f32x4*)(mine + ((i * 4 + j) * 64 + lane) * 4);
@@ -460,9 +468,9 @@ __global__ void __launch_bounds__(128 * SM * SN, 4 / (SM * SN)) qmm_mfma_kernel(
         bl[j] = *(const bf16x8*)(bl_s + (wn * 64 + j * 16 + r16) * kPitch + kk);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bf16x8 ah = *(const bf16x8*)(xh_s + (wm * 64 + i * 16 + r16) * kPitch + kk);
-        const bf16x8 al = *(const bf16x8*)(xl_s + (wm * 64 + i * 16 + r16) * kPitch + kk);
+      for (int i = 0; i < TI; ++i) {
+        const bf16x8 ah = *(const bf16x8*)(xh_s + (wm * SUBM + i * 16 + r16) * kPitch + kk);
+        const bf16x8 al = *(const bf16x8*)(xl_s + (wm * SUBM + i * 16 + r16) * kPitch + kk);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh[j], acc[i][j], 0, 0, 0);
@@ -477,12 +485,12 @@ __global__ void __launch_bounds__(128 * SM * SN, 4 / (SM * SN)) qmm_mfma_kernel(
   // store: lane holds rows 4*(lane/16)+e, column lane%16 of each 16x16 tile
   if (kh == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int gm = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + e;
+          const int gm = m0 + wm * SUBM + i * 16 + (lane >> 4) * 4 + e;
           const int gn = n0 + wn * 64 + j * 16 + (lane & 15);
           if (gm < p.m && gn < n_rows) pt.y[(size_t)gm * pt.ldy + gn] = acc[i][j][e];
         }
