@@ -156,3 +156,33 @@ def test_qkv_fused_rejects_bad_spans_and_aliasing():
     assert "alias" in _err(qg.raw.qmm_affine_t_qkv(A, B, C, D, E, E, G, 1, 64, 32, 4, 4, 4, None))
     assert "group_size" in _err(qg.raw.qmm_affine_t_qkv(A, B, C, D, E, F, G, 1, 64, 3, 4, 4, 4, None))
     assert "null" in _err(qg.raw.qmm_affine_t_qkv(A, None, C, D, E, F, G, 1, 64, 32, 4, 4, 4, None))
+
+
+def test_c_program_builds_and_runs_against_the_header(tmp_path):
+    """The header compiles as C99 with -Wall -Wextra -Werror, a plain C program
+    links against the library, and without a GPU its argument checks pass
+    (with a GPU the same program also checks the bitwise equalities; the gpu
+    test runs the copy built by the build step)."""
+    import importlib.util
+    import subprocess
+    spec = importlib.util.spec_from_file_location("_qg_build_c", os.path.join(ROOT, "tests", "c", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    out = mod.build(str(tmp_path / "abi_check"))
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1")  # argument checks only, even on a GPU host
+    res = subprocess.run([out], capture_output=True, text=True, timeout=120, env=env)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert "abi_check: ok" in res.stdout, res.stdout
+
+
+def test_header_compiles_as_cpp(tmp_path):
+    import shutil
+    import subprocess
+    cxx = shutil.which("g++")
+    if cxx is None:
+        pytest.skip("no g++")
+    src = tmp_path / "h.cpp"
+    src.write_text('#include "qgemv_q4.h"\nint main() { return qg_get_mfma_min_m() < 0; }\n')
+    res = subprocess.run([cxx, "-std=c++11", "-Wall", "-Werror", "-fsyntax-only", "-I", os.path.join(ROOT, "include"), str(src)],
+                         capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
