@@ -214,3 +214,33 @@ NEXT_CONFIGS = {
     "affine_b4_12288x4096_gs64": dict(kind="affine_b4", seed=107, m=8, n=12288, k=4096, gs=64),
     "q4_0_prefill_512x4096": dict(kind="q4_0", seed=108, m=512, n=4096, k=4096),
 }
+
+
+# ---------------------------------------------------------------- device-side
+# Inputs too large to build on the host (weights beyond 2 GiB): random bytes
+# drawn on the GPU with a seeded torch generator.  Only the byte patterns are
+# chosen here; no value is decoded.
+
+def q4_0_random_device(seed: int, n: int, k: int, device: str = "cuda"):
+    """block_q4_0 rows [n][k/32] with random nibbles and fp16 d in [2^-6, 2^-5)
+    (exponent field 9, random mantissa), as a flat uint8 tensor on `device`."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    blocks = n * (k // QK4_0)
+    w = torch.randint(0, 256, (blocks, BLOCK_Q4_0_BYTES), dtype=torch.uint8, device=device, generator=gen)
+    w[:, 1] = (w[:, 1] & 0x03) | 0x24  # fp16 high byte: sign 0, exponent 01001
+    return w.view(-1)
+
+
+def affine_random_device(seed: int, n: int, k: int, group_size: int, device: str = "cuda"):
+    """u8 codes [n, k] in 0..15 and f32 scales, biases [n, k/group_size] with
+    scale ~ U(0.001, 0.01) and bias ~ N(0, 0.02), on `device`."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    q = torch.randint(0, 16, (n, k), dtype=torch.uint8, device=device, generator=gen)
+    g = k // group_size
+    s = torch.rand((n, g), dtype=torch.float32, device=device, generator=gen) * 0.009 + 0.001
+    b = torch.randn((n, g), dtype=torch.float32, device=device, generator=gen) * 0.02
+    return q, s, b
