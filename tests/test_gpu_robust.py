@@ -162,3 +162,30 @@ def test_multi_k_tiled(lib):
         assert np.array_equal(bits(y[:, col:col + n]), bits(host(lib.qgemv_q4_k(dw, dx, n, k))))
         assert_close(y[:, col:col + n], oracle.decode_q4_k(w, n, k), x, f"multi k-tiled col {col}")
         col += n
+
+
+
+@pytest.mark.parametrize("fmt", ["q4_k", "affine"])
+@pytest.mark.parametrize("m", [3, 70])
+def test_non_finite_x_stays_in_its_row(lib, fmt, m):
+    """A NaN in row 0 of x and an infinity in row 1 make every output of
+    those rows non-finite (row 0 all NaN) and leave every other row bitwise
+    as it was, on the GEMV rows (M = 3) and on the matrix-core rows (M = 70).
+    The kernels fold the group minimum or bias into a separate sum of x, so an
+    infinity may come out as NaN where an exact product would give an
+    infinity; only confinement to the row is a stated property."""
+    n, k, gs = 96, 512, 64
+    if fmt == "q4_k":
+        w, x = synth.q4_k_case(7400 + m, m, n, k)
+        call = lambda xx: host(lib.qgemv_q4_k(dev(w), dev(xx), n, k))
+    else:
+        x, q, s, b = synth.affine_case(7400 + m, m, n, k, gs)
+        call = lambda xx: host(lib.qmm_affine_t(dev(xx), dev(q), dev(s), dev(b), gs))
+    y0 = call(x)
+    xb = x.copy()
+    xb[0, 5] = np.nan
+    xb[1, 300] = np.inf
+    y = call(xb)
+    assert np.all(np.isnan(y[0]))
+    assert not np.any(np.isfinite(y[1]))
+    assert np.array_equal(bits(y[2:]), bits(y0[2:]))
