@@ -423,7 +423,7 @@ def main():
         "config": {"workload": "Q4_K GEMV M=1 N=4096 K=4096 (o_proj-sized decode)", "M": 1, "N": 4096,
                    "K": 4096, "weight_format": "Q4_K", "bytes_per_call": h["bytes"],
                    "rotation_copies": h["rotation_copies"], "timing": "hip graph of K calls, hip events"},
-        "roofline": {"bound": "hbm", "kernel": "gemv_kernel<Q4_K>", "achieved": round(value, 1),
+        "roofline": {"bound": "hbm", "kernel": "gemv_ks_kernel<Q4_K>", "achieved": round(value, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(value / HBM_PEAK_GBS, 4),
                      "traffic": read_traffic()},
         "per_config": per,

@@ -277,6 +277,58 @@ hipError_t launch_gemv_mt(const GemvPlan& pl, const GemvParams& p, dim3 g, dim3 
   return hipErrorInvalidValue;
 }
 
+// K-sliced kernel for M = 1 and the 64-weight chunk formats (same bits as
+// the chunked kernel with 32 lanes per row); J = chunks per lane.
+constexpr int kKsRows = 16;
+
+template <int FMT, int NW, int J>
+hipError_t launch_gemv_ks_j(const GemvParams& p, dim3 grid, size_t lds, hipStream_t s) {
+  if (p.parts > 1) {
+    if constexpr (NW == 1 && FMT == FMT_Q4K) {
+      hipLaunchKernelGGL((gemv_ks_kernel<FMT, NW, J, true>), grid, dim3(512), lds, s, p);
+      return hipSuccess;
+    }
+    return hipErrorInvalidValue;
+  }
+  hipLaunchKernelGGL((gemv_ks_kernel<FMT, NW, J, false>), grid, dim3(512), lds, s, p);
+  return hipSuccess;
+}
+
+size_t ks_lds(int j, int nw) {
+  const size_t u = 4 * (size_t)j;
+  return 8 * 16 * (u + 1) * 16 + 8 * 2 * u * 4 + 2 * (size_t)nw * 8 * kKsRows * 4;
+}
+
+// Chunks per lane the K-sliced kernel is built for (0: not eligible).
+template <int FMT, int NW>
+int ks_chunks(const GemvPlan& pl, int64_t m, int64_t k) {
+  if constexpr (FMT != FMT_Q40 && FMT != FMT_Q4K) {
+    return 0;
+  } else {
+    // tuning override (same results either way): QG_GEMV_KS=0 keeps the chunked kernel
+    if (const char* env = getenv("QG_GEMV_KS"))
+      if (env[0] == '0') return 0;
+    if (NW != 1) return 0;
+    if (m != 1 || pl.mt != 1 || pl.l != 32 || pl.r != 1 || !pl.persistent) return 0;
+    const int64_t j = cdiv(k / 64, 32);
+    return j >= 1 && j <= 4 ? (int)j : 0;
+  }
+}
+
+template <int FMT, int NW>
+hipError_t launch_gemv_ks(int j, const GemvParams& p, dim3 grid, hipStream_t s) {
+  // one stream only: for the dual product the chunked kernel measured faster
+  if constexpr (NW != 1 || (FMT != FMT_Q40 && FMT != FMT_Q4K)) return hipErrorInvalidValue;
+  const size_t lds = ks_lds(j, NW);
+  if constexpr (NW == 1 && (FMT == FMT_Q40 || FMT == FMT_Q4K)) switch (j) {
+    case 1: return launch_gemv_ks_j<FMT, NW, 1>(p, grid, lds, s);
+    case 2: return launch_gemv_ks_j<FMT, NW, 2>(p, grid, lds, s);
+    case 3: return launch_gemv_ks_j<FMT, NW, 3>(p, grid, lds, s);
+    case 4: return launch_gemv_ks_j<FMT, NW, 4>(p, grid, lds, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 // Runs a part list on the chunked GEMV kernel (or on the plain one when
 // `plain`), over all m-tiles of x.
 template <int FMT, int NW>
@@ -310,8 +362,9 @@ qg_status run_gemv(const char* op, const HostPart* parts, int nparts, const floa
     return launch_status(op);
   }
   const GemvPlan pl = plan_gemv<FMT>(m, k, NW);
+  const int ks = ks_chunks<FMT, NW>(pl, m, k);
   const GemvGrid gg = grid_gemv<FMT>(pl, parts, nparts);
-  const int rows_per_group = (int)gg.groups_rows;
+  const int rows_per_group = ks ? kKsRows : (int)gg.groups_rows;
   GemvParams p{};
   int64_t groups = 0;
   for (int pi = 0; pi < nparts; ++pi) {
@@ -333,7 +386,21 @@ qg_status run_gemv(const char* op, const HostPart* parts, int nparts, const floa
   p.k = (int)k;
   p.gs = gs;
   p.kt = pl.kt;
-  p.rows_per_block = rows_per_group;
+  if (ks) {
+    p.x = x;
+    p.m_rows = 1;
+    // Up to two workgroups per CU (16 waves; the kernel takes at most 101
+    // VGPRs and 38 KB of LDS), walking row groups beyond that.  Measured on
+    // Q4_K K = 4096 at N = 6144 ... 28672 rows: 3-12% faster than one per CU.
+    // Tuning override QG_GEMV_KS=B (B workgroups per CU; 0 keeps the chunked kernel).
+    int64_t bpc = 2;
+    if (const char* env = getenv("QG_GEMV_KS")) bpc = atoi(env) > 0 ? atoi(env) : 2;
+    const int64_t cap = bpc * device_cus();
+    const int64_t grid = groups < cap ? groups : cap;
+    const hipError_t e = launch_gemv_ks<FMT, NW>(ks, p, dim3((unsigned)grid), s);
+    if (e != hipSuccess) return launch_error(op, "launch setup failed", e);
+    return launch_status(op);
+  }
   const int64_t grid = gg.grid;
   const dim3 block(64 * gg.waves);
   for (int64_t m0 = 0; m0 < m; m0 += pl.mt) {

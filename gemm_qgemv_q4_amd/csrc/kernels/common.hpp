@@ -1,6 +1,7 @@
 // Shared device helpers for the gfx950 kernels of libqgemv_q4.
 #pragma once
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace qg {

@@ -47,26 +47,32 @@ namespace qg {
 // One weight tensor of a product and where its outputs go.
 struct GemvPart {
   const uint8_t* w[2];    // weights of stream 0 and (dual only) stream 1
-  const float* scales;    // affine: [n, K/gs]
-  const float* biases;    // affine: [n, K/gs]
   float* y[2];            // output (m, r) of stream s at y[s][m * ldy + r]
-  long long ldy;
   int n;                  // rows
   int group0;             // first row group of this part
+  const float* scales;    // affine: [n, K/gs]
+  const float* biases;    // affine: [n, K/gs]
+  long long ldy;
 };
 
+// Kernel arguments.  The wavefront reads them through the scalar cache in
+// 64-byte lines, and every line beyond the first costs about 0.2 us before the
+// first weight load can leave (measured on a 4096 x 4096 Q4_K product): the
+// fields that a one-part block-format GEMV needs at M = 1 (x, row_bytes, k,
+// n_groups and part 0's w, y, n, group0) fill exactly the first 64 bytes.
 struct GemvParams {
-  GemvPart part[kMaxParts];
-  int parts;
-  int n_groups;           // row groups over all parts
   const float* x;         // [m_rows, K] of this m-tile
   long long row_bytes;    // bytes per weight row
-  int m_rows;             // valid x rows in this tile (<= MT)
   int k;
-  int gs;                 // affine group size
+  int n_groups;           // row groups over all parts
+  GemvPart part[kMaxParts];
   int kt;                 // K elements staged per LDS tile (multiple of L*CH, or == k)
-  int rows_per_block;     // waves_per_block * P * R
+  int m_rows;             // valid x rows in this tile (<= MT)
+  int gs;                 // affine group size
+  int parts;
 };
+static_assert(offsetof(GemvParams, part) + offsetof(GemvPart, scales) == 64,
+              "x, row_bytes, k, n_groups and part 0's w, y, n, group0 share the first 64 bytes");
 
 template <int FMT> struct FmtTraits;
 template <> struct FmtTraits<FMT_Q40> { static constexpr int CH = 64; static constexpr bool SUMS = true; };
@@ -140,6 +146,19 @@ __device__ __forceinline__ void aff_words(const ChunkAff4& c, uint32_t (&qd)[8])
     qd[2 * i] = __builtin_amdgcn_perm(od, ev, 0x05010400u);
     qd[2 * i + 1] = __builtin_amdgcn_perm(od, ev, 0x07030602u);
   }
+}
+
+// Four codes 0..15, one per byte, as floats.  Read as OCP fp8 (e4m3), the
+// bytes 0..15 are q / 512 exactly (the subnormals and the first binade share
+// one spacing), and the scaled pair conversion multiplies by 2^9: two
+// conversions give four exact codes.
+__device__ __forceinline__ void small_codes_f32(uint32_t v, float& q0, float& q1, float& q2, float& q3) {
+  const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v, 512.0f, false);
+  const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v, 512.0f, true);
+  q0 = lo[0];
+  q1 = lo[1];
+  q2 = hi[0];
+  q3 = hi[1];
 }
 
 // Per-half (32-weight) scale factors of a chunk: y += A0*dot0 + B0*sumx0 + A1*dot1 + B1*sumx1
@@ -225,8 +244,13 @@ __device__ __forceinline__ void compute_chunk(const typename ChunkOf<FMT>::T (&c
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           const uint32_t qd = opaque(words[s][r][e4]);
-          const float q0 = ubyte_f32<0>(qd), q1 = ubyte_f32<1>(qd);
-          const float q2 = ubyte_f32<2>(qd), q3 = ubyte_f32<3>(qd);
+          float q0, q1, q2, q3;
+          if constexpr (FMT == FMT_AFF4) {
+            small_codes_f32(qd, q0, q1, q2, q3);
+          } else {
+            q0 = ubyte_f32<0>(qd), q1 = ubyte_f32<1>(qd);
+            q2 = ubyte_f32<2>(qd), q3 = ubyte_f32<3>(qd);
+          }
 #pragma unroll
           for (int m = 0; m < MT; ++m) {
             float a = sub[s][r][m];
@@ -287,9 +311,8 @@ __device__ __forceinline__ void compute_chunk(const typename ChunkOf<FMT>::T (&c
         for (int s = 0; s < NW; ++s)
 #pragma unroll
           for (int r = 0; r < R; ++r) {
-            const uint32_t v = nib[s][r][e];
-            const float q0 = ubyte_f32<0>(v), q1 = ubyte_f32<1>(v);
-            const float q2 = ubyte_f32<2>(v), q3 = ubyte_f32<3>(v);
+            float q0, q1, q2, q3;
+            small_codes_f32(nib[s][r][e], q0, q1, q2, q3);
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
               float a = sub[s][r][m];
@@ -343,7 +366,7 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams p) {
   const int wv = tid / kWave;
   const int lc = lane % L;
   const int rp = lane / L;
-  const int rows_per_group = p.rows_per_block;
+  const int rows_per_group = (int)(blockDim.x / kWave) * P * R;  // = the host's row-group size
   const int n_groups = p.n_groups;
   const int n_chunks = p.k / CH;
   const int ct_max = p.kt / CH;
@@ -412,7 +435,7 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams p) {
   // takes part in the shuffles.
   auto xload = [&](int m, int j, int k0, int n4) -> f32x4 {
     f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (m < p.m_rows && j < n4) {
+    if ((MT == 1 || m < p.m_rows) && j < n4) {  // MT = 1: m_rows is 1
       const float* xrow = p.x + (size_t)m * p.k + k0;
       if (x_vec) v = *reinterpret_cast<const f32x4*>(xrow + 4 * j);
       else v = f32x4{xrow[4 * j], xrow[4 * j + 1], xrow[4 * j + 2], xrow[4 * j + 3]};
@@ -525,7 +548,7 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams p) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           const float v = group_sum(acc[s][r][m], L);
-          if (lc == 0 && rvalid[r] && m < p.m_rows) cv.y[s][(size_t)m * cv.ldy + rows[r]] = v;
+          if (lc == 0 && rvalid[r] && (MT == 1 || m < p.m_rows)) cv.y[s][(size_t)m * cv.ldy + rows[r]] = v;
         }
     g = g_next;
     cv = nv;
@@ -536,6 +559,173 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams p) {
     }
     if (!persistent) break;
   }
+}
+
+// ---------------------------------------------------------------------------
+// K-sliced GEMV for one x row (M = 1) and the 4-bit block formats (Q4_0,
+// Q4_K; 64-weight chunks).  It computes the same additions in the same order
+// as gemv_kernel with L = 32 lanes per row, MT = 1 and R = 1, so both kernels
+// give the same bits; what changes is which wave does which of them.
+//   * The 32 lanes of a row in gemv_kernel become "virtual lanes" spread over
+//     the 8 waves of a workgroup: wave w holds virtual lanes 4w .. 4w+3 of 16
+//     rows (hardware lane = 4 * row + c, virtual lane 4w + c), so it needs x
+//     only at its own chunks 4w + c + 32j, j < J.
+//   * Each wave stages that slice of x (K/8 floats) in its own LDS region and
+//     then multiplies: no workgroup barrier stands between the staging and the
+//     arithmetic, and all J chunks of a lane are loaded before the first one
+//     is used.
+//   * The butterfly over the 32 virtual lanes keeps its pairing: the two quad
+//     steps run inside the wave (DPP), the three upper levels combine the 8
+//     waves' partial sums through LDS as (w0 + w1, w2 + w3, ...), then pairs
+//     of pairs, then the two halves.
+// A workgroup walks row groups of 16 rows; x stays in LDS between them.
+template <int FMT, int NW, int J, bool MULTI>
+__global__ void __launch_bounds__(512) gemv_ks_kernel(GemvParams p) {
+  static_assert(FMT == FMT_Q40 || FMT == FMT_Q4K, "64-weight chunk formats only");
+  constexpr int CH = 64;
+  constexpr int NE4 = CH / 4;
+  constexpr int U = 4 * J;   // chunks of x held by one wave
+  constexpr int XP = U + 1;  // LDS pitch in float4s (odd: spreads banks on the staging writes)
+  constexpr int WV = 8;
+  constexpr int ROWS = 16;
+  using Chunk = typename ChunkOf<FMT>::T;
+
+  extern __shared__ f32x4 smem[];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x / kWave;
+  const int rloc = lane >> 2;
+  const int c = lane & 3;
+  const int vl = 4 * wv + c;
+  const int n_chunks = p.k / CH;
+  f32x4* xs = smem + wv * (NE4 * XP);                                     // [e4][u] of this wave
+  float* xsum = reinterpret_cast<float*>(smem + WV * NE4 * XP) + wv * (2 * U);  // [u][2]
+  float* red = reinterpret_cast<float*>(smem + WV * NE4 * XP) + WV * 2 * U;     // [2][NW][WV][ROWS]
+
+  // Weights and row of group g for this lane (the row is clamped for the
+  // loads; rows past the part's end are not stored).
+  struct View {
+    const uint8_t* w[NW];
+    int row;
+  };
+  auto view_of = [&](int g, View& v) {
+    int pi = 0;
+    if constexpr (MULTI) {
+      for (int i = 1; i < p.parts; ++i)
+        if (g >= p.part[i].group0) pi = i;
+      pi = __builtin_amdgcn_readfirstlane(pi);
+    }
+    const GemvPart& pt = p.part[pi];
+#pragma unroll
+    for (int s = 0; s < NW; ++s) v.w[s] = pt.w[s];
+    const int rr = (g - pt.group0) * ROWS + rloc;
+    v.row = rr < pt.n ? rr : pt.n - 1;
+  };
+
+  // Chunk tg = vl + 32 j of the lane's row; past the last chunk the last one
+  // is loaded again (same cache lines) and not used.
+  Chunk ch[J][NW];
+  auto fetch_all = [&](const View& v) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int tg = vl + 32 * j;
+      const int tl = tg < n_chunks ? tg : n_chunks - 1;
+#pragma unroll
+      for (int s = 0; s < NW; ++s) ch[j][s] = load_chunk<FMT>(p, v.w[s], nullptr, nullptr, v.row, tl);
+    }
+  };
+
+  int g = blockIdx.x;
+  if (g >= p.n_groups) return;
+  View cv;
+  view_of(g, cv);
+
+  // x of this wave's chunks: float4 16 * (4w + 32j) + lane covers chunks
+  // 4w + 32j .. +3.  The loads go out before the first weights.
+  {
+    const bool x_vec = (reinterpret_cast<uintptr_t>(p.x) & 15u) == 0;
+    const int n4 = p.k >> 2;
+    f32x4 xv[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int f = 16 * (4 * wv + 32 * j) + lane;
+      xv[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      if (f < n4) {
+        if (x_vec) xv[j] = *reinterpret_cast<const f32x4*>(p.x + 4 * f);
+        else xv[j] = f32x4{p.x[4 * f], p.x[4 * f + 1], p.x[4 * f + 2], p.x[4 * f + 3]};
+      }
+    }
+    fetch_all(cv);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int f = 16 * (4 * wv + 32 * j) + lane;
+      const int e4 = lane & 15;
+      const int u = 4 * j + (lane >> 4);
+      if (f < n4) xs[e4 * XP + u] = xv[j];
+      // sum of each 32-element half: 8 consecutive float4s on 8 consecutive lanes
+      const float sm = group_sum(((xv[j].x + xv[j].y) + xv[j].z) + xv[j].w, 8);
+      if (f < n4 && (e4 & 7) == 0) xsum[u * 2 + (e4 >> 3)] = sm;
+    }
+    // LDS operations of one wave complete in order; this only keeps the
+    // compiler from moving the reads above the writes.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
+  // One row group: multiply the loaded chunks, issue the next group's loads,
+  // then finish the butterfly across waves and store.
+  auto group = [&](int it) {
+    float acc[NW][1][1];
+#pragma unroll
+    for (int s = 0; s < NW; ++s) acc[s][0][0] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int tg = vl + 32 * j;
+      if (tg < n_chunks) {
+        Chunk one[NW][1];
+#pragma unroll
+        for (int s = 0; s < NW; ++s) one[s][0] = ch[j][s];
+        compute_chunk<FMT, 1, NW, 1>(one, xs, xsum, XP, U, 4 * j + c, tg, acc);
+      }
+    }
+    float* rb = red + (it & 1) * (NW * WV * ROWS);
+#pragma unroll
+    for (int s = 0; s < NW; ++s) {
+      float v = acc[s][0][0];
+      v += dpp_mov<0xB1>(v);  // quad_perm [1,0,3,2]
+      v += dpp_mov<0x4E>(v);  // quad_perm [2,3,0,1]
+      if (c == 0) rb[(s * WV + wv) * ROWS + rloc] = v;
+    }
+    const int g_done = g;
+    g += (int)gridDim.x;
+    if (g < p.n_groups) {
+      view_of(g, cv);
+      fetch_all(cv);
+    }
+    __syncthreads();
+    if (threadIdx.x < NW * ROWS) {
+      const int s = threadIdx.x / ROWS;
+      const int r = threadIdx.x % ROWS;
+      const float* a = rb + s * WV * ROWS + r;
+      const float b0 = a[0 * ROWS] + a[1 * ROWS];
+      const float b1 = a[2 * ROWS] + a[3 * ROWS];
+      const float b2 = a[4 * ROWS] + a[5 * ROWS];
+      const float b3 = a[6 * ROWS] + a[7 * ROWS];
+      const float t = (b0 + b1) + (b2 + b3);
+      int pi = 0;
+      if constexpr (MULTI) {
+        for (int i = 1; i < p.parts; ++i)
+          if (g_done >= p.part[i].group0) pi = i;
+      }
+      const GemvPart& pt = p.part[pi];
+      const int rr = (g_done - pt.group0) * ROWS + r;
+      if (rr < pt.n) pt.y[s][rr] = t;
+    }
+  };
+  // The first group is peeled off the loop, so that its loads, issued in
+  // straight-line code, are waited for one chunk at a time.
+  group(0);
+  for (int it = 1; g < p.n_groups; ++it) group(it);
 }
 
 // ---------------------------------------------------------------------------

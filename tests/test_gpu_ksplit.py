@@ -1,0 +1,91 @@
+"""The K-sliced GEMV (one x row, Q4_0 and Q4_K) against the chunked GEMV it
+replaces at M = 1: the two kernels make the same additions in the same order,
+so their outputs must agree bit for bit (the tuning switch QG_GEMV_KS=0 selects
+the chunked kernel), and both against the f64 oracle."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from test_gpu_parity import assert_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def bits(a):
+    return np.ascontiguousarray(a).view(np.uint32)
+
+
+def both(call):
+    """(K-sliced result, chunked result) of one call."""
+    old = os.environ.get("QG_GEMV_KS")
+    try:
+        os.environ["QG_GEMV_KS"] = "1"
+        a = call()
+        os.environ["QG_GEMV_KS"] = "0"
+        b = call()
+    finally:
+        if old is None:
+            os.environ.pop("QG_GEMV_KS", None)
+        else:
+            os.environ["QG_GEMV_KS"] = old
+    return a, b
+
+
+# K from one super-block to 32 (one to four chunks per lane, ragged last lanes)
+@pytest.mark.parametrize("n,k", [(1, 256), (15, 512), (17, 1024), (33, 2304), (300, 4096),
+                                 (70, 5888), (40, 8192), (4099, 4096)])
+def test_q4_k_ksplit_equals_chunked(lib, n, k):
+    w, x = synth.q4_k_case(8100 + n, 1, n, k)
+    dw, dx = dev(w), dev(x)
+    a, b = both(lambda: host(lib.qgemv_q4_k(dw, dx, n, k)))
+    assert np.array_equal(bits(a), bits(b))
+    assert_close(a, oracle.decode_q4_k(w, n, k), x, f"q4_k ksplit n{n} k{k}")
+
+
+@pytest.mark.parametrize("n,k", [(3, 64), (257, 4096), (31, 8128)])
+def test_q4_0_ksplit_equals_chunked(lib, n, k):
+    w, x = synth.q4_0_case(8200 + n, 1, n, k)
+    dw, dx = dev(w), dev(x)
+    a, b = both(lambda: host(lib.qgemv_q4_0(dw, dx, n, k)))
+    assert np.array_equal(bits(a), bits(b))
+    assert_close(a, oracle.decode_q4_0(w, n, k), x, f"q4_0 ksplit n{n} k{k}")
+
+
+@pytest.mark.parametrize("n,k", [(50, 4096), (19, 2048 + 64)])
+def test_dual_equals_ksplit_single_calls(lib, n, k):
+    """The dual product keeps the chunked kernel; its second output must still
+    equal the single call, which takes the K-sliced kernel."""
+    wa, wb, x = synth.dual_q4_0_case(8300 + n, 1, n, k)
+    dwa, dwb, dx = dev(wa), dev(wb), dev(x)
+    (a0, a1), (b0, b1) = both(lambda: tuple(host(t) for t in lib.qgemv_dual_q4_0(dwa, dwb, dx, n, k)))
+    assert np.array_equal(bits(a0), bits(b0)) and np.array_equal(bits(a1), bits(b1))
+    single = host(lib.qgemv_q4_0(dwb, dx, n, k))
+    assert np.array_equal(bits(a1), bits(single))
+
+
+def test_multi_ksplit_equals_chunked_and_single(lib):
+    ns, k = (96, 40, 17), 4096
+    ws, x = synth.q4_k_multi_case(8400, 1, ns, k)
+    dws, dx = [dev(w) for w in ws], dev(x)
+    a, b = both(lambda: host(lib.qgemv_q4_k_multi(dws, dx, list(ns), k)))
+    assert np.array_equal(bits(a), bits(b))
+    col = 0
+    for w, dw, n in zip(ws, dws, ns):
+        assert np.array_equal(bits(a[:, col:col + n]), bits(host(lib.qgemv_q4_k(dw, dx, n, k))))
+        col += n
+
+
+def test_unaligned_x_ksplit(lib):
+    import torch
+    n, k = 40, 4096
+    w, x = synth.q4_k_case(8500, 1, n, k)
+    buf = torch.zeros(x.size + 1, dtype=torch.float32, device="cuda")
+    buf[1:] = torch.from_numpy(np.ascontiguousarray(x).ravel()).cuda()
+    xo = buf[1:].view(x.shape)
+    dw = dev(w)
+    a, b = both(lambda: host(lib.qgemv_q4_k(dw, xo, n, k)))
+    assert np.array_equal(bits(a), bits(b))
+    assert np.array_equal(bits(a), bits(host(lib.qgemv_q4_k(dw, dev(x), n, k))))
