@@ -277,56 +277,68 @@ hipError_t launch_gemv_mt(const GemvPlan& pl, const GemvParams& p, dim3 g, dim3 
   return hipErrorInvalidValue;
 }
 
-// K-sliced kernel for M = 1 and the 64-weight chunk formats (same bits as
-// the chunked kernel with 32 lanes per row); J = chunks per lane.
-constexpr int kKsRows = 16;
-
-template <int FMT, int NW, int J>
+// K-sliced kernel for M = 1 (same bits as the chunked kernel with the same
+// L and R); J = chunks per lane and row.
+template <int FMT, int L, int R, int J>
 hipError_t launch_gemv_ks_j(const GemvParams& p, dim3 grid, size_t lds, hipStream_t s) {
   if (p.parts > 1) {
-    if constexpr (NW == 1 && FMT == FMT_Q4K) {
-      hipLaunchKernelGGL((gemv_ks_kernel<FMT, NW, J, true>), grid, dim3(512), lds, s, p);
+    if constexpr (FMT == FMT_Q4K || FMT == FMT_AFF) {
+      hipLaunchKernelGGL((gemv_ks_kernel<FMT, 1, L, R, J, true>), grid, dim3(512), lds, s, p);
       return hipSuccess;
     }
     return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL((gemv_ks_kernel<FMT, NW, J, false>), grid, dim3(512), lds, s, p);
+  hipLaunchKernelGGL((gemv_ks_kernel<FMT, 1, L, R, J, false>), grid, dim3(512), lds, s, p);
   return hipSuccess;
 }
 
-size_t ks_lds(int j, int nw) {
-  const size_t u = 4 * (size_t)j;
-  return 8 * 16 * (u + 1) * 16 + 8 * 2 * u * 4 + 2 * (size_t)nw * 8 * kKsRows * 4;
+template <int FMT>
+size_t ks_lds(int l, int r, int j) {
+  const size_t ne4 = FmtTraits<FMT>::CH / 4;
+  const size_t u = (size_t)(l / 8) * j;
+  const size_t rows = (size_t)(kWave / (l / 8)) * r;
+  return 8 * ne4 * (u + 1) * 16 + 8 * 2 * u * 4 + 2 * 8 * rows * 4;
 }
 
-// Chunks per lane the K-sliced kernel is built for (0: not eligible).
+// Chunks per lane the K-sliced kernel takes for this call (0: not eligible):
+// one x row, one weight stream, x in LDS for the whole K, and the chunked
+// kernel's shape (L, R) = (32, 1) for the 64-weight chunks of Q4_0/Q4_K or
+// (64, 2) for the 32-code chunks of the affine formats (one float4 of x per
+// lane and chunk slice).
 template <int FMT, int NW>
 int ks_chunks(const GemvPlan& pl, int64_t m, int64_t k) {
-  if constexpr (FMT != FMT_Q40 && FMT != FMT_Q4K) {
-    return 0;
-  } else {
-    // tuning override (same results either way): QG_GEMV_KS=0 keeps the chunked kernel
-    if (const char* env = getenv("QG_GEMV_KS"))
-      if (env[0] == '0') return 0;
-    if (NW != 1) return 0;
-    if (m != 1 || pl.mt != 1 || pl.l != 32 || pl.r != 1 || !pl.persistent) return 0;
-    const int64_t j = cdiv(k / 64, 32);
-    return j >= 1 && j <= 4 ? (int)j : 0;
+  // tuning override (same results either way): QG_GEMV_KS=0 keeps the chunked kernel
+  if (const char* env = getenv("QG_GEMV_KS"))
+    if (env[0] == '0') return 0;
+  // the dual product (two streams) keeps the chunked kernel: it measured faster there
+  if (NW != 1 || m != 1 || pl.mt != 1 || !pl.persistent) return 0;
+  constexpr bool Q4 = FMT == FMT_Q40 || FMT == FMT_Q4K;
+  if (Q4 ? !(pl.l == 32 && pl.r == 1) : !(pl.l == 64 && pl.r == 2)) return 0;
+  const int64_t j = cdiv(k / FmtTraits<FMT>::CH, pl.l);
+  return j >= 1 && j <= 4 ? (int)j : 0;
+}
+
+template <int FMT, int L, int R>
+hipError_t launch_gemv_ks_lr(int j, const GemvParams& p, dim3 grid, hipStream_t s) {
+  const size_t lds = ks_lds<FMT>(L, R, j);
+  switch (j) {
+    case 1: return launch_gemv_ks_j<FMT, L, R, 1>(p, grid, lds, s);
+    case 2: return launch_gemv_ks_j<FMT, L, R, 2>(p, grid, lds, s);
+    case 3: return launch_gemv_ks_j<FMT, L, R, 3>(p, grid, lds, s);
+    case 4: return launch_gemv_ks_j<FMT, L, R, 4>(p, grid, lds, s);
   }
+  return hipErrorInvalidValue;
 }
 
 template <int FMT, int NW>
-hipError_t launch_gemv_ks(int j, const GemvParams& p, dim3 grid, hipStream_t s) {
-  // one stream only: for the dual product the chunked kernel measured faster
-  if constexpr (NW != 1 || (FMT != FMT_Q40 && FMT != FMT_Q4K)) return hipErrorInvalidValue;
-  const size_t lds = ks_lds(j, NW);
-  if constexpr (NW == 1 && (FMT == FMT_Q40 || FMT == FMT_Q4K)) switch (j) {
-    case 1: return launch_gemv_ks_j<FMT, NW, 1>(p, grid, lds, s);
-    case 2: return launch_gemv_ks_j<FMT, NW, 2>(p, grid, lds, s);
-    case 3: return launch_gemv_ks_j<FMT, NW, 3>(p, grid, lds, s);
-    case 4: return launch_gemv_ks_j<FMT, NW, 4>(p, grid, lds, s);
+hipError_t launch_gemv_ks(const GemvPlan& pl, int j, const GemvParams& p, dim3 grid, hipStream_t s) {
+  if constexpr (NW != 1) {
+    return hipErrorInvalidValue;
+  } else if constexpr (FMT == FMT_Q40 || FMT == FMT_Q4K) {
+    return pl.l == 32 && pl.r == 1 ? launch_gemv_ks_lr<FMT, 32, 1>(j, p, grid, s) : hipErrorInvalidValue;
+  } else {
+    return pl.l == 64 && pl.r == 2 ? launch_gemv_ks_lr<FMT, 64, 2>(j, p, grid, s) : hipErrorInvalidValue;
   }
-  return hipErrorInvalidValue;
 }
 
 // Runs a part list on the chunked GEMV kernel (or on the plain one when
@@ -364,7 +376,7 @@ qg_status run_gemv(const char* op, const HostPart* parts, int nparts, const floa
   const GemvPlan pl = plan_gemv<FMT>(m, k, NW);
   const int ks = ks_chunks<FMT, NW>(pl, m, k);
   const GemvGrid gg = grid_gemv<FMT>(pl, parts, nparts);
-  const int rows_per_group = ks ? kKsRows : (int)gg.groups_rows;
+  const int rows_per_group = ks ? (int)(kWave / (pl.l / 8) * pl.r) : (int)gg.groups_rows;
   GemvParams p{};
   int64_t groups = 0;
   for (int pi = 0; pi < nparts; ++pi) {
@@ -397,7 +409,7 @@ qg_status run_gemv(const char* op, const HostPart* parts, int nparts, const floa
     if (const char* env = getenv("QG_GEMV_KS")) bpc = atoi(env) > 0 ? atoi(env) : 2;
     const int64_t cap = bpc * device_cus();
     const int64_t grid = groups < cap ? groups : cap;
-    const hipError_t e = launch_gemv_ks<FMT, NW>(ks, p, dim3((unsigned)grid), s);
+    const hipError_t e = launch_gemv_ks<FMT, NW>(pl, ks, p, dim3((unsigned)grid), s);
     if (e != hipSuccess) return launch_error(op, "launch setup failed", e);
     return launch_status(op);
   }

@@ -562,50 +562,56 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// K-sliced GEMV for one x row (M = 1) and the 4-bit block formats (Q4_0,
-// Q4_K; 64-weight chunks).  It computes the same additions in the same order
-// as gemv_kernel with L = 32 lanes per row, MT = 1 and R = 1, so both kernels
-// give the same bits; what changes is which wave does which of them.
-//   * The 32 lanes of a row in gemv_kernel become "virtual lanes" spread over
-//     the 8 waves of a workgroup: wave w holds virtual lanes 4w .. 4w+3 of 16
-//     rows (hardware lane = 4 * row + c, virtual lane 4w + c), so it needs x
-//     only at its own chunks 4w + c + 32j, j < J.
-//   * Each wave stages that slice of x (K/8 floats) in its own LDS region and
-//     then multiplies: no workgroup barrier stands between the staging and the
+// K-sliced GEMV for one x row (M = 1).  It computes the same additions in the
+// same order as gemv_kernel with the same L (lanes per row) and R (rows per
+// lane) at MT = 1, so both kernels give the same bits; what changes is which
+// wave does which of them.
+//   * The L lanes of a row in gemv_kernel become "virtual lanes" spread over
+//     the 8 waves of a workgroup: wave w holds virtual lanes LW*w .. LW*w+LW-1
+//     (LW = L/8) of 64/LW row sets of R rows each (hardware lane = LW * set +
+//     c, virtual lane LW*w + c), so it needs x only at its own chunks
+//     LW*w + c + L*j, j < J: one eighth of K.
+//   * Each wave stages that slice of x in its own LDS region and then
+//     multiplies: no workgroup barrier stands between the staging and the
 //     arithmetic, and all J chunks of a lane are loaded before the first one
 //     is used.
-//   * The butterfly over the 32 virtual lanes keeps its pairing: the two quad
-//     steps run inside the wave (DPP), the three upper levels combine the 8
-//     waves' partial sums through LDS as (w0 + w1, w2 + w3, ...), then pairs
-//     of pairs, then the two halves.
-// A workgroup walks row groups of 16 rows; x stays in LDS between them.
-template <int FMT, int NW, int J, bool MULTI>
+//   * The butterfly over the L virtual lanes keeps its pairing: its first
+//     log2(LW) levels run inside the wave (DPP), the three upper levels
+//     combine the 8 waves' partial sums through LDS as (w0 + w1, w2 + w3,
+//     ...), then pairs of pairs, then the two halves.
+// A workgroup walks row groups of 64/LW*R rows; x stays in LDS between them.
+template <int FMT, int NW, int L, int R, int J, bool MULTI>
 __global__ void __launch_bounds__(512) gemv_ks_kernel(GemvParams p) {
-  static_assert(FMT == FMT_Q40 || FMT == FMT_Q4K, "64-weight chunk formats only");
-  constexpr int CH = 64;
+  static_assert(L == 32 || L == 64, "8 waves of 4 or 8 virtual lanes");
+  constexpr int CH = FmtTraits<FMT>::CH;
   constexpr int NE4 = CH / 4;
-  constexpr int U = 4 * J;   // chunks of x held by one wave
-  constexpr int XP = U + 1;  // LDS pitch in float4s (odd: spreads banks on the staging writes)
   constexpr int WV = 8;
-  constexpr int ROWS = 16;
+  constexpr int LW = L / WV;             // lanes of a row inside one wave
+  constexpr int RS = kWave / LW;         // row sets per wave
+  constexpr int ROWS = RS * R;           // rows per group
+  constexpr int U = LW * J;              // chunks of x held by one wave
+  constexpr int XP = U + 1;              // LDS pitch in float4s (odd: spreads banks on the staging writes)
+  static_assert(LW * NE4 == kWave, "one float4 of x per lane and chunk slice");
   using Chunk = typename ChunkOf<FMT>::T;
 
   extern __shared__ f32x4 smem[];
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x / kWave;
-  const int rloc = lane >> 2;
-  const int c = lane & 3;
-  const int vl = 4 * wv + c;
+  const int rset = lane / LW;
+  const int c = lane % LW;
+  const int vl = LW * wv + c;
   const int n_chunks = p.k / CH;
-  f32x4* xs = smem + wv * (NE4 * XP);                                     // [e4][u] of this wave
+  f32x4* xs = smem + wv * (NE4 * XP);                                           // [e4][u] of this wave
   float* xsum = reinterpret_cast<float*>(smem + WV * NE4 * XP) + wv * (2 * U);  // [u][2]
   float* red = reinterpret_cast<float*>(smem + WV * NE4 * XP) + WV * 2 * U;     // [2][NW][WV][ROWS]
 
-  // Weights and row of group g for this lane (the row is clamped for the
+  // Weights and rows of group g for this lane (rows are clamped for the
   // loads; rows past the part's end are not stored).
   struct View {
     const uint8_t* w[NW];
-    int row;
+    const float* sc;
+    const float* bi;
+    int row[R];
   };
   auto view_of = [&](int g, View& v) {
     int pi = 0;
@@ -617,20 +623,27 @@ __global__ void __launch_bounds__(512) gemv_ks_kernel(GemvParams p) {
     const GemvPart& pt = p.part[pi];
 #pragma unroll
     for (int s = 0; s < NW; ++s) v.w[s] = pt.w[s];
-    const int rr = (g - pt.group0) * ROWS + rloc;
-    v.row = rr < pt.n ? rr : pt.n - 1;
+    v.sc = pt.scales;
+    v.bi = pt.biases;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int rr = (g - pt.group0) * ROWS + rset + RS * r;
+      v.row[r] = rr < pt.n ? rr : pt.n - 1;
+    }
   };
 
-  // Chunk tg = vl + 32 j of the lane's row; past the last chunk the last one
+  // Chunk tg = vl + L j of the lane's rows; past the last chunk the last one
   // is loaded again (same cache lines) and not used.
-  Chunk ch[J][NW];
+  Chunk ch[J][NW][R];
   auto fetch_all = [&](const View& v) {
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int tg = vl + 32 * j;
+      const int tg = vl + L * j;
       const int tl = tg < n_chunks ? tg : n_chunks - 1;
 #pragma unroll
-      for (int s = 0; s < NW; ++s) ch[j][s] = load_chunk<FMT>(p, v.w[s], nullptr, nullptr, v.row, tl);
+      for (int s = 0; s < NW; ++s)
+#pragma unroll
+        for (int r = 0; r < R; ++r) ch[j][s][r] = load_chunk<FMT>(p, v.w[s], v.sc, v.bi, v.row[r], tl);
     }
   };
 
@@ -639,15 +652,15 @@ __global__ void __launch_bounds__(512) gemv_ks_kernel(GemvParams p) {
   View cv;
   view_of(g, cv);
 
-  // x of this wave's chunks: float4 16 * (4w + 32j) + lane covers chunks
-  // 4w + 32j .. +3.  The loads go out before the first weights.
+  // x of this wave's chunks: float4 NE4 * (LW*w + L*j) + lane covers chunks
+  // LW*w + L*j .. +LW-1.  The loads go out before the first weights.
   {
     const bool x_vec = (reinterpret_cast<uintptr_t>(p.x) & 15u) == 0;
     const int n4 = p.k >> 2;
     f32x4 xv[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int f = 16 * (4 * wv + 32 * j) + lane;
+      const int f = NE4 * (LW * wv + L * j) + lane;
       xv[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       if (f < n4) {
         if (x_vec) xv[j] = *reinterpret_cast<const f32x4*>(p.x + 4 * f);
@@ -657,9 +670,9 @@ __global__ void __launch_bounds__(512) gemv_ks_kernel(GemvParams p) {
     fetch_all(cv);
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int f = 16 * (4 * wv + 32 * j) + lane;
-      const int e4 = lane & 15;
-      const int u = 4 * j + (lane >> 4);
+      const int f = NE4 * (LW * wv + L * j) + lane;
+      const int e4 = lane % NE4;
+      const int u = LW * j + lane / NE4;
       if (f < n4) xs[e4 * XP + u] = xv[j];
       // sum of each 32-element half: 8 consecutive float4s on 8 consecutive lanes
       const float sm = group_sum(((xv[j].x + xv[j].y) + xv[j].z) + xv[j].w, 8);
@@ -675,27 +688,27 @@ __global__ void __launch_bounds__(512) gemv_ks_kernel(GemvParams p) {
   // One row group: multiply the loaded chunks, issue the next group's loads,
   // then finish the butterfly across waves and store.
   auto group = [&](int it) {
-    float acc[NW][1][1];
+    float acc[NW][R][1];
 #pragma unroll
-    for (int s = 0; s < NW; ++s) acc[s][0][0] = 0.0f;
+    for (int s = 0; s < NW; ++s)
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[s][r][0] = 0.0f;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int tg = vl + 32 * j;
-      if (tg < n_chunks) {
-        Chunk one[NW][1];
-#pragma unroll
-        for (int s = 0; s < NW; ++s) one[s][0] = ch[j][s];
-        compute_chunk<FMT, 1, NW, 1>(one, xs, xsum, XP, U, 4 * j + c, tg, acc);
-      }
+      const int tg = vl + L * j;
+      if (tg < n_chunks) compute_chunk<FMT, 1, NW, R>(ch[j], xs, xsum, XP, U, LW * j + c, tg, acc);
     }
     float* rb = red + (it & 1) * (NW * WV * ROWS);
 #pragma unroll
-    for (int s = 0; s < NW; ++s) {
-      float v = acc[s][0][0];
-      v += dpp_mov<0xB1>(v);  // quad_perm [1,0,3,2]
-      v += dpp_mov<0x4E>(v);  // quad_perm [2,3,0,1]
-      if (c == 0) rb[(s * WV + wv) * ROWS + rloc] = v;
-    }
+    for (int s = 0; s < NW; ++s)
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float v = acc[s][r][0];
+        v += dpp_mov<0xB1>(v);                      // quad_perm [1,0,3,2]
+        v += dpp_mov<0x4E>(v);                      // quad_perm [2,3,0,1]
+        if constexpr (LW == 8) v += dpp_mov<0x141>(v);  // row_half_mirror
+        if (c == 0) rb[(s * WV + wv) * ROWS + rset + RS * r] = v;
+      }
     const int g_done = g;
     g += (int)gridDim.x;
     if (g < p.n_groups) {

@@ -1,7 +1,8 @@
-"""The K-sliced GEMV (one x row, Q4_0 and Q4_K) against the chunked GEMV it
-replaces at M = 1: the two kernels make the same additions in the same order,
-so their outputs must agree bit for bit (the tuning switch QG_GEMV_KS=0 selects
-the chunked kernel), and both against the f64 oracle."""
+"""The K-sliced GEMV (one x row: Q4_0, Q4_K, u8 and packed affine codes,
+single and multi-part) against the chunked GEMV it replaces at M = 1: the two
+kernels make the same additions in the same order, so their outputs must agree
+bit for bit (the tuning switch QG_GEMV_KS=0 selects the chunked kernel), and
+both against the f64 oracle."""
 import os
 
 import numpy as np
@@ -89,3 +90,39 @@ def test_unaligned_x_ksplit(lib):
     a, b = both(lambda: host(lib.qgemv_q4_k(dw, xo, n, k)))
     assert np.array_equal(bits(a), bits(b))
     assert np.array_equal(bits(a), bits(host(lib.qgemv_q4_k(dw, dev(x), n, k))))
+
+
+# affine codes: 32-code chunks, 64 lanes per row and two rows per lane in both
+# kernels; K from 2048 (one chunk per lane) to 8192 (four), ragged last lanes
+@pytest.mark.parametrize("n,k,gs,code_max", [(1, 2048, 64, 15), (17, 2208, 32, 255), (40, 4096, 64, 15),
+                                             (33, 6144, 512, 255), (300, 8192, 128, 15), (2049, 4096, 64, 255)])
+def test_affine_ksplit_equals_chunked(lib, n, k, gs, code_max):
+    x, q, s, b = synth.affine_case(8600 + n, 1, n, k, gs, code_max)
+    dx, dq, ds, db = dev(x), dev(q), dev(s), dev(b)
+    a, c = both(lambda: host(lib.qmm_affine_t(dx, dq, ds, db, gs)))
+    assert np.array_equal(bits(a), bits(c))
+    assert_close(a, oracle.decode_affine(q, s, b, n, k, gs), x, f"affine ksplit n{n} k{k} gs{gs}")
+
+
+@pytest.mark.parametrize("n,k,gs", [(29, 4096, 64), (64, 2208, 32), (5, 8192, 256)])
+def test_packed_ksplit_equals_chunked_and_u8(lib, n, k, gs):
+    import torch
+    x, q, s, b = synth.affine_case(8700 + n, 1, n, k, gs)
+    wp = torch.from_numpy(synth.pack_b4_u32(q).view(np.int32)).cuda()
+    dx, ds, db = dev(x), dev(s), dev(b)
+    a, c = both(lambda: host(lib.qmm_affine_t_packed(dx, wp, ds, db, gs)))
+    assert np.array_equal(bits(a), bits(c))
+    assert np.array_equal(bits(a), bits(host(lib.qmm_affine_t(dx, dev(q), ds, db, gs))))
+
+
+def test_fused_qkv_ksplit_equals_chunked_and_split(lib):
+    k, gs, qs, ks, vs = 4096, 64, 96, 40, 17
+    n = qs + ks + vs
+    x, q, s, b = synth.affine_case(8800, 1, n, k, gs)
+    dx, dq, ds, db = dev(x), dev(q), dev(s), dev(b)
+    a, c = both(lambda: tuple(host(t) for t in lib.qmm_affine_t_qkv(dx, dq, ds, db, gs, qs, ks, vs)))
+    for u, v in zip(a, c):
+        assert np.array_equal(bits(u), bits(v))
+    y = lib.qmm_affine_t(dx, dq, ds, db, gs)
+    for got, ref in zip(a, lib.qkv_split_f32(y, 1, qs, ks, vs)):
+        assert np.array_equal(bits(got), bits(host(ref)))
