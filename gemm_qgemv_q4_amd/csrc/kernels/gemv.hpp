@@ -213,6 +213,16 @@ __device__ __forceinline__ void unpack_q4k(const ChunkQ4K& c, int h, uint32_t (&
                          : (q[i] >> 4) & 0x0F0F0F0Fu);   // sub-block 2c+1: high nibbles
 }
 
+// x of one chunk for a single x row, read from LDS before any of it is used:
+// all NE4 reads are in flight together instead of two at a time, so a wave
+// waits for LDS once per chunk.  (Only the timing of the reads changes.)
+template <int NE4>
+__device__ __forceinline__ void preload_x(const f32x4* xs, int ctp, int t, f32x4 (&xall)[NE4]) {
+#pragma unroll
+  for (int e4 = 0; e4 < NE4; ++e4) xall[e4] = xs[e4 * ctp + t];
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Decode one chunk of every (stream, row) and accumulate it.
 template <int FMT, int MT, int NW, int R>
 __device__ __forceinline__ void compute_chunk(const typename ChunkOf<FMT>::T (&ch)[NW][R], const f32x4* xs,
@@ -234,11 +244,13 @@ __device__ __forceinline__ void compute_chunk(const typename ChunkOf<FMT>::T (&c
       for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int m = 0; m < MT; ++m) sub[s][r][m] = 0.0f;
+    f32x4 xall[MT == 1 ? NE4 : 1];
+    if constexpr (MT == 1) preload_x<NE4>(xs, ctp, t, xall);
 #pragma unroll
     for (int e4 = 0; e4 < NE4; ++e4) {
       f32x4 xv[MT];
 #pragma unroll
-      for (int m = 0; m < MT; ++m) xv[m] = xs[(m * NE4 + e4) * ctp + t];
+      for (int m = 0; m < MT; ++m) xv[m] = MT == 1 ? xall[MT == 1 ? e4 : 0] : xs[(m * NE4 + e4) * ctp + t];
 #pragma unroll
       for (int s = 0; s < NW; ++s)
 #pragma unroll
@@ -284,6 +296,8 @@ __device__ __forceinline__ void compute_chunk(const typename ChunkOf<FMT>::T (&c
         if constexpr (FMT == FMT_Q40) hs[s][r] = q40_scales(ch[s][r]);
         else hs[s][r] = q4k_scales(ch[s][r], tg & 3);
       }
+    f32x4 xall[MT == 1 ? NE4 : 1];
+    if constexpr (MT == 1) preload_x<NE4>(xs, ctp, t, xall);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       uint32_t nib[NW][R][8];
@@ -306,7 +320,7 @@ __device__ __forceinline__ void compute_chunk(const typename ChunkOf<FMT>::T (&c
         const int e4 = h * 8 + e;
         f32x4 xv[MT];
 #pragma unroll
-        for (int m = 0; m < MT; ++m) xv[m] = xs[(m * NE4 + e4) * ctp + t];
+        for (int m = 0; m < MT; ++m) xv[m] = MT == 1 ? xall[MT == 1 ? e4 : 0] : xs[(m * NE4 + e4) * ctp + t];
 #pragma unroll
         for (int s = 0; s < NW; ++s)
 #pragma unroll
