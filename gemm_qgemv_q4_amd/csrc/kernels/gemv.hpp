@@ -213,13 +213,17 @@ __device__ __forceinline__ void unpack_q4k(const ChunkQ4K& c, int h, uint32_t (&
                          : (q[i] >> 4) & 0x0F0F0F0Fu);   // sub-block 2c+1: high nibbles
 }
 
-// x of one chunk for a single x row, read from LDS before any of it is used:
-// all NE4 reads are in flight together instead of two at a time, so a wave
-// waits for LDS once per chunk.  (Only the timing of the reads changes.)
+// x of one chunk for a single x row and its two per-32 sums, read from LDS
+// before any of them is used: all reads are in flight together instead of two
+// at a time, so a wave waits for LDS once per chunk.  (Only the timing of the
+// reads changes.)
 template <int NE4>
-__device__ __forceinline__ void preload_x(const f32x4* xs, int ctp, int t, f32x4 (&xall)[NE4]) {
+__device__ __forceinline__ void preload_x(const f32x4* xs, const float* xsum, int ctp, int t, f32x4 (&xall)[NE4],
+                                          float (&sall)[2]) {
 #pragma unroll
   for (int e4 = 0; e4 < NE4; ++e4) xall[e4] = xs[e4 * ctp + t];
+  sall[0] = xsum[t * 2];
+  sall[1] = NE4 > 8 ? xsum[t * 2 + 1] : 0.0f;  // 32-element chunks have one sum
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -245,7 +249,8 @@ __device__ __forceinline__ void compute_chunk(const typename ChunkOf<FMT>::T (&c
 #pragma unroll
         for (int m = 0; m < MT; ++m) sub[s][r][m] = 0.0f;
     f32x4 xall[MT == 1 ? NE4 : 1];
-    if constexpr (MT == 1) preload_x<NE4>(xs, ctp, t, xall);
+    float sall[2];
+    if constexpr (MT == 1) preload_x<NE4>(xs, xsum, ctp, t, xall, sall);
 #pragma unroll
     for (int e4 = 0; e4 < NE4; ++e4) {
       f32x4 xv[MT];
@@ -276,7 +281,7 @@ __device__ __forceinline__ void compute_chunk(const typename ChunkOf<FMT>::T (&c
     }
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      const float sx = xsum[(m * ct_max + t) * 2];
+      const float sx = MT == 1 ? sall[0] : xsum[(m * ct_max + t) * 2];
 #pragma unroll
       for (int s = 0; s < NW; ++s)
 #pragma unroll
@@ -297,7 +302,8 @@ __device__ __forceinline__ void compute_chunk(const typename ChunkOf<FMT>::T (&c
         else hs[s][r] = q4k_scales(ch[s][r], tg & 3);
       }
     f32x4 xall[MT == 1 ? NE4 : 1];
-    if constexpr (MT == 1) preload_x<NE4>(xs, ctp, t, xall);
+    float sall[2];
+    if constexpr (MT == 1) preload_x<NE4>(xs, xsum, ctp, t, xall, sall);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       uint32_t nib[NW][R][8];
@@ -341,7 +347,7 @@ __device__ __forceinline__ void compute_chunk(const typename ChunkOf<FMT>::T (&c
       // fold this 32-weight half: acc += A*dot + B*sum(x)
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        const float sx = xsum[(m * ct_max + t) * 2 + h];
+        const float sx = MT == 1 ? sall[h] : xsum[(m * ct_max + t) * 2 + h];
 #pragma unroll
         for (int s = 0; s < NW; ++s)
 #pragma unroll
