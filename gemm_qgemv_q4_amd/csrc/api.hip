@@ -19,6 +19,7 @@
 #include "qgemv_q4.h"
 #include "kernels/gemv.hpp"
 #include "kernels/mfma.hpp"
+#include "kernels/mma_gemv.hpp"
 #include "kernels/split.hpp"
 
 using namespace qg;
@@ -341,6 +342,60 @@ hipError_t launch_gemv_ks(const GemvPlan& pl, int j, const GemvParams& p, dim3 g
   }
 }
 
+// Matrix-core GEMV for 2..8 rows of x per launch and the affine formats:
+// group size >= 64, K a multiple of 512 with K/512 in {1, 2, 4, 8} (up to 8
+// pairs of 32-column blocks per wave, so x of 8 rows fits in LDS), codes
+// aligned for their vector loads.  Returns the pairs per wave (0: not taken).
+template <int FMT>
+int mma_pairs(const HostPart* parts, int nparts, int64_t m, int64_t k, int64_t gs) {
+  if constexpr (FMT != FMT_AFF && FMT != FMT_AFF4) {
+    return 0;
+  } else {
+    // tuning override (different rounding, same tolerance): QG_GEMV_MMA=0 keeps the FMA kernels
+    if (const char* env = getenv("QG_GEMV_MMA"))
+      if (env[0] == '0') return 0;
+    if (m < 2 || gs < 64 || k % 512 != 0) return 0;
+    const int64_t np = k / 512;
+    if (np != 1 && np != 2 && np != 4 && np != 8) return 0;
+    for (int pi = 0; pi < nparts; ++pi)
+      if (!aligned(parts[pi].w[0], FMT == FMT_AFF ? 16 : 8)) return 0;
+    return (int)np;
+  }
+}
+
+template <int FMT, int NP>
+hipError_t launch_gemv_mma_np(const GemvParams& p, dim3 grid, hipStream_t s) {
+  constexpr size_t lds = (size_t)mma_lds_bytes(NP);
+  auto kern = p.parts > 1 ? gemv_mma_kernel<FMT, NP, true> : gemv_mma_kernel<FMT, NP, false>;
+  if constexpr (lds > 64 * 1024) {
+    static std::atomic<bool> raised[2] = {false, false};
+    const int which = p.parts > 1 ? 1 : 0;
+    if (!raised[which].load()) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      raised[which].store(true);
+    }
+  }
+  hipLaunchKernelGGL(kern, grid, dim3(512), lds, s, p);
+  return hipSuccess;
+}
+
+template <int FMT>
+hipError_t launch_gemv_mma(int np, const GemvParams& p, dim3 grid, hipStream_t s) {
+  if constexpr (FMT != FMT_AFF && FMT != FMT_AFF4) {
+    return hipErrorInvalidValue;
+  } else {
+    switch (np) {
+      case 1: return launch_gemv_mma_np<FMT, 1>(p, grid, s);
+      case 2: return launch_gemv_mma_np<FMT, 2>(p, grid, s);
+      case 4: return launch_gemv_mma_np<FMT, 4>(p, grid, s);
+      case 8: return launch_gemv_mma_np<FMT, 8>(p, grid, s);
+    }
+    return hipErrorInvalidValue;
+  }
+}
+
 // Runs a part list on the chunked GEMV kernel (or on the plain one when
 // `plain`), over all m-tiles of x.
 template <int FMT, int NW>
@@ -374,9 +429,10 @@ qg_status run_gemv(const char* op, const HostPart* parts, int nparts, const floa
     return launch_status(op);
   }
   const GemvPlan pl = plan_gemv<FMT>(m, k, NW);
-  const int ks = ks_chunks<FMT, NW>(pl, m, k);
+  const int mma = NW == 1 ? mma_pairs<FMT>(parts, nparts, m, k, gs) : 0;
+  const int ks = mma ? 0 : ks_chunks<FMT, NW>(pl, m, k);
   const GemvGrid gg = grid_gemv<FMT>(pl, parts, nparts);
-  const int rows_per_group = ks ? (int)(kWave / (pl.l / 8) * pl.r) : (int)gg.groups_rows;
+  const int rows_per_group = mma ? 16 : ks ? (int)(kWave / (pl.l / 8) * pl.r) : (int)gg.groups_rows;
   GemvParams p{};
   int64_t groups = 0;
   for (int pi = 0; pi < nparts; ++pi) {
@@ -398,6 +454,19 @@ qg_status run_gemv(const char* op, const HostPart* parts, int nparts, const floa
   p.k = (int)k;
   p.gs = gs;
   p.kt = pl.kt;
+  if (mma) {
+    // one workgroup per CU (the x tile fills most of the LDS), walking row groups
+    const int64_t grid = groups < device_cus() ? groups : device_cus();
+    for (int64_t m0 = 0; m0 < m; m0 += kMmaMaxM) {
+      GemvParams q = p;
+      q.x = x + m0 * k;
+      for (int pi = 0; pi < nparts; ++pi) q.part[pi].y[0] = p.part[pi].y[0] + m0 * p.part[pi].ldy;
+      q.m_rows = (int)(m - m0 < kMmaMaxM ? m - m0 : kMmaMaxM);
+      const hipError_t e = launch_gemv_mma<FMT>(mma, q, dim3((unsigned)grid), s);
+      if (e != hipSuccess) return launch_error(op, "launch setup failed", e);
+    }
+    return launch_status(op);
+  }
   if (ks) {
     p.x = x;
     p.m_rows = 1;

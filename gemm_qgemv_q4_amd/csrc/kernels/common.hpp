@@ -18,7 +18,9 @@ constexpr int kMaxParts = 8;
 typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4a4 __attribute__((ext_vector_type(4), aligned(4)));  // dword-aligned: one global_load_dwordx4
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 // Hide a value from the optimiser so that a following byte extract maps to
 // v_cvt_f32_ubyteN instead of being re-folded into one bfe per nibble.
