@@ -280,25 +280,45 @@ hipError_t launch_gemv_mt(const GemvPlan& pl, const GemvParams& p, dim3 g, dim3 
 
 // K-sliced kernel for M = 1 (same bits as the chunked kernel with the same
 // L and R); J = chunks per lane and row.
-template <int FMT, int L, int R, int J>
+template <int FMT, int L, int R, int J, int WV>
 hipError_t launch_gemv_ks_j(const GemvParams& p, dim3 grid, size_t lds, hipStream_t s) {
   if (p.parts > 1) {
     if constexpr (FMT == FMT_Q4K || FMT == FMT_AFF) {
-      hipLaunchKernelGGL((gemv_ks_kernel<FMT, 1, L, R, J, true>), grid, dim3(512), lds, s, p);
+      hipLaunchKernelGGL((gemv_ks_kernel<FMT, 1, L, R, J, WV, true>), grid, dim3(64 * WV), lds, s, p);
       return hipSuccess;
     }
     return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL((gemv_ks_kernel<FMT, 1, L, R, J, false>), grid, dim3(512), lds, s, p);
+  hipLaunchKernelGGL((gemv_ks_kernel<FMT, 1, L, R, J, WV, false>), grid, dim3(64 * WV), lds, s, p);
   return hipSuccess;
 }
 
 template <int FMT>
-size_t ks_lds(int l, int r, int j) {
+size_t ks_lds(int l, int r, int j, int wv) {
   const size_t ne4 = FmtTraits<FMT>::CH / 4;
-  const size_t u = (size_t)(l / 8) * j;
-  const size_t rows = (size_t)(kWave / (l / 8)) * r;
-  return 8 * ne4 * (u + 1) * 16 + 8 * 2 * u * 4 + 2 * 8 * rows * 4;
+  const size_t u = (size_t)(l / wv) * j;
+  const size_t rows = (size_t)(kWave / (l / wv)) * r;
+  return wv * ne4 * (u + 1) * 16 + wv * 2 * u * 4 + 2 * wv * rows * 4;
+}
+
+// Waves per workgroup of the K-sliced kernel.  The affine formats use 8.  For
+// the 64-weight chunks of Q4_0/Q4_K, 4 waves of 8 virtual lanes (row groups of
+// 8 rows, twice the workgroups) measured faster where every virtual lane has a
+// chunk (K >= 2048): 6.6 vs 7.0 us for the multi-part q|k|v product, 11.5 vs
+// 12.3 us for its three separate calls, a tie at 4096 x 4096; at K = 1024
+// 8 waves are faster (2.35 vs 2.48 us).  Tuning override QG_GEMV_KS_WAVES=4|8
+// for the Q4 formats (same results either way).
+template <int FMT>
+int ks_waves(int64_t k) {
+  if constexpr (FMT != FMT_Q40 && FMT != FMT_Q4K) {
+    return 8;
+  } else {
+    if (const char* env = getenv("QG_GEMV_KS_WAVES")) {
+      const int w = atoi(env);
+      if (w == 4 || w == 8) return w;
+    }
+    return k / 64 >= 32 ? 4 : 8;
+  }
 }
 
 // Chunks per lane the K-sliced kernel takes for this call (0: not eligible):
@@ -319,14 +339,14 @@ int ks_chunks(const GemvPlan& pl, int64_t m, int64_t k) {
   return j >= 1 && j <= 4 ? (int)j : 0;
 }
 
-template <int FMT, int L, int R>
+template <int FMT, int L, int R, int WV>
 hipError_t launch_gemv_ks_lr(int j, const GemvParams& p, dim3 grid, hipStream_t s) {
-  const size_t lds = ks_lds<FMT>(L, R, j);
+  const size_t lds = ks_lds<FMT>(L, R, j, WV);
   switch (j) {
-    case 1: return launch_gemv_ks_j<FMT, L, R, 1>(p, grid, lds, s);
-    case 2: return launch_gemv_ks_j<FMT, L, R, 2>(p, grid, lds, s);
-    case 3: return launch_gemv_ks_j<FMT, L, R, 3>(p, grid, lds, s);
-    case 4: return launch_gemv_ks_j<FMT, L, R, 4>(p, grid, lds, s);
+    case 1: return launch_gemv_ks_j<FMT, L, R, 1, WV>(p, grid, lds, s);
+    case 2: return launch_gemv_ks_j<FMT, L, R, 2, WV>(p, grid, lds, s);
+    case 3: return launch_gemv_ks_j<FMT, L, R, 3, WV>(p, grid, lds, s);
+    case 4: return launch_gemv_ks_j<FMT, L, R, 4, WV>(p, grid, lds, s);
   }
   return hipErrorInvalidValue;
 }
@@ -336,9 +356,11 @@ hipError_t launch_gemv_ks(const GemvPlan& pl, int j, const GemvParams& p, dim3 g
   if constexpr (NW != 1) {
     return hipErrorInvalidValue;
   } else if constexpr (FMT == FMT_Q40 || FMT == FMT_Q4K) {
-    return pl.l == 32 && pl.r == 1 ? launch_gemv_ks_lr<FMT, 32, 1>(j, p, grid, s) : hipErrorInvalidValue;
+    if (!(pl.l == 32 && pl.r == 1)) return hipErrorInvalidValue;
+    return ks_waves<FMT>(p.k) == 4 ? launch_gemv_ks_lr<FMT, 32, 1, 4>(j, p, grid, s)
+                                   : launch_gemv_ks_lr<FMT, 32, 1, 8>(j, p, grid, s);
   } else {
-    return pl.l == 64 && pl.r == 2 ? launch_gemv_ks_lr<FMT, 64, 2>(j, p, grid, s) : hipErrorInvalidValue;
+    return pl.l == 64 && pl.r == 2 ? launch_gemv_ks_lr<FMT, 64, 2, 8>(j, p, grid, s) : hipErrorInvalidValue;
   }
 }
 
@@ -432,7 +454,8 @@ qg_status run_gemv(const char* op, const HostPart* parts, int nparts, const floa
   const int mma = NW == 1 ? mma_pairs<FMT>(parts, nparts, m, k, gs) : 0;
   const int ks = mma ? 0 : ks_chunks<FMT, NW>(pl, m, k);
   const GemvGrid gg = grid_gemv<FMT>(pl, parts, nparts);
-  const int rows_per_group = mma ? 16 : ks ? (int)(kWave / (pl.l / 8) * pl.r) : (int)gg.groups_rows;
+  const int ks_wv = ks ? ks_waves<FMT>(k) : 0;
+  const int rows_per_group = mma ? 16 : ks ? (int)(kWave / (pl.l / ks_wv) * pl.r) : (int)gg.groups_rows;
   GemvParams p{};
   int64_t groups = 0;
   for (int pi = 0; pi < nparts; ++pi) {
@@ -470,13 +493,14 @@ qg_status run_gemv(const char* op, const HostPart* parts, int nparts, const floa
   if (ks) {
     p.x = x;
     p.m_rows = 1;
-    // Up to two workgroups per CU (16 waves; the kernel takes at most 101
-    // VGPRs and 38 KB of LDS), walking row groups beyond that.  Measured on
-    // Q4_K K = 4096 at N = 6144 ... 28672 rows: 3-12% faster than one per CU.
-    // Tuning override QG_GEMV_KS=B (B workgroups per CU; 0 keeps the chunked kernel).
+    // Up to 16 waves per CU (two 8-wave or four 4-wave workgroups; they are
+    // resident together where the kernel stays within 128 VGPRs), walking row
+    // groups beyond that.  Measured on Q4_K K = 4096 at N = 6144 ... 28672
+    // rows: 3-12% faster than 8 waves per CU.  Tuning override QG_GEMV_KS=B
+    // (B times 8 waves per CU; 0 keeps the chunked kernel).
     int64_t bpc = 2;
     if (const char* env = getenv("QG_GEMV_KS")) bpc = atoi(env) > 0 ? atoi(env) : 2;
-    const int64_t cap = bpc * device_cus();
+    const int64_t cap = bpc * (8 / ks_wv) * device_cus();
     const int64_t grid = groups < cap ? groups : cap;
     const hipError_t e = launch_gemv_ks<FMT, NW>(pl, ks, p, dim3((unsigned)grid), s);
     if (e != hipSuccess) return launch_error(op, "launch setup failed", e);

@@ -587,31 +587,31 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams p) {
 // lane) at MT = 1, so both kernels give the same bits; what changes is which
 // wave does which of them.
 //   * The L lanes of a row in gemv_kernel become "virtual lanes" spread over
-//     the 8 waves of a workgroup: wave w holds virtual lanes LW*w .. LW*w+LW-1
-//     (LW = L/8) of 64/LW row sets of R rows each (hardware lane = LW * set +
-//     c, virtual lane LW*w + c), so it needs x only at its own chunks
-//     LW*w + c + L*j, j < J: one eighth of K.
+//     the WV waves of a workgroup (4 or 8): wave w holds virtual lanes
+//     LW*w .. LW*w+LW-1 (LW = L/WV) of 64/LW row sets of R rows each (hardware
+//     lane = LW * set + c, virtual lane LW*w + c), so it needs x only at its
+//     own chunks LW*w + c + L*j: one WV-th of K.
 //   * Each wave stages that slice of x in its own LDS region and then
 //     multiplies: no workgroup barrier stands between the staging and the
 //     arithmetic, and all J chunks of a lane are loaded before the first one
 //     is used.
 //   * The butterfly over the L virtual lanes keeps its pairing: its first
-//     log2(LW) levels run inside the wave (DPP), the three upper levels
-//     combine the 8 waves' partial sums through LDS as (w0 + w1, w2 + w3,
-//     ...), then pairs of pairs, then the two halves.
+//     log2(LW) levels run inside the wave (DPP), the upper log2(WV) levels
+//     combine the waves' partial sums through LDS as (w0 + w1, w2 + w3, ...),
+//     then pairs of pairs, and so on.
 // A workgroup walks row groups of 64/LW*R rows; x stays in LDS between them.
-template <int FMT, int NW, int L, int R, int J, bool MULTI>
+template <int FMT, int NW, int L, int R, int J, int WV, bool MULTI>
 __global__ void __launch_bounds__(512) gemv_ks_kernel(GemvParams p) {
-  static_assert(L == 32 || L == 64, "8 waves of 4 or 8 virtual lanes");
+  static_assert((L == 32 || L == 64) && (WV == 4 || WV == 8) && L / WV >= 4, "4 or 8 waves of 4 or 8 virtual lanes");
   constexpr int CH = FmtTraits<FMT>::CH;
   constexpr int NE4 = CH / 4;
-  constexpr int WV = 8;
   constexpr int LW = L / WV;             // lanes of a row inside one wave
   constexpr int RS = kWave / LW;         // row sets per wave
   constexpr int ROWS = RS * R;           // rows per group
   constexpr int U = LW * J;              // chunks of x held by one wave
   constexpr int XP = U + 1;              // LDS pitch in float4s (odd: spreads banks on the staging writes)
-  static_assert(LW * NE4 == kWave, "one float4 of x per lane and chunk slice");
+  constexpr int XS = LW * NE4 / kWave;   // float4s of x per lane and chunk slice
+  static_assert(XS >= 1 && XS * kWave == LW * NE4, "whole float4s of x per lane");
   using Chunk = typename ChunkOf<FMT>::T;
 
   extern __shared__ f32x4 smem[];
@@ -677,10 +677,10 @@ __global__ void __launch_bounds__(512) gemv_ks_kernel(GemvParams p) {
   {
     const bool x_vec = (reinterpret_cast<uintptr_t>(p.x) & 15u) == 0;
     const int n4 = p.k >> 2;
-    f32x4 xv[J];
+    f32x4 xv[J * XS];
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int f = NE4 * (LW * wv + L * j) + lane;
+    for (int j = 0; j < J * XS; ++j) {
+      const int f = NE4 * (LW * wv + L * (j / XS)) + kWave * (j % XS) + lane;
       xv[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       if (f < n4) {
         if (x_vec) xv[j] = *reinterpret_cast<const f32x4*>(p.x + 4 * f);
@@ -689,10 +689,11 @@ __global__ void __launch_bounds__(512) gemv_ks_kernel(GemvParams p) {
     }
     fetch_all(cv);
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int f = NE4 * (LW * wv + L * j) + lane;
-      const int e4 = lane % NE4;
-      const int u = LW * j + lane / NE4;
+    for (int j = 0; j < J * XS; ++j) {
+      const int f = NE4 * (LW * wv + L * (j / XS)) + kWave * (j % XS) + lane;
+      const int li = kWave * (j % XS) + lane;  // float4 within the slice
+      const int e4 = li % NE4;
+      const int u = LW * (j / XS) + li / NE4;
       if (f < n4) xs[e4 * XP + u] = xv[j];
       // sum of each 32-element half: 8 consecutive float4s on 8 consecutive lanes
       const float sm = group_sum(((xv[j].x + xv[j].y) + xv[j].z) + xv[j].w, 8);
@@ -742,9 +743,14 @@ __global__ void __launch_bounds__(512) gemv_ks_kernel(GemvParams p) {
       const float* a = rb + s * WV * ROWS + r;
       const float b0 = a[0 * ROWS] + a[1 * ROWS];
       const float b1 = a[2 * ROWS] + a[3 * ROWS];
-      const float b2 = a[4 * ROWS] + a[5 * ROWS];
-      const float b3 = a[6 * ROWS] + a[7 * ROWS];
-      const float t = (b0 + b1) + (b2 + b3);
+      float t;
+      if constexpr (WV == 8) {
+        const float b2 = a[4 * ROWS] + a[5 * ROWS];
+        const float b3 = a[6 * ROWS] + a[7 * ROWS];
+        t = (b0 + b1) + (b2 + b3);
+      } else {
+        t = b0 + b1;
+      }
       int pi = 0;
       if constexpr (MULTI) {
         for (int i = 1; i < p.parts; ++i)

@@ -126,3 +126,25 @@ def test_fused_qkv_ksplit_equals_chunked_and_split(lib):
     y = lib.qmm_affine_t(dx, dq, ds, db, gs)
     for got, ref in zip(a, lib.qkv_split_f32(y, 1, qs, ks, vs)):
         assert np.array_equal(bits(got), bits(host(ref)))
+
+
+@pytest.mark.parametrize("k", [1024, 4096])
+def test_q4_k_ksplit_waves_do_not_change_bits(lib, k):
+    """4 or 8 waves per workgroup (8 or 4 virtual lanes per wave) regroup the
+    same additions; the outputs agree bit for bit, multi-part included."""
+    ns = (96, 40, 17)
+    ws, x = synth.q4_k_multi_case(8900 + k, 1, ns, k)
+    dws, dx = [dev(w) for w in ws], dev(x)
+    out = {}
+    old = os.environ.get("QG_GEMV_KS_WAVES")
+    try:
+        for wv in ("4", "8"):
+            os.environ["QG_GEMV_KS_WAVES"] = wv
+            out[wv] = (host(lib.qgemv_q4_k_multi(dws, dx, list(ns), k)), host(lib.qgemv_q4_k(dws[0], dx, ns[0], k)))
+    finally:
+        if old is None:
+            os.environ.pop("QG_GEMV_KS_WAVES", None)
+        else:
+            os.environ["QG_GEMV_KS_WAVES"] = old
+    for a, b in zip(out["4"], out["8"]):
+        assert np.array_equal(bits(a), bits(b))
