@@ -280,25 +280,25 @@ hipError_t launch_gemv_mt(const GemvPlan& pl, const GemvParams& p, dim3 g, dim3 
 
 // K-sliced kernel for M = 1 (same bits as the chunked kernel with the same
 // L and R); J = chunks per lane and row.
-template <int FMT, int L, int R, int J, int WV>
+template <int FMT, int NW, int L, int R, int J, int WV>
 hipError_t launch_gemv_ks_j(const GemvParams& p, dim3 grid, size_t lds, hipStream_t s) {
   if (p.parts > 1) {
-    if constexpr (FMT == FMT_Q4K || FMT == FMT_AFF) {
-      hipLaunchKernelGGL((gemv_ks_kernel<FMT, 1, L, R, J, WV, true>), grid, dim3(64 * WV), lds, s, p);
+    if constexpr (NW == 1 && (FMT == FMT_Q4K || FMT == FMT_AFF)) {
+      hipLaunchKernelGGL((gemv_ks_kernel<FMT, NW, L, R, J, WV, true>), grid, dim3(64 * WV), lds, s, p);
       return hipSuccess;
     }
     return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL((gemv_ks_kernel<FMT, 1, L, R, J, WV, false>), grid, dim3(64 * WV), lds, s, p);
+  hipLaunchKernelGGL((gemv_ks_kernel<FMT, NW, L, R, J, WV, false>), grid, dim3(64 * WV), lds, s, p);
   return hipSuccess;
 }
 
 template <int FMT>
-size_t ks_lds(int l, int r, int j, int wv) {
+size_t ks_lds(int nw, int l, int r, int j, int wv) {
   const size_t ne4 = FmtTraits<FMT>::CH / 4;
   const size_t u = (size_t)(l / wv) * j;
   const size_t rows = (size_t)(kWave / (l / wv)) * r;
-  return wv * ne4 * (u + 1) * 16 + wv * 2 * u * 4 + 2 * wv * rows * 4;
+  return wv * ne4 * (u + 1) * 16 + wv * 2 * u * 4 + 2 * (size_t)nw * wv * rows * 4;
 }
 
 // Waves per workgroup of the K-sliced kernel.  The affine formats use 8.  For
@@ -322,45 +322,43 @@ int ks_waves(int64_t k) {
 }
 
 // Chunks per lane the K-sliced kernel takes for this call (0: not eligible):
-// one x row, one weight stream, x in LDS for the whole K, and the chunked
-// kernel's shape (L, R) = (32, 1) for the 64-weight chunks of Q4_0/Q4_K or
-// (64, 2) for the 32-code chunks of the affine formats (one float4 of x per
-// lane and chunk slice).
+// one x row, x in LDS for the whole K, and the chunked kernel's shape (L, R)
+// = (32, 1) for the 64-weight chunks of Q4_0/Q4_K (one or two weight
+// streams) or (64, 2) for the 32-code chunks of the affine formats.
 template <int FMT, int NW>
 int ks_chunks(const GemvPlan& pl, int64_t m, int64_t k) {
   // tuning override (same results either way): QG_GEMV_KS=0 keeps the chunked kernel
   if (const char* env = getenv("QG_GEMV_KS"))
     if (env[0] == '0') return 0;
-  // the dual product (two streams) keeps the chunked kernel: it measured faster there
-  if (NW != 1 || m != 1 || pl.mt != 1 || !pl.persistent) return 0;
+  if (m != 1 || pl.mt != 1 || !pl.persistent) return 0;
   constexpr bool Q4 = FMT == FMT_Q40 || FMT == FMT_Q4K;
   if (Q4 ? !(pl.l == 32 && pl.r == 1) : !(pl.l == 64 && pl.r == 2)) return 0;
   const int64_t j = cdiv(k / FmtTraits<FMT>::CH, pl.l);
   return j >= 1 && j <= 4 ? (int)j : 0;
 }
 
-template <int FMT, int L, int R, int WV>
+template <int FMT, int NW, int L, int R, int WV>
 hipError_t launch_gemv_ks_lr(int j, const GemvParams& p, dim3 grid, hipStream_t s) {
-  const size_t lds = ks_lds<FMT>(L, R, j, WV);
+  const size_t lds = ks_lds<FMT>(NW, L, R, j, WV);
   switch (j) {
-    case 1: return launch_gemv_ks_j<FMT, L, R, 1, WV>(p, grid, lds, s);
-    case 2: return launch_gemv_ks_j<FMT, L, R, 2, WV>(p, grid, lds, s);
-    case 3: return launch_gemv_ks_j<FMT, L, R, 3, WV>(p, grid, lds, s);
-    case 4: return launch_gemv_ks_j<FMT, L, R, 4, WV>(p, grid, lds, s);
+    case 1: return launch_gemv_ks_j<FMT, NW, L, R, 1, WV>(p, grid, lds, s);
+    case 2: return launch_gemv_ks_j<FMT, NW, L, R, 2, WV>(p, grid, lds, s);
+    case 3: return launch_gemv_ks_j<FMT, NW, L, R, 3, WV>(p, grid, lds, s);
+    case 4: return launch_gemv_ks_j<FMT, NW, L, R, 4, WV>(p, grid, lds, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <int FMT, int NW>
 hipError_t launch_gemv_ks(const GemvPlan& pl, int j, const GemvParams& p, dim3 grid, hipStream_t s) {
-  if constexpr (NW != 1) {
-    return hipErrorInvalidValue;
-  } else if constexpr (FMT == FMT_Q40 || FMT == FMT_Q4K) {
+  if constexpr (FMT == FMT_Q40 || FMT == FMT_Q4K) {
     if (!(pl.l == 32 && pl.r == 1)) return hipErrorInvalidValue;
-    return ks_waves<FMT>(p.k) == 4 ? launch_gemv_ks_lr<FMT, 32, 1, 4>(j, p, grid, s)
-                                   : launch_gemv_ks_lr<FMT, 32, 1, 8>(j, p, grid, s);
+    return ks_waves<FMT>(p.k) == 4 ? launch_gemv_ks_lr<FMT, NW, 32, 1, 4>(j, p, grid, s)
+                                   : launch_gemv_ks_lr<FMT, NW, 32, 1, 8>(j, p, grid, s);
+  } else if constexpr (NW == 1) {
+    return pl.l == 64 && pl.r == 2 ? launch_gemv_ks_lr<FMT, NW, 64, 2, 8>(j, p, grid, s) : hipErrorInvalidValue;
   } else {
-    return pl.l == 64 && pl.r == 2 ? launch_gemv_ks_lr<FMT, 64, 2, 8>(j, p, grid, s) : hipErrorInvalidValue;
+    return hipErrorInvalidValue;
   }
 }
 

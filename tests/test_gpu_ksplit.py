@@ -56,9 +56,9 @@ def test_q4_0_ksplit_equals_chunked(lib, n, k):
 
 
 @pytest.mark.parametrize("n,k", [(50, 4096), (19, 2048 + 64)])
-def test_dual_equals_ksplit_single_calls(lib, n, k):
-    """The dual product keeps the chunked kernel; its second output must still
-    equal the single call, which takes the K-sliced kernel."""
+def test_dual_ksplit_equals_chunked_and_single_calls(lib, n, k):
+    """The dual product on the K-sliced kernel equals the chunked kernel and
+    two single calls, bit for bit."""
     wa, wb, x = synth.dual_q4_0_case(8300 + n, 1, n, k)
     dwa, dwb, dx = dev(wa), dev(wb), dev(x)
     (a0, a1), (b0, b1) = both(lambda: tuple(host(t) for t in lib.qgemv_dual_q4_0(dwa, dwb, dx, n, k)))
