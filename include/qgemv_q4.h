@@ -37,6 +37,11 @@
  *    equalities stated below (dual = two singles, multi-part = one call per
  *    part, packed = unpacked, fused split = product then split) hold bit for
  *    bit on both paths.
+ *  - Few rows on the matrix cores: for 2 <= M below that threshold, the
+ *    affine formats with group_size >= 64, K a multiple of 512 with K/512 in
+ *    {1, 2, 4, 8} and codes aligned (16 bytes for u8, 8 for packed) run on
+ *    the matrix cores in launches of up to 8 rows of x, with x split the
+ *    same way and no scratch.  The same tolerance and equalities hold.
  */
 #ifndef QGEMV_Q4_H
 #define QGEMV_Q4_H
