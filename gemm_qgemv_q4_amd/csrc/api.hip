@@ -278,27 +278,27 @@ hipError_t launch_gemv_mt(const GemvPlan& pl, const GemvParams& p, dim3 g, dim3 
   return hipErrorInvalidValue;
 }
 
-// K-sliced kernel for M = 1 (same bits as the chunked kernel with the same
-// L and R); J = chunks per lane and row.
-template <int FMT, int NW, int L, int R, int J, int WV>
+// K-sliced kernel for tiles of MT rows of x (same bits as the chunked kernel
+// with the same MT, L and R); J = chunks per lane and row.
+template <int FMT, int MT, int NW, int L, int R, int J, int WV>
 hipError_t launch_gemv_ks_j(const GemvParams& p, dim3 grid, size_t lds, hipStream_t s) {
   if (p.parts > 1) {
     if constexpr (NW == 1 && (FMT == FMT_Q4K || FMT == FMT_AFF)) {
-      hipLaunchKernelGGL((gemv_ks_kernel<FMT, NW, L, R, J, WV, true>), grid, dim3(64 * WV), lds, s, p);
+      hipLaunchKernelGGL((gemv_ks_kernel<FMT, MT, NW, L, R, J, WV, true>), grid, dim3(64 * WV), lds, s, p);
       return hipSuccess;
     }
     return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL((gemv_ks_kernel<FMT, NW, L, R, J, WV, false>), grid, dim3(64 * WV), lds, s, p);
+  hipLaunchKernelGGL((gemv_ks_kernel<FMT, MT, NW, L, R, J, WV, false>), grid, dim3(64 * WV), lds, s, p);
   return hipSuccess;
 }
 
 template <int FMT>
-size_t ks_lds(int nw, int l, int r, int j, int wv) {
+size_t ks_lds(int mt, int nw, int l, int r, int j, int wv) {
   const size_t ne4 = FmtTraits<FMT>::CH / 4;
   const size_t u = (size_t)(l / wv) * j;
   const size_t rows = (size_t)(kWave / (l / wv)) * r;
-  return wv * ne4 * (u + 1) * 16 + wv * 2 * u * 4 + 2 * (size_t)nw * wv * rows * 4;
+  return (size_t)mt * (wv * ne4 * (u + 1) * 16 + wv * 2 * u * 4 + 2 * (size_t)nw * wv * rows * 4);
 }
 
 // Waves per workgroup of the K-sliced kernel.  The affine formats use 8.  For
@@ -322,29 +322,35 @@ int ks_waves(int64_t k) {
 }
 
 // Chunks per lane the K-sliced kernel takes for this call (0: not eligible):
-// one x row, x in LDS for the whole K, and the chunked kernel's shape (L, R)
-// = (32, 1) for the 64-weight chunks of Q4_0/Q4_K (one or two weight
-// streams) or (64, 2) for the 32-code chunks of the affine formats.
+// x in LDS for the whole K and the chunked kernel's shape (L, R) = (32, 1)
+// for the 64-weight chunks of Q4_0/Q4_K (one or two weight streams; one x row,
+// or tiles of 2 or 4 rows where 4 waves are used) or (64, 2) for the 32-code
+// chunks of the affine formats (one x row).
 template <int FMT, int NW>
 int ks_chunks(const GemvPlan& pl, int64_t m, int64_t k) {
   // tuning override (same results either way): QG_GEMV_KS=0 keeps the chunked kernel
   if (const char* env = getenv("QG_GEMV_KS"))
     if (env[0] == '0') return 0;
-  if (m != 1 || pl.mt != 1 || !pl.persistent) return 0;
   constexpr bool Q4 = FMT == FMT_Q40 || FMT == FMT_Q4K;
+  if (!pl.persistent) return 0;
+  // tiles of 2 or 4 rows of x: the dual Q4_0 product at M = 4 takes 11.0 us
+  // here against 14.1 us on the chunked kernel; at 8 rows (22.1 vs 18.5 us)
+  // the chunked kernel stays
+  if (pl.mt > 1 && !(Q4 && pl.mt <= 4 && ks_waves<FMT>(k) == 4)) return 0;
   if (Q4 ? !(pl.l == 32 && pl.r == 1) : !(pl.l == 64 && pl.r == 2)) return 0;
   const int64_t j = cdiv(k / FmtTraits<FMT>::CH, pl.l);
+  (void)m;
   return j >= 1 && j <= 4 ? (int)j : 0;
 }
 
-template <int FMT, int NW, int L, int R, int WV>
+template <int FMT, int MT, int NW, int L, int R, int WV>
 hipError_t launch_gemv_ks_lr(int j, const GemvParams& p, dim3 grid, hipStream_t s) {
-  const size_t lds = ks_lds<FMT>(NW, L, R, j, WV);
+  const size_t lds = ks_lds<FMT>(MT, NW, L, R, j, WV);
   switch (j) {
-    case 1: return launch_gemv_ks_j<FMT, NW, L, R, 1, WV>(p, grid, lds, s);
-    case 2: return launch_gemv_ks_j<FMT, NW, L, R, 2, WV>(p, grid, lds, s);
-    case 3: return launch_gemv_ks_j<FMT, NW, L, R, 3, WV>(p, grid, lds, s);
-    case 4: return launch_gemv_ks_j<FMT, NW, L, R, 4, WV>(p, grid, lds, s);
+    case 1: return launch_gemv_ks_j<FMT, MT, NW, L, R, 1, WV>(p, grid, lds, s);
+    case 2: return launch_gemv_ks_j<FMT, MT, NW, L, R, 2, WV>(p, grid, lds, s);
+    case 3: return launch_gemv_ks_j<FMT, MT, NW, L, R, 3, WV>(p, grid, lds, s);
+    case 4: return launch_gemv_ks_j<FMT, MT, NW, L, R, 4, WV>(p, grid, lds, s);
   }
   return hipErrorInvalidValue;
 }
@@ -353,10 +359,17 @@ template <int FMT, int NW>
 hipError_t launch_gemv_ks(const GemvPlan& pl, int j, const GemvParams& p, dim3 grid, hipStream_t s) {
   if constexpr (FMT == FMT_Q40 || FMT == FMT_Q4K) {
     if (!(pl.l == 32 && pl.r == 1)) return hipErrorInvalidValue;
-    return ks_waves<FMT>(p.k) == 4 ? launch_gemv_ks_lr<FMT, NW, 32, 1, 4>(j, p, grid, s)
-                                   : launch_gemv_ks_lr<FMT, NW, 32, 1, 8>(j, p, grid, s);
+    const bool four = ks_waves<FMT>(p.k) == 4;
+    switch (pl.mt) {
+      case 1: return four ? launch_gemv_ks_lr<FMT, 1, NW, 32, 1, 4>(j, p, grid, s)
+                          : launch_gemv_ks_lr<FMT, 1, NW, 32, 1, 8>(j, p, grid, s);
+      case 2: return four ? launch_gemv_ks_lr<FMT, 2, NW, 32, 1, 4>(j, p, grid, s) : hipErrorInvalidValue;
+      case 4: return four ? launch_gemv_ks_lr<FMT, 4, NW, 32, 1, 4>(j, p, grid, s) : hipErrorInvalidValue;
+    }
+    return hipErrorInvalidValue;
   } else if constexpr (NW == 1) {
-    return pl.l == 64 && pl.r == 2 ? launch_gemv_ks_lr<FMT, NW, 64, 2, 8>(j, p, grid, s) : hipErrorInvalidValue;
+    return pl.l == 64 && pl.r == 2 && pl.mt == 1 ? launch_gemv_ks_lr<FMT, 1, NW, 64, 2, 8>(j, p, grid, s)
+                                                 : hipErrorInvalidValue;
   } else {
     return hipErrorInvalidValue;
   }
@@ -489,8 +502,6 @@ qg_status run_gemv(const char* op, const HostPart* parts, int nparts, const floa
     return launch_status(op);
   }
   if (ks) {
-    p.x = x;
-    p.m_rows = 1;
     // Up to 16 waves per CU (two 8-wave or four 4-wave workgroups; they are
     // resident together where the kernel stays within 128 VGPRs), walking row
     // groups beyond that.  Measured on Q4_K K = 4096 at N = 6144 ... 28672
@@ -500,8 +511,15 @@ qg_status run_gemv(const char* op, const HostPart* parts, int nparts, const floa
     if (const char* env = getenv("QG_GEMV_KS")) bpc = atoi(env) > 0 ? atoi(env) : 2;
     const int64_t cap = bpc * (8 / ks_wv) * device_cus();
     const int64_t grid = groups < cap ? groups : cap;
-    const hipError_t e = launch_gemv_ks<FMT, NW>(pl, ks, p, dim3((unsigned)grid), s);
-    if (e != hipSuccess) return launch_error(op, "launch setup failed", e);
+    for (int64_t m0 = 0; m0 < m; m0 += pl.mt) {
+      GemvParams q = p;
+      q.x = x + m0 * k;
+      for (int pi = 0; pi < nparts; ++pi)
+        for (int st = 0; st < 2; ++st) q.part[pi].y[st] = p.part[pi].y[st] + m0 * p.part[pi].ldy;
+      q.m_rows = (int)(m - m0 < pl.mt ? m - m0 : pl.mt);
+      const hipError_t e = launch_gemv_ks<FMT, NW>(pl, ks, q, dim3((unsigned)grid), s);
+      if (e != hipSuccess) return launch_error(op, "launch setup failed", e);
+    }
     return launch_status(op);
   }
   const int64_t grid = gg.grid;

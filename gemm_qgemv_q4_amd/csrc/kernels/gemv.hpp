@@ -582,25 +582,25 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// K-sliced GEMV for one x row (M = 1).  It computes the same additions in the
-// same order as gemv_kernel with the same L (lanes per row) and R (rows per
-// lane) at MT = 1, so both kernels give the same bits; what changes is which
+// K-sliced GEMV for a tile of MT rows of x.  It computes the same additions
+// in the same order as gemv_kernel with the same MT, L (lanes per row) and R
+// (rows per lane), so both kernels give the same bits; what changes is which
 // wave does which of them.
 //   * The L lanes of a row in gemv_kernel become "virtual lanes" spread over
 //     the WV waves of a workgroup (4 or 8): wave w holds virtual lanes
 //     LW*w .. LW*w+LW-1 (LW = L/WV) of 64/LW row sets of R rows each (hardware
 //     lane = LW * set + c, virtual lane LW*w + c), so it needs x only at its
 //     own chunks LW*w + c + L*j: one WV-th of K.
-//   * Each wave stages that slice of x in its own LDS region and then
-//     multiplies: no workgroup barrier stands between the staging and the
-//     arithmetic, and all J chunks of a lane are loaded before the first one
-//     is used.
+//   * Each wave stages that slice of x (for each of the MT rows) in its own
+//     LDS region and then multiplies: no workgroup barrier stands between the
+//     staging and the arithmetic, and all J chunks of a lane are loaded before
+//     the first one is used.
 //   * The butterfly over the L virtual lanes keeps its pairing: its first
 //     log2(LW) levels run inside the wave (DPP), the upper log2(WV) levels
 //     combine the waves' partial sums through LDS as (w0 + w1, w2 + w3, ...),
 //     then pairs of pairs, and so on.
 // A workgroup walks row groups of 64/LW*R rows; x stays in LDS between them.
-template <int FMT, int NW, int L, int R, int J, int WV, bool MULTI>
+template <int FMT, int MT, int NW, int L, int R, int J, int WV, bool MULTI>
 __global__ void __launch_bounds__(512) gemv_ks_kernel(GemvParams p) {
   static_assert((L == 32 || L == 64) && (WV == 4 || WV == 8) && L / WV >= 4, "4 or 8 waves of 4 or 8 virtual lanes");
   constexpr int CH = FmtTraits<FMT>::CH;
@@ -621,9 +621,9 @@ __global__ void __launch_bounds__(512) gemv_ks_kernel(GemvParams p) {
   const int c = lane % LW;
   const int vl = LW * wv + c;
   const int n_chunks = p.k / CH;
-  f32x4* xs = smem + wv * (NE4 * XP);                                           // [e4][u] of this wave
-  float* xsum = reinterpret_cast<float*>(smem + WV * NE4 * XP) + wv * (2 * U);  // [u][2]
-  float* red = reinterpret_cast<float*>(smem + WV * NE4 * XP) + WV * 2 * U;     // [2][NW][WV][ROWS]
+  f32x4* xs = smem + wv * (MT * NE4 * XP);                                                // [m][e4][u] of this wave
+  float* xsum = reinterpret_cast<float*>(smem + WV * MT * NE4 * XP) + wv * (MT * 2 * U);  // [m][u][2]
+  float* red = reinterpret_cast<float*>(smem + WV * MT * NE4 * XP) + WV * MT * 2 * U;     // [2][NW][WV][ROWS][MT]
 
   // Weights and rows of group g for this lane (rows are clamped for the
   // loads; rows past the part's end are not stored).
@@ -672,33 +672,39 @@ __global__ void __launch_bounds__(512) gemv_ks_kernel(GemvParams p) {
   View cv;
   view_of(g, cv);
 
-  // x of this wave's chunks: float4 NE4 * (LW*w + L*j) + lane covers chunks
-  // LW*w + L*j .. +LW-1.  The loads go out before the first weights.
+  // x of this wave's chunks, for each of the MT rows of x: float4
+  // NE4 * (LW*w + L*j) + lane covers chunks LW*w + L*j .. +LW-1.  The loads go
+  // out before the first weights; rows past m_rows are zero.
   {
     const bool x_vec = (reinterpret_cast<uintptr_t>(p.x) & 15u) == 0;
     const int n4 = p.k >> 2;
-    f32x4 xv[J * XS];
+    f32x4 xv[MT][J * XS];
 #pragma unroll
-    for (int j = 0; j < J * XS; ++j) {
-      const int f = NE4 * (LW * wv + L * (j / XS)) + kWave * (j % XS) + lane;
-      xv[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      if (f < n4) {
-        if (x_vec) xv[j] = *reinterpret_cast<const f32x4*>(p.x + 4 * f);
-        else xv[j] = f32x4{p.x[4 * f], p.x[4 * f + 1], p.x[4 * f + 2], p.x[4 * f + 3]};
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int j = 0; j < J * XS; ++j) {
+        const int f = NE4 * (LW * wv + L * (j / XS)) + kWave * (j % XS) + lane;
+        const float* xr = p.x + (size_t)m * p.k;
+        xv[m][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if ((MT == 1 || m < p.m_rows) && f < n4) {
+          if (x_vec) xv[m][j] = *reinterpret_cast<const f32x4*>(xr + 4 * f);
+          else xv[m][j] = f32x4{xr[4 * f], xr[4 * f + 1], xr[4 * f + 2], xr[4 * f + 3]};
+        }
       }
-    }
     fetch_all(cv);
 #pragma unroll
-    for (int j = 0; j < J * XS; ++j) {
-      const int f = NE4 * (LW * wv + L * (j / XS)) + kWave * (j % XS) + lane;
-      const int li = kWave * (j % XS) + lane;  // float4 within the slice
-      const int e4 = li % NE4;
-      const int u = LW * (j / XS) + li / NE4;
-      if (f < n4) xs[e4 * XP + u] = xv[j];
-      // sum of each 32-element half: 8 consecutive float4s on 8 consecutive lanes
-      const float sm = group_sum(((xv[j].x + xv[j].y) + xv[j].z) + xv[j].w, 8);
-      if (f < n4 && (e4 & 7) == 0) xsum[u * 2 + (e4 >> 3)] = sm;
-    }
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int j = 0; j < J * XS; ++j) {
+        const int f = NE4 * (LW * wv + L * (j / XS)) + kWave * (j % XS) + lane;
+        const int li = kWave * (j % XS) + lane;  // float4 within the slice
+        const int e4 = li % NE4;
+        const int u = LW * (j / XS) + li / NE4;
+        if (f < n4) xs[(m * NE4 + e4) * XP + u] = xv[m][j];
+        // sum of each 32-element half: 8 consecutive float4s on 8 consecutive lanes
+        const float sm = group_sum(((xv[m][j].x + xv[m][j].y) + xv[m][j].z) + xv[m][j].w, 8);
+        if (f < n4 && (e4 & 7) == 0) xsum[(m * U + u) * 2 + (e4 >> 3)] = sm;
+      }
     // LDS operations of one wave complete in order; this only keeps the
     // compiler from moving the reads above the writes.
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -709,27 +715,31 @@ __global__ void __launch_bounds__(512) gemv_ks_kernel(GemvParams p) {
   // One row group: multiply the loaded chunks, issue the next group's loads,
   // then finish the butterfly across waves and store.
   auto group = [&](int it) {
-    float acc[NW][R][1];
+    float acc[NW][R][MT];
 #pragma unroll
     for (int s = 0; s < NW; ++s)
 #pragma unroll
-      for (int r = 0; r < R; ++r) acc[s][r][0] = 0.0f;
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[s][r][m] = 0.0f;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       const int tg = vl + L * j;
-      if (tg < n_chunks) compute_chunk<FMT, 1, NW, R>(ch[j], xs, xsum, XP, U, LW * j + c, tg, acc);
+      if (tg < n_chunks) compute_chunk<FMT, MT, NW, R>(ch[j], xs, xsum, XP, U, LW * j + c, tg, acc);
     }
-    float* rb = red + (it & 1) * (NW * WV * ROWS);
+    float* rb = red + (it & 1) * (NW * WV * ROWS * MT);
 #pragma unroll
     for (int s = 0; s < NW; ++s)
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        float v = acc[s][r][0];
-        v += dpp_mov<0xB1>(v);                      // quad_perm [1,0,3,2]
-        v += dpp_mov<0x4E>(v);                      // quad_perm [2,3,0,1]
-        if constexpr (LW == 8) v += dpp_mov<0x141>(v);  // row_half_mirror
-        if (c == 0) rb[(s * WV + wv) * ROWS + rset + RS * r] = v;
-      }
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          float v = acc[s][r][m];
+          v += dpp_mov<0xB1>(v);                      // quad_perm [1,0,3,2]
+          v += dpp_mov<0x4E>(v);                      // quad_perm [2,3,0,1]
+          if constexpr (LW == 8) v += dpp_mov<0x141>(v);  // row_half_mirror
+          if (c == 0) rb[((s * WV + wv) * ROWS + rset + RS * r) * MT + m] = v;
+        }
     const int g_done = g;
     g += (int)gridDim.x;
     if (g < p.n_groups) {
@@ -737,16 +747,18 @@ __global__ void __launch_bounds__(512) gemv_ks_kernel(GemvParams p) {
       fetch_all(cv);
     }
     __syncthreads();
-    if (threadIdx.x < NW * ROWS) {
-      const int s = threadIdx.x / ROWS;
-      const int r = threadIdx.x % ROWS;
-      const float* a = rb + s * WV * ROWS + r;
-      const float b0 = a[0 * ROWS] + a[1 * ROWS];
-      const float b1 = a[2 * ROWS] + a[3 * ROWS];
+    if (threadIdx.x < NW * ROWS * MT) {
+      const int s = threadIdx.x / (ROWS * MT);
+      const int r = threadIdx.x / MT % ROWS;
+      const int m = threadIdx.x % MT;
+      constexpr int WS = ROWS * MT;  // stride between waves
+      const float* a = rb + (s * WV * ROWS + r) * MT + m;
+      const float b0 = a[0 * WS] + a[1 * WS];
+      const float b1 = a[2 * WS] + a[3 * WS];
       float t;
       if constexpr (WV == 8) {
-        const float b2 = a[4 * ROWS] + a[5 * ROWS];
-        const float b3 = a[6 * ROWS] + a[7 * ROWS];
+        const float b2 = a[4 * WS] + a[5 * WS];
+        const float b3 = a[6 * WS] + a[7 * WS];
         t = (b0 + b1) + (b2 + b3);
       } else {
         t = b0 + b1;
@@ -758,7 +770,7 @@ __global__ void __launch_bounds__(512) gemv_ks_kernel(GemvParams p) {
       }
       const GemvPart& pt = p.part[pi];
       const int rr = (g_done - pt.group0) * ROWS + r;
-      if (rr < pt.n) pt.y[s][rr] = t;
+      if (rr < pt.n && (MT == 1 || m < p.m_rows)) pt.y[s][(size_t)m * pt.ldy + rr] = t;
     }
   };
   // The first group is peeled off the loop, so that its loads, issued in

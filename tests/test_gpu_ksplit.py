@@ -148,3 +148,29 @@ def test_q4_k_ksplit_waves_do_not_change_bits(lib, k):
             os.environ["QG_GEMV_KS_WAVES"] = old
     for a, b in zip(out["4"], out["8"]):
         assert np.array_equal(bits(a), bits(b))
+
+
+# two to four rows of x (tiles of 2 or 4 rows, 4 waves per workgroup at K >= 2048)
+@pytest.mark.parametrize("m,n,k", [(2, 33, 2048), (3, 300, 4096), (4, 70, 8192), (4, 4099, 4096)])
+def test_q4_k_ksplit_rows_of_x_equal_chunked(lib, m, n, k):
+    w, x = synth.q4_k_case(9700 + m + n, m, n, k)
+    dw, dx = dev(w), dev(x)
+    a, b = both(lambda: host(lib.qgemv_q4_k(dw, dx, n, k)))
+    assert np.array_equal(bits(a), bits(b))
+    assert_close(a, oracle.decode_q4_k(w, n, k), x, f"q4_k ksplit m{m} n{n} k{k}")
+
+
+@pytest.mark.parametrize("m", [2, 4])
+def test_dual_and_multi_ksplit_rows_of_x_equal_chunked(lib, m):
+    n, k = 40, 4096
+    wa, wb, x = synth.dual_q4_0_case(9800 + m, m, n, k)
+    dwa, dwb, dx = dev(wa), dev(wb), dev(x)
+    (a0, a1), (b0, b1) = both(lambda: tuple(host(t) for t in lib.qgemv_dual_q4_0(dwa, dwb, dx, n, k)))
+    assert np.array_equal(bits(a0), bits(b0)) and np.array_equal(bits(a1), bits(b1))
+    assert np.array_equal(bits(a0), bits(host(lib.qgemv_q4_0(dwa, dx, n, k))))
+    assert_close(a1, oracle.decode_q4_0(wb, n, k), x, f"dual ksplit m{m}")
+    ns = (96, 40, 17)
+    ws, xm = synth.q4_k_multi_case(9850 + m, m, ns, k)
+    dws, dxm = [dev(w) for w in ws], dev(xm)
+    a, b = both(lambda: host(lib.qgemv_q4_k_multi(dws, dxm, list(ns), k)))
+    assert np.array_equal(bits(a), bits(b))
