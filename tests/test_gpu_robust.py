@@ -91,6 +91,49 @@ def test_graph_replays_match_eager(lib):
     del g
 
 
+def test_graph_replays_small_m_paths(lib):
+    """The matrix-core GEMV (affine, M = 8) and the K-sliced kernel on a tile
+    of 4 rows of x (dual Q4_0, M = 4) captured in one HIP graph: three replays
+    on changing x, each equal bit for bit to eager calls made between them."""
+    import torch
+    n, k, gs = 96, 1024, 64
+    xa, q, s, b = synth.affine_case(7300, 8, n, k, gs)
+    wa, wb, xd = synth.dual_q4_0_case(7301, 4, n, 2048)
+    dq, ds, db, dwa, dwb = dev(q), dev(s), dev(b), dev(wa), dev(wb)
+    dxa, dxd = dev(xa), dev(xd)
+    ya = torch.empty((8, n), dtype=torch.float32, device="cuda")
+    y0 = torch.empty((4, n), dtype=torch.float32, device="cuda")
+    y1 = torch.empty((4, n), dtype=torch.float32, device="cuda")
+
+    def step():
+        lib.qmm_affine_t(dxa, dq, ds, db, gs, y=ya)
+        lib.qgemv_dual_q4_0(dwa, dwb, dxd, n, 2048, y_a=y0, y_b=y1)
+
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    rng = synth.rng(7302)
+    for rep in range(3):
+        nxa = synth.normal_f32(rng, (8, k))
+        nxd = synth.normal_f32(rng, (4, 2048))
+        dxa.copy_(torch.from_numpy(nxa))
+        dxd.copy_(torch.from_numpy(nxd))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [host(t).copy() for t in (ya, y0, y1)]
+        ea = host(lib.qmm_affine_t(dxa, dq, ds, db, gs))
+        e0, e1 = (host(t) for t in lib.qgemv_dual_q4_0(dwa, dwb, dxd, n, 2048))
+        assert np.array_equal(bits(got[0]), bits(ea)), rep
+        assert np.array_equal(bits(got[1]), bits(e0)), rep
+        assert np.array_equal(bits(got[2]), bits(e1)), rep
+        assert_close(got[0], oracle.decode_affine(q, s, b, n, k, gs), nxa, f"graph mma rep {rep}")
+        assert_close(got[2], oracle.decode_q4_0(wb, n, 2048), nxd, f"graph dual rep {rep}")
+    del g
+
+
 def test_two_streams_do_not_interfere(lib):
     """The same products issued on two streams at once (each call's scratch is
     stream-ordered) give the eager single-stream bits."""
