@@ -20,6 +20,7 @@
 #include "kernels/gemv.hpp"
 #include "kernels/mfma.hpp"
 #include "kernels/mma_gemv.hpp"
+#include "kernels/xr_gemv.hpp"
 #include "kernels/split.hpp"
 
 using namespace qg;
@@ -429,6 +430,62 @@ hipError_t launch_gemv_mma(int np, const GemvParams& p, dim3 grid, hipStream_t s
   }
 }
 
+// Q4_0 from 2 rows of x on the matrix cores with x held in registers
+// (gemv_xr_kernel): K a multiple of 512 up to 4096 (one wave per 512
+// columns), weights 16-byte aligned.  Every weight stream of the part list
+// (both of a dual product) becomes one part of the launch.
+bool xr_ok(const HostPart* parts, int nparts, int nw, int64_t m, int64_t k) {
+  // tuning override (different rounding, same tolerance): QG_GEMV_XR=0 keeps the FMA kernels,
+  // QG_GEMV_XR=M takes this kernel from M rows of x on
+  int64_t min_m = 2;
+  if (const char* env = getenv("QG_GEMV_XR")) {
+    if (env[0] == '0') return false;
+    if (atoi(env) > 0) min_m = atoi(env);
+  }
+  if (m < min_m || k % 512 != 0 || k > 512 * kXrMaxWaves) return false;
+  if (nparts * nw > kMaxParts) return false;
+  for (int pi = 0; pi < nparts; ++pi)
+    for (int st = 0; st < nw; ++st)
+      if (!aligned(parts[pi].w[st], 16)) return false;
+  return true;
+}
+
+qg_status run_gemv_xr(const char* op, const HostPart* parts, int nparts, int nw, const float* x, int64_t m,
+                      int64_t k, hipStream_t s) {
+  GemvParams p{};
+  int64_t groups = 0;
+  int np = 0;
+  for (int pi = 0; pi < nparts; ++pi) {
+    for (int st = 0; st < nw; ++st) {
+      GemvPart& gp = p.part[np++];
+      gp.w[0] = gp.w[1] = static_cast<const uint8_t*>(parts[pi].w[st]);
+      gp.y[0] = gp.y[1] = parts[pi].y[st];
+      gp.ldy = parts[pi].ldy;
+      gp.n = (int)parts[pi].n;
+      gp.group0 = (int)groups;
+      groups += cdiv(parts[pi].n, 16);
+    }
+  }
+  p.parts = np;
+  p.n_groups = (int)groups;
+  p.row_bytes = row_bytes_of<FMT_Q40>(k);
+  p.k = (int)k;
+  // x of a workgroup lives in its waves' registers: one workgroup per CU for
+  // K = 4096, more for shorter rows
+  const int waves = (int)(k / 512);
+  const int64_t cap = (int64_t)device_cus() * (kXrMaxWaves / waves);
+  const int64_t grid = groups < cap ? groups : cap;
+  auto kern = np > 1 ? gemv_xr_kernel<true> : gemv_xr_kernel<false>;
+  for (int64_t m0 = 0; m0 < m; m0 += kXrMaxM) {
+    GemvParams q = p;
+    q.x = x + m0 * k;
+    for (int pi = 0; pi < np; ++pi) q.part[pi].y[0] = q.part[pi].y[1] = p.part[pi].y[0] + m0 * p.part[pi].ldy;
+    q.m_rows = (int)(m - m0 < kXrMaxM ? m - m0 : kXrMaxM);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * waves), 0, s, q);
+  }
+  return launch_status(op);
+}
+
 // Runs a part list on the chunked GEMV kernel (or on the plain one when
 // `plain`), over all m-tiles of x.
 template <int FMT, int NW>
@@ -460,6 +517,9 @@ qg_status run_gemv(const char* op, const HostPart* parts, int nparts, const floa
       }
     }
     return launch_status(op);
+  }
+  if constexpr (FMT == FMT_Q40) {
+    if (xr_ok(parts, nparts, NW, m, k)) return run_gemv_xr(op, parts, nparts, NW, x, m, k, s);
   }
   const GemvPlan pl = plan_gemv<FMT>(m, k, NW);
   const int mma = NW == 1 ? mma_pairs<FMT>(parts, nparts, m, k, gs) : 0;

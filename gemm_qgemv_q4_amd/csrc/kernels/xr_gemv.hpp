@@ -1,0 +1,207 @@
+// Q4_0 products at 2..8 rows of x on the gfx950 matrix cores, with x held in
+// registers for the whole launch.
+//
+// y[m, n] = sum_b d[n, b] * ( sum_{k in b} x[m, k] q[n, k]  -  8 sum_{k in b} x[m, k] )
+// over the 32-weight blocks b of a row [GGML block_q4_0: w = d (q - 8)].
+//
+// Each 32-weight block is one v_mfma_f32_16x16x32_bf16 whose 16 columns are
+// 16 weight rows and whose 16 rows are x: rows 0..7 hold bf16(x) of the (up
+// to) 8 rows of x, rows 8..15 hold bf16(x - bf16(x)).  Both halves of x thus
+// ride in one MFMA, and the output's two partial sums are added at the end
+// (x carries 16 significant bits, relative error <= 2^-18 per element; the
+// codes 0..15 are exact in bf16 and the products exact in the f32
+// accumulator).  The block sums of x come from the same MFMA unit (x times a
+// column of ones), so that a block of codes 8 gives exactly P - 8 X = 0.
+//
+// Work split: a workgroup of K/512 waves owns 16 weight rows at a time; wave
+// w owns columns 512 w .. 512 w + 511, i.e. NB = 16 blocks (288 bytes of each
+// row).  The wave keeps its slice of x as 16 MFMA A operands (64 VGPRs) and
+// the block sums (64 VGPRs) for the whole launch, so after the first load x
+// costs no memory or LDS traffic.  The MFMA wants, in lane l, 4 code bytes of
+// weight row l % 16; loads that narrow touch 16 rows per instruction and
+// stream poorly, so the wave reads its 16 x 288 bytes with 16-byte loads
+// along the rows (18 lanes per row), writes them to its own LDS region and
+// reads the MFMA operands from there.  The loads of the next row group leave
+// before the arithmetic on the current one.  The wave partials of an output
+// are added in a fixed order through LDS, one barrier per row group.
+#pragma once
+#include "common.hpp"
+#include "gemv.hpp"
+
+namespace qg {
+
+constexpr int kXrNB = 16;        // 32-weight blocks per wave
+constexpr int kXrMaxWaves = 8;   // K <= 4096
+constexpr int kXrMaxM = 8;       // x rows per launch
+constexpr int kRowLds = 304;     // LDS bytes per weight row copy (288 used)
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two bytes holding codes 0..15 (byte pair `hiword` of v) as two exact bf16:
+// read as OCP e4m3 the bytes 0..15 are q / 512, scaled back by 2^9.
+template <bool HIWORD>
+__device__ __forceinline__ uint32_t codes2_bf16(uint32_t v) {
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 512.0f, HIWORD);
+  return __builtin_bit_cast(uint32_t, c);
+}
+
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  const bf16x2 c = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, c);
+}
+
+__device__ __forceinline__ uint32_t dpp_row_ror8(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, true);  // row_ror:8
+}
+
+template <bool MULTI>
+__global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p) {
+  constexpr int NB = kXrNB;
+  __shared__ float red[2][kXrMaxWaves][16][16];  // [buffer][wave][MFMA row][column]
+  __shared__ u32x4 wlds[kXrMaxWaves][16 * kRowLds / 16];  // per wave: 16 rows of kRowLds bytes
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x / kWave;
+  const int waves = blockDim.x / kWave;
+  const int r = lane & 15;  // MFMA row of A (x row r & 7; bf16(x) for r < 8, the remainder for r >= 8) and column of B
+  const int kp = lane >> 4;  // K piece: code bytes 4 kp .. 4 kp + 3 of a block (weights 4kp.., 16 + 4kp..)
+  const bool lo_row = r >= 8;
+  const int kb0 = wv * NB;  // first block of this wave
+
+  int t = blockIdx.x;
+  if (t >= p.n_groups) return;
+
+  // ---- x slice: lane loads weights 4kp..4kp+3 (rows 0..7) or 16+4kp.. (rows 8..15)
+  // of its x row for every block; the two lanes r and r + 8 then trade halves.
+  const int mx = r & 7;
+  const bool live = mx < p.m_rows;
+  const float* xp = p.x + (size_t)(live ? mx : 0) * p.k + 32 * kb0 + 4 * kp + (lo_row ? 16 : 0);
+  f32x4 xv[NB];
+#pragma unroll
+  for (int s = 0; s < NB; ++s) xv[s] = *reinterpret_cast<const f32x4a4*>(xp + 32 * s);
+
+  // ---- weight loads of one row group: 16 rows x 288 bytes as 288 pieces of
+  // 16 bytes (piece i: row i / 18, bytes 16 (i % 18) of the wave's slice);
+  // lane l loads pieces l + 64 j.  Pieces past 288 load piece 287 again and are
+  // not stored.  Rows are whole multiples of 288 bytes, so every piece is
+  // 16-byte aligned when the weights are.
+  auto part_of = [&](int tile) -> const GemvPart& {
+    int pi = 0;
+    if constexpr (MULTI) {
+      for (int i = 1; i < p.parts; ++i)
+        if (tile >= p.part[i].group0) pi = i;
+      pi = __builtin_amdgcn_readfirstlane(pi);
+    }
+    return p.part[pi];
+  };
+  constexpr int PIECES = 16 * 18;
+  constexpr int LOADS = (PIECES + kWave - 1) / kWave;  // 5
+  u32x4 gq[LOADS];
+  auto fetch = [&](int tile) {
+    const GemvPart& pt = part_of(tile);
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int i = lane + kWave * j < PIECES ? lane + kWave * j : PIECES - 1;
+      const int rr = (tile - pt.group0) * 16 + i / 18;
+      const int row = rr < pt.n ? rr : pt.n - 1;  // clamped for the loads; not stored
+      gq[j] = *reinterpret_cast<const u32x4*>(pt.w[0] + (size_t)row * (size_t)p.row_bytes + 288 * wv + 16 * (i % 18));
+    }
+  };
+  // The wave's LDS copy: row n at byte kRowLds n (a stride of 76 dwords puts
+  // the 16 rows x 4 pieces of one MFMA operand read in 64 distinct banks).
+  uint8_t* wl = reinterpret_cast<uint8_t*>(&wlds[wv][0]);
+  auto stage = [&]() {
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int i = lane + kWave * j;
+      if (i < PIECES) *reinterpret_cast<u32x4*>(wl + kRowLds * (i / 18) + 16 * (i % 18)) = gq[j];
+    }
+    // LDS operations of one wave complete in order; this only keeps the
+    // compiler from moving the reads above the writes.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  fetch(t);
+  // the weight loads leave before the x arithmetic below, behind the x loads only
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- A operands and block sums.  Row r < 8 takes bf16(x) of weights
+  // [4kp..4kp+3, 16+4kp..16+4kp+3]; row r + 8 takes bf16(x - bf16(x)) of the same.
+  bf16x8 a[NB];
+  f32x4 xs[NB];  // -8 * (block sum of this lane's MFMA rows 4kp .. 4kp+3)
+  {
+    const bf16x8 ones = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
+                         (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
+    const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < NB; ++s) {
+      const f32x4 v = live ? xv[s] : z;
+      const uint32_t h01 = pk_bf16(v.x, v.y), h23 = pk_bf16(v.z, v.w);
+      const float f0 = __builtin_bit_cast(float, h01 << 16), f1 = __builtin_bit_cast(float, h01 & 0xFFFF0000u);
+      const float f2 = __builtin_bit_cast(float, h23 << 16), f3 = __builtin_bit_cast(float, h23 & 0xFFFF0000u);
+      const uint32_t l01 = pk_bf16(v.x - f0, v.y - f1), l23 = pk_bf16(v.z - f2, v.w - f3);
+      // lane r sends the remainders of its half to row r + 8, which sends its bf16(x) back
+      const uint32_t r01 = dpp_row_ror8(lo_row ? h01 : l01);
+      const uint32_t r23 = dpp_row_ror8(lo_row ? h23 : l23);
+      const u32x4 av = lo_row ? u32x4{r01, r23, l01, l23} : u32x4{h01, h23, r01, r23};
+      a[s] = __builtin_bit_cast(bf16x8, av);
+      const f32x4 bs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], ones, z, 0, 0, 0);
+      xs[s] = bs * -8.0f;
+    }
+  }
+
+  for (int it = 0;; ++it) {
+    const int tn = t + (int)gridDim.x;
+    const bool more = tn < p.n_groups;
+    stage();
+    fetch(more ? tn : t);  // the next row group (after the last one: this one again, unused)
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    // Block s of row r sits at byte 18 s of the row's copy.  Even blocks start
+    // 4-byte aligned: code bytes 4kp.. at 2 + 4kp, read as two dwords; odd
+    // blocks have them in one dword.  The scale is the low (even) or high
+    // (odd) half of the dword holding the block start.
+    const uint8_t* rl = wl + kRowLds * r;
+#pragma unroll
+    for (int s = 0; s < NB; ++s) {
+      uint32_t v, db;
+      const uint8_t* blk = rl + 18 * s;
+      if (s % 2 == 0) {
+        const uint32_t q0 = *reinterpret_cast<const uint32_t*>(blk + 4 * kp);
+        const uint32_t q1 = *reinterpret_cast<const uint32_t*>(blk + 4 * kp + 4);
+        v = __builtin_amdgcn_alignbyte(q1, q0, 2);
+        db = *reinterpret_cast<const uint32_t*>(blk);
+      } else {
+        v = *reinterpret_cast<const uint32_t*>(blk + 2 + 4 * kp);
+        db = *reinterpret_cast<const uint32_t*>(blk - 2) >> 16;
+      }
+      const uint32_t lo = v & 0x0F0F0F0Fu;
+      const uint32_t hi = (v >> 4) & 0x0F0F0F0Fu;
+      const u32x4 bv = {codes2_bf16<false>(lo), codes2_bf16<true>(lo), codes2_bf16<false>(hi), codes2_bf16<true>(hi)};
+      const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+      const f32x4 P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], __builtin_bit_cast(bf16x8, bv), z, 0, 0, 0);
+      const float d = f16_bits_to_f32(db);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(d, P[i] + xs[s][i], acc[i]);
+    }
+    // acc[i]: MFMA row 4 kp + i (x row (4kp+i) & 7, high or low part) for weight row r of the group
+    float* rb = &red[it & 1][wv][0][0];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rb[(4 * kp + i) * 16 + r] = acc[i];
+    __syncthreads();
+    for (int e = threadIdx.x; e < kXrMaxM * 16; e += blockDim.x) {
+      const int m = e >> 4;
+      const int n = e & 15;
+      float sum = red[it & 1][0][m][n] + red[it & 1][0][m + 8][n];
+      for (int w = 1; w < waves; ++w) sum += red[it & 1][w][m][n] + red[it & 1][w][m + 8][n];
+      const GemvPart& pt = part_of(t);
+      const int rr = (t - pt.group0) * 16 + n;
+      if (m < p.m_rows && rr < pt.n) pt.y[0][(size_t)m * pt.ldy + rr] = sum;
+    }
+    // red[it & 1] is written again two groups later, after the next barrier
+    if (!more) break;
+    t = tn;
+  }
+}
+
+}  // namespace qg

@@ -20,18 +20,21 @@ def bits(a):
 
 
 def both(call):
-    """(K-sliced result, chunked result) of one call."""
-    old = os.environ.get("QG_GEMV_KS")
+    """(K-sliced result, chunked result) of one call.  The matrix-core Q4_0
+    GEMV, which takes Q4_0 from 2 rows of x on, is switched off for both."""
+    old = {v: os.environ.get(v) for v in ("QG_GEMV_KS", "QG_GEMV_XR")}
     try:
+        os.environ["QG_GEMV_XR"] = "0"
         os.environ["QG_GEMV_KS"] = "1"
         a = call()
         os.environ["QG_GEMV_KS"] = "0"
         b = call()
     finally:
-        if old is None:
-            os.environ.pop("QG_GEMV_KS", None)
-        else:
-            os.environ["QG_GEMV_KS"] = old
+        for v, o in old.items():
+            if o is None:
+                os.environ.pop(v, None)
+            else:
+                os.environ[v] = o
     return a, b
 
 
