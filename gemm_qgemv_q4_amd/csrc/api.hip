@@ -430,14 +430,17 @@ hipError_t launch_gemv_mma(int np, const GemvParams& p, dim3 grid, hipStream_t s
   }
 }
 
-// Q4_0 from 2 rows of x on the matrix cores with x held in registers
-// (gemv_xr_kernel): K a multiple of 512 up to 4096 (one wave per 512
-// columns), weights 16-byte aligned.  Every weight stream of the part list
+// Q4_0 and Q4_K from 3 rows of x on the matrix cores with x held in
+// registers (gemv_xr_kernel): K a multiple of 512 up to 4096 (one wave per
+// 512 columns), weights 16-byte aligned.  Every weight stream of the part list
 // (both of a dual product) becomes one part of the launch.
 bool xr_ok(const HostPart* parts, int nparts, int nw, int64_t m, int64_t k) {
   // tuning override (different rounding, same tolerance): QG_GEMV_XR=0 keeps the FMA kernels,
   // QG_GEMV_XR=M takes this kernel from M rows of x on
-  int64_t min_m = 2;
+  // Measured (graph replay, K = 4096): at 2 rows the K-sliced FMA kernel is
+  // ahead (N = 4096: 6.2 vs 7.4 us), from 3 rows this one (N = 14336: 19.4 vs
+  // 13.9 us at 3 rows, 50.1 vs 15.4 us at 8).
+  int64_t min_m = 3;
   if (const char* env = getenv("QG_GEMV_XR")) {
     if (env[0] == '0') return false;
     if (atoi(env) > 0) min_m = atoi(env);
@@ -450,6 +453,7 @@ bool xr_ok(const HostPart* parts, int nparts, int nw, int64_t m, int64_t k) {
   return true;
 }
 
+template <int FMT>
 qg_status run_gemv_xr(const char* op, const HostPart* parts, int nparts, int nw, const float* x, int64_t m,
                       int64_t k, hipStream_t s) {
   GemvParams p{};
@@ -468,14 +472,16 @@ qg_status run_gemv_xr(const char* op, const HostPart* parts, int nparts, int nw,
   }
   p.parts = np;
   p.n_groups = (int)groups;
-  p.row_bytes = row_bytes_of<FMT_Q40>(k);
+  p.row_bytes = row_bytes_of<FMT>(k);
   p.k = (int)k;
   // x of a workgroup lives in its waves' registers: one workgroup per CU for
   // K = 4096, more for shorter rows
   const int waves = (int)(k / 512);
-  const int64_t cap = (int64_t)device_cus() * (kXrMaxWaves / waves);
+  int64_t cap = (int64_t)device_cus() * (kXrMaxWaves / waves);
+  if (const char* env = getenv("QG_GEMV_XR_GRID"))  // tuning override: workgroups
+    if (atoi(env) > 0) cap = atoi(env);
   const int64_t grid = groups < cap ? groups : cap;
-  auto kern = np > 1 ? gemv_xr_kernel<true> : gemv_xr_kernel<false>;
+  auto kern = np > 1 ? gemv_xr_kernel<FMT, true> : gemv_xr_kernel<FMT, false>;
   for (int64_t m0 = 0; m0 < m; m0 += kXrMaxM) {
     GemvParams q = p;
     q.x = x + m0 * k;
@@ -518,8 +524,8 @@ qg_status run_gemv(const char* op, const HostPart* parts, int nparts, const floa
     }
     return launch_status(op);
   }
-  if constexpr (FMT == FMT_Q40) {
-    if (xr_ok(parts, nparts, NW, m, k)) return run_gemv_xr(op, parts, nparts, NW, x, m, k, s);
+  if constexpr (FMT == FMT_Q40 || FMT == FMT_Q4K) {
+    if (xr_ok(parts, nparts, NW, m, k)) return run_gemv_xr<FMT>(op, parts, nparts, NW, x, m, k, s);
   }
   const GemvPlan pl = plan_gemv<FMT>(m, k, NW);
   const int mma = NW == 1 ? mma_pairs<FMT>(parts, nparts, m, k, gs) : 0;

@@ -1,8 +1,11 @@
-// Q4_0 products at 2..8 rows of x on the gfx950 matrix cores, with x held in
-// registers for the whole launch.
+// Q4_0 and Q4_K products at 3..8 rows of x on the gfx950 matrix cores, with
+// x held in registers for the whole launch.
 //
-// y[m, n] = sum_b d[n, b] * ( sum_{k in b} x[m, k] q[n, k]  -  8 sum_{k in b} x[m, k] )
-// over the 32-weight blocks b of a row [GGML block_q4_0: w = d (q - 8)].
+// Q4_0: y[m, n] = sum_b d[n, b] (P[m, n, b] - 8 X[m, b])      [GGML block_q4_0: w = d (q - 8)]
+// Q4_K: y[m, n] = sum_j (d sc_j)[n] P[m, n, j] - (dmin m_j)[n] X[m, j]
+//                                               [GGML block_q4_K: w = d sc_j q - dmin m_j]
+// with P = sum over a 32-weight block (Q4_0) or sub-block (Q4_K) of x q and X
+// the sum of x over it.
 //
 // Each 32-weight block is one v_mfma_f32_16x16x32_bf16 whose 16 columns are
 // 16 weight rows and whose 16 rows are x: rows 0..7 hold bf16(x) of the (up
@@ -11,7 +14,8 @@
 // (x carries 16 significant bits, relative error <= 2^-18 per element; the
 // codes 0..15 are exact in bf16 and the products exact in the f32
 // accumulator).  The block sums of x come from the same MFMA unit (x times a
-// column of ones), so that a block of codes 8 gives exactly P - 8 X = 0.
+// column of -8 for Q4_0, of ones for Q4_K), so that a Q4_0 block of codes 8
+// gives exactly P - 8 X = 0.
 //
 // Work split: a workgroup of K/512 waves owns 16 weight rows at a time; wave
 // w owns columns 512 w .. 512 w + 511, i.e. NB = 16 blocks (288 bytes of each
@@ -54,8 +58,10 @@ __device__ __forceinline__ uint32_t dpp_row_ror8(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, true);  // row_ror:8
 }
 
-template <bool MULTI>
+template <int FMT, bool MULTI>
 __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p) {
+  static_assert(FMT == FMT_Q40 || FMT == FMT_Q4K, "4-bit block formats");
+  constexpr bool K4 = FMT == FMT_Q4K;
   constexpr int NB = kXrNB;
   __shared__ float red[2][kXrMaxWaves][16][16];  // [buffer][wave][MFMA row][column]
   __shared__ u32x4 wlds[kXrMaxWaves][16 * kRowLds / 16];  // per wave: 16 rows of kRowLds bytes
@@ -64,26 +70,26 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p)
   const int wv = threadIdx.x / kWave;
   const int waves = blockDim.x / kWave;
   const int r = lane & 15;  // MFMA row of A (x row r & 7; bf16(x) for r < 8, the remainder for r >= 8) and column of B
-  const int kp = lane >> 4;  // K piece: code bytes 4 kp .. 4 kp + 3 of a block (weights 4kp.., 16 + 4kp..)
+  const int kp = lane >> 4;  // K piece: weights 4kp..4kp+3, 16+4kp..16+4kp+3 of a Q4_0 block, 8kp..8kp+7 of a Q4_K sub-block
   const bool lo_row = r >= 8;
   const int kb0 = wv * NB;  // first block of this wave
 
   int t = blockIdx.x;
   if (t >= p.n_groups) return;
 
-  // ---- x slice: lane loads weights 4kp..4kp+3 (rows 0..7) or 16+4kp.. (rows 8..15)
-  // of its x row for every block; the two lanes r and r + 8 then trade halves.
+  // ---- x slice: for every block lane r < 8 loads the first four of its K
+  // piece's x values, lane r + 8 the last four; the two then trade halves.
   const int mx = r & 7;
   const bool live = mx < p.m_rows;
-  const float* xp = p.x + (size_t)(live ? mx : 0) * p.k + 32 * kb0 + 4 * kp + (lo_row ? 16 : 0);
+  const int e0 = K4 ? 8 * kp + (lo_row ? 4 : 0) : 4 * kp + (lo_row ? 16 : 0);
+  const float* xp = p.x + (size_t)(live ? mx : 0) * p.k + 32 * kb0 + e0;
   f32x4 xv[NB];
 #pragma unroll
   for (int s = 0; s < NB; ++s) xv[s] = *reinterpret_cast<const f32x4a4*>(xp + 32 * s);
 
   // ---- weight loads of one row group: 16 rows x 288 bytes as 288 pieces of
   // 16 bytes (piece i: row i / 18, bytes 16 (i % 18) of the wave's slice);
-  // lane l loads pieces l + 64 j.  Pieces past 288 load piece 287 again and are
-  // not stored.  Rows are whole multiples of 288 bytes, so every piece is
+  // lane l loads pieces l + 64 j (past piece 287: piece 287 again).  Rows are whole multiples of 288 bytes, so every piece is
   // 16-byte aligned when the weights are.
   auto part_of = [&](int tile) -> const GemvPart& {
     int pi = 0;
@@ -96,8 +102,8 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p)
   };
   constexpr int PIECES = 16 * 18;
   constexpr int LOADS = (PIECES + kWave - 1) / kWave;  // 5
-  u32x4 gq[LOADS];
-  auto fetch = [&](int tile) {
+  u32x4 ga[LOADS], gb[LOADS];  // two row groups in flight
+  auto fetch = [&](u32x4 (&gq)[LOADS], int tile) {
     const GemvPart& pt = part_of(tile);
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
@@ -110,11 +116,12 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p)
   // The wave's LDS copy: row n at byte kRowLds n (a stride of 76 dwords puts
   // the 16 rows x 4 pieces of one MFMA operand read in 64 distinct banks).
   uint8_t* wl = reinterpret_cast<uint8_t*>(&wlds[wv][0]);
-  auto stage = [&]() {
+  auto stage = [&](const u32x4 (&gq)[LOADS]) {
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
-      const int i = lane + kWave * j;
-      if (i < PIECES) *reinterpret_cast<u32x4*>(wl + kRowLds * (i / 18) + 16 * (i % 18)) = gq[j];
+      // lanes past piece 287 loaded piece 287 again and write the same bytes there
+      const int i = lane + kWave * j < PIECES ? lane + kWave * j : PIECES - 1;
+      *reinterpret_cast<u32x4*>(wl + kRowLds * (i / 18) + 16 * (i % 18)) = gq[j];
     }
     // LDS operations of one wave complete in order; this only keeps the
     // compiler from moving the reads above the writes.
@@ -122,17 +129,26 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p)
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
-  fetch(t);
+  // Row groups t and t + G (G workgroups) are loaded first; group t + 2G leaves
+  // when group t has been copied to LDS.  Past the last group the loads repeat
+  // a group of this workgroup and are not used.
+  const int G = (int)gridDim.x;
+  fetch(ga, t);
+  fetch(gb, t + G < p.n_groups ? t + G : t);
   // the weight loads leave before the x arithmetic below, behind the x loads only
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- A operands and block sums.  Row r < 8 takes bf16(x) of weights
-  // [4kp..4kp+3, 16+4kp..16+4kp+3]; row r + 8 takes bf16(x - bf16(x)) of the same.
+  // ---- A operands and block sums.  Row r < 8 takes bf16(x) of its K piece's
+  // 8 weights, row r + 8 takes bf16(x - bf16(x)) of the same.
   bf16x8 a[NB];
-  f32x4 xs[NB];  // -8 * (block sum of this lane's MFMA rows 4kp .. 4kp+3)
+  f32x4 xs[NB];  // Q4_0: -8 X, Q4_K: X, of this lane's MFMA rows 4kp .. 4kp+3
   {
-    const bf16x8 ones = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
-                         (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
+    // Q4_0: x times a column of -8 is exactly -8 times the block sum (a
+    // power-of-two scale commutes with the rounding), so that P + xs is
+    // exactly 0 for a block of codes 8
+    const float cs = K4 ? 1.0f : -8.0f;
+    const bf16x8 m8 = {(__bf16)cs, (__bf16)cs, (__bf16)cs, (__bf16)cs,
+                       (__bf16)cs, (__bf16)cs, (__bf16)cs, (__bf16)cs};
     const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int s = 0; s < NB; ++s) {
@@ -146,43 +162,95 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p)
       const uint32_t r23 = dpp_row_ror8(lo_row ? h23 : l23);
       const u32x4 av = lo_row ? u32x4{r01, r23, l01, l23} : u32x4{h01, h23, r01, r23};
       a[s] = __builtin_bit_cast(bf16x8, av);
-      const f32x4 bs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], ones, z, 0, 0, 0);
-      xs[s] = bs * -8.0f;
+      xs[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], m8, z, 0, 0, 0);
     }
   }
 
-  for (int it = 0;; ++it) {
-    const int tn = t + (int)gridDim.x;
-    const bool more = tn < p.n_groups;
-    stage();
-    fetch(more ? tn : t);  // the next row group (after the last one: this one again, unused)
+  // One row group from buffer gq: copy it to LDS, send the loads of the group
+  // two ahead into gq, multiply, add the wave partials.
+  int it = 0;
+  auto tile = [&](u32x4 (&gq)[LOADS]) {
+    stage(gq);
+    const int t2 = t + 2 * G;
+    fetch(gq, t2 < p.n_groups ? t2 : t);
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    // Block s of row r sits at byte 18 s of the row's copy.  Even blocks start
-    // 4-byte aligned: code bytes 4kp.. at 2 + 4kp, read as two dwords; odd
-    // blocks have them in one dword.  The scale is the low (even) or high
-    // (odd) half of the dword holding the block start.
     const uint8_t* rl = wl + kRowLds * r;
-#pragma unroll
-    for (int s = 0; s < NB; ++s) {
-      uint32_t v, db;
-      const uint8_t* blk = rl + 18 * s;
-      if (s % 2 == 0) {
-        const uint32_t q0 = *reinterpret_cast<const uint32_t*>(blk + 4 * kp);
-        const uint32_t q1 = *reinterpret_cast<const uint32_t*>(blk + 4 * kp + 4);
-        v = __builtin_amdgcn_alignbyte(q1, q0, 2);
-        db = *reinterpret_cast<const uint32_t*>(blk);
-      } else {
-        v = *reinterpret_cast<const uint32_t*>(blk + 2 + 4 * kp);
-        db = *reinterpret_cast<const uint32_t*>(blk - 2) >> 16;
-      }
-      const uint32_t lo = v & 0x0F0F0F0Fu;
-      const uint32_t hi = (v >> 4) & 0x0F0F0F0Fu;
-      const u32x4 bv = {codes2_bf16<false>(lo), codes2_bf16<true>(lo), codes2_bf16<false>(hi), codes2_bf16<true>(hi)};
+    auto mfma = [&](int s, uint32_t c0, uint32_t c1) -> f32x4 {
+      const u32x4 bv = {codes2_bf16<false>(c0), codes2_bf16<true>(c0), codes2_bf16<false>(c1), codes2_bf16<true>(c1)};
       const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-      const f32x4 P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], __builtin_bit_cast(bf16x8, bv), z, 0, 0, 0);
-      const float d = f16_bits_to_f32(db);
+      return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], __builtin_bit_cast(bf16x8, bv), z, 0, 0, 0);
+    };
+    if constexpr (!K4) {
+      // Block s of row r sits at byte 18 s of the row's copy.  Even blocks start
+      // 4-byte aligned: code bytes 4kp.. at 2 + 4kp, read as two dwords; odd
+      // blocks have them in one dword.  The scale is the low (even) or high
+      // (odd) half of the dword holding the block start.
+      auto product = [&](int s, uint32_t& db) -> f32x4 {
+        uint32_t v;
+        const uint8_t* blk = rl + 18 * s;
+        if (s % 2 == 0) {
+          const uint32_t q0 = *reinterpret_cast<const uint32_t*>(blk + 4 * kp);
+          const uint32_t q1 = *reinterpret_cast<const uint32_t*>(blk + 4 * kp + 4);
+          v = __builtin_amdgcn_alignbyte(q1, q0, 2);
+          db = *reinterpret_cast<const uint32_t*>(blk);
+        } else {
+          v = *reinterpret_cast<const uint32_t*>(blk + 2 + 4 * kp);
+          db = *reinterpret_cast<const uint32_t*>(blk - 2) >> 16;
+        }
+        return mfma(s, v & 0x0F0F0F0Fu, (v >> 4) & 0x0F0F0F0Fu);
+      };
+      // block s + 1 is multiplied before block s is scaled into acc
+      uint32_t db0;
+      f32x4 P0 = product(0, db0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(d, P[i] + xs[s][i], acc[i]);
+      for (int s = 0; s < NB; ++s) {
+        uint32_t db1 = 0;
+        f32x4 P1 = P0;
+        if (s + 1 < NB) P1 = product(s + 1, db1);
+        const float d = f16_bits_to_f32(db0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(d, P0[i] + xs[s][i], acc[i]);
+        P0 = P1;
+        db0 = db1;
+      }
+    } else {
+      // Super-block b (two per wave) of row r sits at byte 144 b of the row's
+      // copy: d, dmin, 12 scale bytes, then 4 runs of 32 code bytes.  Sub-block
+      // j takes the low (j even) or high nibbles of run j / 2; K piece kp is
+      // its bytes 8kp .. 8kp + 7.
+#pragma unroll
+      for (int b = 0; b < NB / 8; ++b) {
+        const uint8_t* sb = rl + 144 * b;
+        const u32x4 hd = *reinterpret_cast<const u32x4*>(sb);
+        const float d = f16_bits_to_f32(hd[0]), dmin = f16_bits_to_f32(hd[0] >> 16);
+        // 6-bit scales and mins of sub-blocks 0..3 and 4..7, one per byte
+        const uint32_t sc03 = hd[1] & 0x3F3F3F3Fu, mn03 = hd[2] & 0x3F3F3F3Fu;
+        const uint32_t sc47 = (hd[3] & 0x0F0F0F0Fu) | ((hd[1] >> 2) & 0x30303030u);
+        const uint32_t mn47 = ((hd[3] >> 4) & 0x0F0F0F0Fu) | ((hd[2] >> 2) & 0x30303030u);
+        uint2 qv[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) qv[c] = *reinterpret_cast<const uint2*>(sb + 16 + 32 * c + 8 * kp);
+        auto product = [&](int j) -> f32x4 {
+          const uint2 v = qv[j / 2];
+          const int sh = 4 * (j % 2);
+          return mfma(8 * b + j, (v.x >> sh) & 0x0F0F0F0Fu, (v.y >> sh) & 0x0F0F0F0Fu);
+        };
+        f32x4 P0 = product(0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          f32x4 P1 = P0;
+          if (j + 1 < 8) P1 = product(j + 1);
+          const uint32_t scw = j < 4 ? sc03 : sc47, mnw = j < 4 ? mn03 : mn47;
+          const float ds = d * (float)((scw >> (8 * (j % 4))) & 0xFFu);
+          const float dm = -(dmin * (float)((mnw >> (8 * (j % 4))) & 0xFFu));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[i] = __builtin_fmaf(ds, P0[i], acc[i]);
+            acc[i] = __builtin_fmaf(dm, xs[8 * b + j][i], acc[i]);
+          }
+          P0 = P1;
+        }
+      }
     }
     // acc[i]: MFMA row 4 kp + i (x row (4kp+i) & 7, high or low part) for weight row r of the group
     float* rb = &red[it & 1][wv][0][0];
@@ -199,8 +267,18 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p)
       if (m < p.m_rows && rr < pt.n) pt.y[0][(size_t)m * pt.ldy + rr] = sum;
     }
     // red[it & 1] is written again two groups later, after the next barrier
-    if (!more) break;
-    t = tn;
+    ++it;
+    t += G;
+  };
+  // The first two groups are peeled off the loop: in straight-line code the
+  // compiler waits for each group's own loads, at the loop head for all.
+  tile(ga);
+  if (t >= p.n_groups) return;
+  tile(gb);
+  while (t < p.n_groups) {
+    tile(ga);
+    if (t >= p.n_groups) break;
+    tile(gb);
   }
 }
 

@@ -1,7 +1,8 @@
-"""The matrix-core Q4_0 GEMV with x in registers (2..8 rows of x per launch,
-K a multiple of 512 up to 4096) against the f64 oracle, and its stated
-equalities: the dual product bitwise equal to two single calls, each row of x
-independent of the others, blocks of codes 8 giving exactly zero.  The tuning
+"""The matrix-core Q4_0 / Q4_K GEMV with x in registers (from 3 rows of x, up
+to 8 per launch, K a multiple of 512 up to 4096) against the f64 oracle, and
+its stated equalities: the dual Q4_0 and the multi-part Q4_K products bitwise
+equal to single calls, each row of x independent of the others, Q4_0 blocks of
+codes 8 giving exactly zero, the hand-worked Q4_K super-block exactly.  The tuning
 switch QG_GEMV_XR=0 selects the FMA kernels, whose results must agree within
 the same tolerance.  Shapes outside that range (K = 4160, 8192, 256) take the
 FMA kernels and are checked the same way."""
@@ -33,10 +34,10 @@ def with_env(val, call):
             os.environ["QG_GEMV_XR"] = old
 
 
-# M from 2 to 40 (one to five launches of up to 8 rows), K from one wave (512)
+# M from 3 to 40 (one to five launches of up to 8 rows), K from one wave (512)
 # to eight (4096) and 3072 (six waves), ragged N (1, 15, 17 rows: partial
 # 16-row groups); then shapes that stay on the FMA kernels
-CASES = [(2, 1, 512), (3, 17, 1024), (8, 33, 2048), (5, 100, 3072), (8, 300, 4096), (4, 16, 4096),
+CASES = [(3, 1, 512), (3, 17, 1024), (8, 33, 2048), (5, 100, 3072), (8, 300, 4096), (4, 16, 4096),
          (9, 40, 4096), (16, 15, 1024), (40, 65, 512), (7, 1000, 4096),
          (4, 20, 4160), (3, 9, 8192), (6, 30, 256)]
 
@@ -54,7 +55,7 @@ def test_q4_0_xr_against_oracle_and_fma_path(lib, m, n, k):
     assert np.array_equal(bits(y), bits(host(lib.qgemv_q4_0(dw, dx, n, k))))
 
 
-@pytest.mark.parametrize("m,n,k", [(2, 50, 4096), (4, 4096, 4096), (8, 257, 2048), (5, 31, 512), (13, 19, 1024)])
+@pytest.mark.parametrize("m,n,k", [(3, 50, 4096), (4, 4096, 4096), (8, 257, 2048), (5, 31, 512), (13, 19, 1024)])
 def test_dual_xr_bitwise_equals_two_singles(lib, m, n, k):
     wa, wb, x = synth.dual_q4_0_case(9500 + m + n, m, n, k)
     dwa, dwb, dx = dev(wa), dev(wb), dev(x)
@@ -67,22 +68,22 @@ def test_dual_xr_bitwise_equals_two_singles(lib, m, n, k):
 
 def test_xr_rows_of_x_are_independent(lib):
     """Output row m depends on x row m only: the same x row gives the same bits
-    at any position of an 8-row tile and in a 2-row launch."""
+    at any position of an 8-row tile and of a 3-row launch."""
     n, k = 70, 4096
     w, x = synth.q4_0_case(9600, 8, n, k)
     dw = dev(w)
     y8 = host(lib.qgemv_q4_0(dw, dev(x), n, k))
     for pos in (0, 3, 7):
-        x2 = np.stack([x[(pos + 1) % 8], x[pos]])
-        y2 = host(lib.qgemv_q4_0(dw, dev(x2), n, k))
-        assert np.array_equal(bits(y2[1]), bits(y8[pos])), pos
+        x3 = np.stack([x[(pos + 1) % 8], x[pos], x[(pos + 2) % 8]])
+        y3 = host(lib.qgemv_q4_0(dw, dev(x3), n, k))
+        assert np.array_equal(bits(y3[1]), bits(y8[pos])), pos
 
 
 def test_xr_blocks_of_eights_give_exact_zero(lib):
-    """Rows whose blocks all hold codes 8 (w = 0 for any scale) give exactly 0;
-    a row of the hand block [d = 0.5, qs[0] = 0x1F, qs[1] = 0x80, rest 0x88]
-    followed by such blocks gives -4 sum x[.., 1] ... exactly the oracle value
-    for integer x."""
+    """Rows whose blocks all hold codes 8 (w = 0 for any scale) give exactly 0
+    for any x, and a row holding the hand block [d = 0.5, qs[0] = 0x1F,
+    qs[1] = 0x80, rest 0x88] at block 3 gives 3.5 x[96] - 4 x[97] - 3.5 x[112],
+    exactly for integer x."""
     n, k, m = 33, 2048, 6
     g = np.random.default_rng(9700)
     blocks = np.zeros((n, k // 32, 18), np.uint8)
@@ -90,18 +91,21 @@ def test_xr_blocks_of_eights_give_exact_zero(lib):
                       np.uint8).reshape(n, k // 32, 2)
     blocks[:, :, 0:2] = d
     blocks[:, :, 2:] = 0x88
-    # row 5: the hand block at block 3
     blocks[5, 3, 0:2] = np.frombuffer(np.float16(0.5).tobytes(), np.uint8)
     blocks[5, 3, 2] = 0x1F
     blocks[5, 3, 3] = 0x80
     w = blocks.reshape(-1)
-    x = g.integers(-4, 5, size=(m, k)).astype(np.float32)
-    y = host(lib.qgemv_q4_0(dev(w), dev(x), n, k))
+    dw = dev(w)
+    xi = g.integers(-4, 5, size=(m, k)).astype(np.float32)
+    y = host(lib.qgemv_q4_0(dw, dev(xi), n, k))
     want = np.zeros((m, n), np.float32)
-    # hand block: w[0] = 3.5, w[1] = -4.0, w[16] = -3.5, others 0 (columns 96 + j)
-    want[:, 5] = 3.5 * x[:, 96] - 4.0 * x[:, 97] - 3.5 * x[:, 112]
+    want[:, 5] = 3.5 * xi[:, 96] - 4.0 * xi[:, 97] - 3.5 * xi[:, 112]
     assert np.array_equal(bits(y), bits(want))
-    assert_close(y, oracle.decode_q4_0(w, n, k), x, "eights")
+    xn = synth.normal_f32(g, (m, k))
+    y = host(lib.qgemv_q4_0(dw, dev(xn), n, k))
+    rest = [i for i in range(n) if i != 5]
+    assert np.array_equal(bits(y[:, rest]), bits(np.zeros((m, n - 1), np.float32)))
+    assert_close(y, oracle.decode_q4_0(w, n, k), xn, "eights")
 
 
 def test_xr_non_finite_x_stays_in_its_row(lib):
@@ -114,3 +118,55 @@ def test_xr_non_finite_x_stays_in_its_row(lib):
     assert np.all(np.isfinite(y[finite]))
     assert_close(y[finite], oracle.decode_q4_0(w, n, k), x[finite], "finite rows")
     assert not np.any(np.isfinite(y[4]))
+
+
+# ------------------------------------------------------------------ Q4_K
+Q4K_CASES = [(3, 1, 512), (4, 17, 1024), (8, 33, 2048), (5, 100, 3072), (8, 300, 4096), (9, 40, 4096),
+             (16, 15, 1024), (7, 1000, 4096), (4, 20, 4352), (3, 9, 8192), (6, 30, 256)]
+
+
+@pytest.mark.parametrize("m,n,k", Q4K_CASES)
+def test_q4_k_xr_against_oracle_and_fma_path(lib, m, n, k):
+    w, x = synth.q4_k_case(9900 + m + n, m, n, k)
+    dw, dx = dev(w), dev(x)
+    y = host(lib.qgemv_q4_k(dw, dx, n, k))
+    w64 = oracle.decode_q4_k(w, n, k)
+    assert_close(y, w64, x, f"q4_k xr m{m} n{n} k{k}")
+    y_fma = with_env("0", lambda: host(lib.qgemv_q4_k(dw, dx, n, k)))
+    assert_close(y_fma, w64, x, "fma path")
+    assert np.array_equal(bits(y), bits(host(lib.qgemv_q4_k(dw, dx, n, k))))
+
+
+@pytest.mark.parametrize("m,ns,k", [(3, (7, 1, 40), 1024), (8, (64, 64), 2048), (5, (33,) * 8, 512),
+                                    (4, (4096, 1024, 1024), 4096)])
+def test_q4_k_multi_xr_bitwise_equals_singles(lib, m, ns, k):
+    ws, x = synth.q4_k_multi_case(10000 + m + k, m, ns, k)
+    dws, dx = [dev(w) for w in ws], dev(x)
+    y = host(lib.qgemv_q4_k_multi(dws, dx, list(ns), k))
+    col = 0
+    for w, dw, n in zip(ws, dws, ns):
+        assert np.array_equal(bits(y[:, col:col + n]), bits(host(lib.qgemv_q4_k(dw, dx, n, k)))), col
+        assert_close(y[:, col:col + n], oracle.decode_q4_k(w, n, k), x, f"multi xr col {col}")
+        col += n
+
+
+def test_q4_k_xr_hand_super_block_exact(lib):
+    """The hand-worked super-block (d = 1, dmin = 0.5, scale bytes 0xC1 at 0,
+    0x42 at 4, 0x23 at 8; code bytes 0x52 at 0, 0x07 at 64) in the first of two
+    super-blocks, a zero super-block in the second, at 4 rows of integer x: the
+    products are exact, so the result equals the oracle's bit for bit; with
+    x = ones it is the worked value."""
+    import json
+    from conftest import GOLDEN
+    fx = json.load(open(os.path.join(GOLDEN, "q4_k_hand_block.json")))
+    hand = np.frombuffer(bytes.fromhex(fx["bytes_hex"]), dtype=np.uint8)
+    row = np.concatenate([hand, np.zeros(144, np.uint8)])
+    w = np.stack([row, np.zeros_like(row), row]).reshape(-1)
+    n, k = 3, 512
+    g = np.random.default_rng(10100)
+    x = g.integers(-4, 5, size=(4, k)).astype(np.float32)
+    x[0] = 1.0
+    y = host(lib.qgemv_q4_k(dev(w), dev(x), n, k))
+    want = (x.astype(np.float64) @ oracle.decode_q4_k(w, n, k).T).astype(np.float32)
+    assert np.array_equal(bits(y), bits(want))
+    assert list(y[0]) == [fx["y_ones"], 0.0, fx["y_ones"]]
