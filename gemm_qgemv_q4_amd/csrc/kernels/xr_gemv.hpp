@@ -102,7 +102,7 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p)
   };
   constexpr int PIECES = 16 * 18;
   constexpr int LOADS = (PIECES + kWave - 1) / kWave;  // 5
-  u32x4 ga[LOADS], gb[LOADS];  // two row groups in flight
+  u32x4 ga[LOADS];  // the next row group in flight
   auto fetch = [&](u32x4 (&gq)[LOADS], int tile) {
     const GemvPart& pt = part_of(tile);
 #pragma unroll
@@ -129,12 +129,12 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p)
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
-  // Row groups t and t + G (G workgroups) are loaded first; group t + 2G leaves
-  // when group t has been copied to LDS.  Past the last group the loads repeat
-  // a group of this workgroup and are not used.
+  // Row group t is loaded first; group t + G (G workgroups) leaves when group
+  // t has been copied to LDS.  Past the last group the loads repeat a group of
+  // this workgroup and are not used.  (Two groups in flight measured 4-8%
+  // slower.)
   const int G = (int)gridDim.x;
   fetch(ga, t);
-  fetch(gb, t + G < p.n_groups ? t + G : t);
   // the weight loads leave before the x arithmetic below, behind the x loads only
   __builtin_amdgcn_sched_barrier(0);
 
@@ -166,12 +166,12 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p)
     }
   }
 
-  // One row group from buffer gq: copy it to LDS, send the loads of the group
-  // two ahead into gq, multiply, add the wave partials.
+  // One row group from buffer gq: copy it to LDS, send the loads of the next
+  // group into gq, multiply, add the wave partials.
   int it = 0;
   auto tile = [&](u32x4 (&gq)[LOADS]) {
     stage(gq);
-    const int t2 = t + 2 * G;
+    const int t2 = t + G;
     fetch(gq, t2 < p.n_groups ? t2 : t);
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     const uint8_t* rl = wl + kRowLds * r;
@@ -270,16 +270,8 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p)
     ++it;
     t += G;
   };
-  // The first two groups are peeled off the loop: in straight-line code the
-  // compiler waits for each group's own loads, at the loop head for all.
   tile(ga);
-  if (t >= p.n_groups) return;
-  tile(gb);
-  while (t < p.n_groups) {
-    tile(ga);
-    if (t >= p.n_groups) break;
-    tile(gb);
-  }
+  while (t < p.n_groups) tile(ga);
 }
 
 }  // namespace qg
