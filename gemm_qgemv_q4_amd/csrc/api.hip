@@ -430,11 +430,12 @@ hipError_t launch_gemv_mma(int np, const GemvParams& p, dim3 grid, hipStream_t s
   }
 }
 
-// Q4_0 and Q4_K from 3 rows of x on the matrix cores with x held in
-// registers (gemv_xr_kernel): K a multiple of 512 up to 4096 (one wave per
-// 512 columns), weights 16-byte aligned.  Every weight stream of the part list
+// Q4_0, Q4_K and the affine formats (group size >= 64) from 3 rows of x on
+// the matrix cores with x held in registers (gemv_xr_kernel): K a multiple of
+// 512 up to 4096 (one wave per 512 columns), weights 16-byte aligned.  Every weight stream of the part list
 // (both of a dual product) becomes one part of the launch.
-bool xr_ok(const HostPart* parts, int nparts, int nw, int64_t m, int64_t k) {
+template <int FMT>
+bool xr_ok(const HostPart* parts, int nparts, int nw, int64_t m, int64_t k, int64_t gs) {
   // tuning override (different rounding, same tolerance): QG_GEMV_XR=0 keeps the FMA kernels,
   // QG_GEMV_XR=M takes this kernel from M rows of x on
   // Measured (graph replay, K = 4096): at 2 rows the K-sliced FMA kernel is
@@ -446,6 +447,7 @@ bool xr_ok(const HostPart* parts, int nparts, int nw, int64_t m, int64_t k) {
     if (atoi(env) > 0) min_m = atoi(env);
   }
   if (m < min_m || k % 512 != 0 || k > 512 * kXrMaxWaves) return false;
+  if ((FMT == FMT_AFF || FMT == FMT_AFF4) && gs < 64) return false;
   if (nparts * nw > kMaxParts) return false;
   for (int pi = 0; pi < nparts; ++pi)
     for (int st = 0; st < nw; ++st)
@@ -455,7 +457,7 @@ bool xr_ok(const HostPart* parts, int nparts, int nw, int64_t m, int64_t k) {
 
 template <int FMT>
 qg_status run_gemv_xr(const char* op, const HostPart* parts, int nparts, int nw, const float* x, int64_t m,
-                      int64_t k, hipStream_t s) {
+                      int64_t k, int gs, hipStream_t s) {
   GemvParams p{};
   int64_t groups = 0;
   int np = 0;
@@ -464,6 +466,8 @@ qg_status run_gemv_xr(const char* op, const HostPart* parts, int nparts, int nw,
       GemvPart& gp = p.part[np++];
       gp.w[0] = gp.w[1] = static_cast<const uint8_t*>(parts[pi].w[st]);
       gp.y[0] = gp.y[1] = parts[pi].y[st];
+      gp.scales = parts[pi].scales;
+      gp.biases = parts[pi].biases;
       gp.ldy = parts[pi].ldy;
       gp.n = (int)parts[pi].n;
       gp.group0 = (int)groups;
@@ -474,6 +478,7 @@ qg_status run_gemv_xr(const char* op, const HostPart* parts, int nparts, int nw,
   p.n_groups = (int)groups;
   p.row_bytes = row_bytes_of<FMT>(k);
   p.k = (int)k;
+  p.gs = gs;
   // x of a workgroup lives in its waves' registers: one workgroup per CU for
   // K = 4096, more for shorter rows
   const int waves = (int)(k / 512);
@@ -524,9 +529,7 @@ qg_status run_gemv(const char* op, const HostPart* parts, int nparts, const floa
     }
     return launch_status(op);
   }
-  if constexpr (FMT == FMT_Q40 || FMT == FMT_Q4K) {
-    if (xr_ok(parts, nparts, NW, m, k)) return run_gemv_xr<FMT>(op, parts, nparts, NW, x, m, k, s);
-  }
+  if (xr_ok<FMT>(parts, nparts, NW, m, k, gs)) return run_gemv_xr<FMT>(op, parts, nparts, NW, x, m, k, gs, s);
   const GemvPlan pl = plan_gemv<FMT>(m, k, NW);
   const int mma = NW == 1 ? mma_pairs<FMT>(parts, nparts, m, k, gs) : 0;
   const int ks = mma ? 0 : ks_chunks<FMT, NW>(pl, m, k);

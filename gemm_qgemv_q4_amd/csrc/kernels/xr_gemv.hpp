@@ -1,11 +1,13 @@
-// Q4_0 and Q4_K products at 3..8 rows of x on the gfx950 matrix cores, with
-// x held in registers for the whole launch.
+// Q4_0, Q4_K and affine-code products at 3..8 rows of x on the gfx950 matrix
+// cores, with x held in registers for the whole launch.
 //
 // Q4_0: y[m, n] = sum_b d[n, b] (P[m, n, b] - 8 X[m, b])      [GGML block_q4_0: w = d (q - 8)]
 // Q4_K: y[m, n] = sum_j (d sc_j)[n] P[m, n, j] - (dmin m_j)[n] X[m, j]
 //                                               [GGML block_q4_K: w = d sc_j q - dmin m_j]
-// with P = sum over a 32-weight block (Q4_0) or sub-block (Q4_K) of x q and X
-// the sum of x over it.
+// affine: y[m, n] = sum_b s[n, g(b)] P[m, n, b] + b[n, g(b)] X[m, b]
+//                                               [MLX affine groups: w = s q + b]
+// with P = sum over a 32-weight block (Q4_0, affine) or sub-block (Q4_K) of
+// x q and X the sum of x over it.
 //
 // Each 32-weight block is one v_mfma_f32_16x16x32_bf16 whose 16 columns are
 // 16 weight rows and whose 16 rows are x: rows 0..7 hold bf16(x) of the (up
@@ -37,7 +39,15 @@ namespace qg {
 constexpr int kXrNB = 16;        // 32-weight blocks per wave
 constexpr int kXrMaxWaves = 8;   // K <= 4096
 constexpr int kXrMaxM = 8;       // x rows per launch
-constexpr int kRowLds = 304;     // LDS bytes per weight row copy (288 used)
+
+// Bytes of one weight row in a wave's 512-column slice, and the LDS stride of
+// its copy (chosen so that the 16 rows x 4 K pieces of one MFMA operand read
+// fall in distinct banks or, for 8-byte reads, distinct banks per half wave).
+template <int FMT> struct XrRow;
+template <> struct XrRow<FMT_Q40> { static constexpr int bytes = 288, lds = 304; };
+template <> struct XrRow<FMT_Q4K> { static constexpr int bytes = 288, lds = 304; };
+template <> struct XrRow<FMT_AFF> { static constexpr int bytes = 512, lds = 544; };
+template <> struct XrRow<FMT_AFF4> { static constexpr int bytes = 256, lds = 272; };
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -60,11 +70,14 @@ __device__ __forceinline__ uint32_t dpp_row_ror8(uint32_t v) {
 
 template <int FMT, bool MULTI>
 __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p) {
-  static_assert(FMT == FMT_Q40 || FMT == FMT_Q4K, "4-bit block formats");
   constexpr bool K4 = FMT == FMT_Q4K;
+  constexpr bool AF = FMT == FMT_AFF || FMT == FMT_AFF4;
+  constexpr int SLICE = XrRow<FMT>::bytes;
+  constexpr int kRowLds = XrRow<FMT>::lds;
   constexpr int NB = kXrNB;
   __shared__ float red[2][kXrMaxWaves][16][16];  // [buffer][wave][MFMA row][column]
   __shared__ u32x4 wlds[kXrMaxWaves][16 * kRowLds / 16];  // per wave: 16 rows of kRowLds bytes
+  __shared__ float sbl[AF ? kXrMaxWaves : 1][2][16][8];   // affine: per wave, scale and bias of 16 rows x 8 groups
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x / kWave;
@@ -81,16 +94,17 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p)
   // piece's x values, lane r + 8 the last four; the two then trade halves.
   const int mx = r & 7;
   const bool live = mx < p.m_rows;
-  const int e0 = K4 ? 8 * kp + (lo_row ? 4 : 0) : 4 * kp + (lo_row ? 16 : 0);
+  const int e0 = FMT == FMT_Q40 ? 4 * kp + (lo_row ? 16 : 0) : 8 * kp + (lo_row ? 4 : 0);
   const float* xp = p.x + (size_t)(live ? mx : 0) * p.k + 32 * kb0 + e0;
   f32x4 xv[NB];
 #pragma unroll
   for (int s = 0; s < NB; ++s) xv[s] = *reinterpret_cast<const f32x4a4*>(xp + 32 * s);
 
-  // ---- weight loads of one row group: 16 rows x 288 bytes as 288 pieces of
-  // 16 bytes (piece i: row i / 18, bytes 16 (i % 18) of the wave's slice);
-  // lane l loads pieces l + 64 j (past piece 287: piece 287 again).  Rows are whole multiples of 288 bytes, so every piece is
-  // 16-byte aligned when the weights are.
+  // ---- weight loads of one row group: 16 rows x SLICE bytes (288 for the
+  // block formats) as pieces of 16 bytes (piece i: row i / (SLICE / 16), bytes
+  // 16 (i % (SLICE / 16)) of the wave's slice); lane l loads pieces l + 64 j
+  // (past the last piece: the last one again).  Rows are whole multiples of
+  // SLICE bytes, so every piece is 16-byte aligned when the weights are.
   auto part_of = [&](int tile) -> const GemvPart& {
     int pi = 0;
     if constexpr (MULTI) {
@@ -100,17 +114,35 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p)
     }
     return p.part[pi];
   };
-  constexpr int PIECES = 16 * 18;
-  constexpr int LOADS = (PIECES + kWave - 1) / kWave;  // 5
+  constexpr int PPR = SLICE / 16;  // pieces per row
+  constexpr int PIECES = 16 * PPR;
+  constexpr int LOADS = (PIECES + kWave - 1) / kWave;  // 5, 8 (u8 codes) or 4 (packed)
+  // affine: scale and bias of group g of row i / 8, g = i % 8 (groups past the
+  // wave's last one repeat it)
+  const int gsh = AF ? __builtin_ctz((unsigned)p.gs) : 0;
+  const int wgroups = AF ? (p.gs >= 512 ? 1 : 512 >> gsh) : 0;
+  const int g0 = AF ? (512 * wv) >> gsh : 0;
   u32x4 ga[LOADS];  // the next row group in flight
+  float gsb[AF ? 4 : 1];  // affine: its scales or biases
   auto fetch = [&](u32x4 (&gq)[LOADS], int tile) {
     const GemvPart& pt = part_of(tile);
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
       const int i = lane + kWave * j < PIECES ? lane + kWave * j : PIECES - 1;
-      const int rr = (tile - pt.group0) * 16 + i / 18;
+      const int rr = (tile - pt.group0) * 16 + i / PPR;
       const int row = rr < pt.n ? rr : pt.n - 1;  // clamped for the loads; not stored
-      gq[j] = *reinterpret_cast<const u32x4*>(pt.w[0] + (size_t)row * (size_t)p.row_bytes + 288 * wv + 16 * (i % 18));
+      gq[j] = *reinterpret_cast<const u32x4*>(pt.w[0] + (size_t)row * (size_t)p.row_bytes + SLICE * wv + 16 * (i % PPR));
+    }
+    if constexpr (AF) {
+      // lanes 0..31 the scales, 32..63 the biases, 4 entries each
+      const int rr = (tile - pt.group0) * 16 + (lane & 31) / 2;
+      const int row = rr < pt.n ? rr : pt.n - 1;
+      const float* src = (lane < 32 ? pt.scales : pt.biases) + (size_t)row * (size_t)(p.k >> gsh) + g0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int g = 4 * (lane & 1) + e;
+        gsb[e] = src[g < wgroups ? g : wgroups - 1];
+      }
     }
   };
   // The wave's LDS copy: row n at byte kRowLds n (a stride of 76 dwords puts
@@ -121,7 +153,12 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p)
     for (int j = 0; j < LOADS; ++j) {
       // lanes past piece 287 loaded piece 287 again and write the same bytes there
       const int i = lane + kWave * j < PIECES ? lane + kWave * j : PIECES - 1;
-      *reinterpret_cast<u32x4*>(wl + kRowLds * (i / 18) + 16 * (i % 18)) = gq[j];
+      *reinterpret_cast<u32x4*>(wl + kRowLds * (i / PPR) + 16 * (i % PPR)) = gq[j];
+    }
+    if constexpr (AF) {
+      float* d = &sbl[wv][lane >> 5][(lane & 31) / 2][4 * (lane & 1)];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) d[e] = gsb[e];
     }
     // LDS operations of one wave complete in order; this only keeps the
     // compiler from moving the reads above the writes.
@@ -139,28 +176,37 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p)
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- A operands and block sums.  Row r < 8 takes bf16(x) of its K piece's
-  // 8 weights, row r + 8 takes bf16(x - bf16(x)) of the same.
+  // 8 weights, row r + 8 takes bf16(x - bf16(x)) of the same.  The block
+  // formats take the weights in order; affine codes take them as
+  // [0, 2, 4, 6, 1, 3, 5, 7], the order of the even and odd nibbles of a
+  // packed word (u8 codes use the same order, so both give the same bits).
   bf16x8 a[NB];
-  f32x4 xs[NB];  // Q4_0: -8 X, Q4_K: X, of this lane's MFMA rows 4kp .. 4kp+3
+  f32x4 xs[NB];  // Q4_0: -8 X, else X, of this lane's MFMA rows 4kp .. 4kp+3
   {
     // Q4_0: x times a column of -8 is exactly -8 times the block sum (a
     // power-of-two scale commutes with the rounding), so that P + xs is
     // exactly 0 for a block of codes 8
-    const float cs = K4 ? 1.0f : -8.0f;
+    const float cs = FMT == FMT_Q40 ? -8.0f : 1.0f;
     const bf16x8 m8 = {(__bf16)cs, (__bf16)cs, (__bf16)cs, (__bf16)cs,
                        (__bf16)cs, (__bf16)cs, (__bf16)cs, (__bf16)cs};
     const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int s = 0; s < NB; ++s) {
       const f32x4 v = live ? xv[s] : z;
-      const uint32_t h01 = pk_bf16(v.x, v.y), h23 = pk_bf16(v.z, v.w);
+      // pairs of this lane's four values: (0, 1), (2, 3), or (0, 2), (1, 3) for affine codes
+      const float u0 = v.x, u1 = AF ? v.z : v.y, u2 = AF ? v.y : v.z, u3 = v.w;
+      const uint32_t h01 = pk_bf16(u0, u1), h23 = pk_bf16(u2, u3);
       const float f0 = __builtin_bit_cast(float, h01 << 16), f1 = __builtin_bit_cast(float, h01 & 0xFFFF0000u);
       const float f2 = __builtin_bit_cast(float, h23 << 16), f3 = __builtin_bit_cast(float, h23 & 0xFFFF0000u);
-      const uint32_t l01 = pk_bf16(v.x - f0, v.y - f1), l23 = pk_bf16(v.z - f2, v.w - f3);
+      const uint32_t l01 = pk_bf16(u0 - f0, u1 - f1), l23 = pk_bf16(u2 - f2, u3 - f3);
       // lane r sends the remainders of its half to row r + 8, which sends its bf16(x) back
       const uint32_t r01 = dpp_row_ror8(lo_row ? h01 : l01);
       const uint32_t r23 = dpp_row_ror8(lo_row ? h23 : l23);
-      const u32x4 av = lo_row ? u32x4{r01, r23, l01, l23} : u32x4{h01, h23, r01, r23};
+      u32x4 av;
+      if constexpr (AF)  // [own, received] pairs interleaved: 0 2 | 4 6 | 1 3 | 5 7
+        av = lo_row ? u32x4{r01, l01, r23, l23} : u32x4{h01, r01, h23, r23};
+      else
+        av = lo_row ? u32x4{r01, r23, l01, l23} : u32x4{h01, h23, r01, r23};
       a[s] = __builtin_bit_cast(bf16x8, av);
       xs[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], m8, z, 0, 0, 0);
     }
@@ -180,7 +226,7 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p)
       const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
       return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], __builtin_bit_cast(bf16x8, bv), z, 0, 0, 0);
     };
-    if constexpr (!K4) {
+    if constexpr (FMT == FMT_Q40) {
       // Block s of row r sits at byte 18 s of the row's copy.  Even blocks start
       // 4-byte aligned: code bytes 4kp.. at 2 + 4kp, read as two dwords; odd
       // blocks have them in one dword.  The scale is the low (even) or high
@@ -213,7 +259,7 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p)
         P0 = P1;
         db0 = db1;
       }
-    } else {
+    } else if constexpr (K4) {
       // Super-block b (two per wave) of row r sits at byte 144 b of the row's
       // copy: d, dmin, 12 scale bytes, then 4 runs of 32 code bytes.  Sub-block
       // j takes the low (j even) or high nibbles of run j / 2; K piece kp is
@@ -250,6 +296,39 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p)
           }
           P0 = P1;
         }
+      }
+    } else {
+      // Affine codes: block s of row r is bytes 32 s (u8) or 16 s (packed) of
+      // the row's copy; K piece kp is its bytes 8kp .. 8kp + 7 (u8) or word kp
+      // (packed), taken in the order [0, 2, 4, 6, 1, 3, 5, 7].  The scale and
+      // bias of its group come from the staged table.
+      const float* sr = &sbl[wv][0][r][0];
+      const float* br = &sbl[wv][1][r][0];
+      auto product = [&](int s) -> f32x4 {
+        if constexpr (FMT == FMT_AFF) {
+          const uint2 v = *reinterpret_cast<const uint2*>(rl + 32 * s + 8 * kp);
+          const u32x4 bv = {pk_bf16(ubyte_f32<0>(v.x), ubyte_f32<2>(v.x)), pk_bf16(ubyte_f32<0>(v.y), ubyte_f32<2>(v.y)),
+                            pk_bf16(ubyte_f32<1>(v.x), ubyte_f32<3>(v.x)), pk_bf16(ubyte_f32<1>(v.y), ubyte_f32<3>(v.y))};
+          const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+          return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], __builtin_bit_cast(bf16x8, bv), z, 0, 0, 0);
+        } else {
+          const uint32_t v = *reinterpret_cast<const uint32_t*>(rl + 16 * s + 4 * kp);
+          return mfma(s, v & 0x0F0F0F0Fu, (v >> 4) & 0x0F0F0F0Fu);
+        }
+      };
+      f32x4 P0 = product(0);
+#pragma unroll
+      for (int s = 0; s < NB; ++s) {
+        f32x4 P1 = P0;
+        if (s + 1 < NB) P1 = product(s + 1);
+        const int gi = (32 * s) >> gsh;  // group of block s among the wave's groups
+        const float sc = sr[gi], bi = br[gi];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[i] = __builtin_fmaf(sc, P0[i], acc[i]);
+          acc[i] = __builtin_fmaf(bi, xs[s][i], acc[i]);
+        }
+        P0 = P1;
       }
     }
     // acc[i]: MFMA row 4 kp + i (x row (4kp+i) & 7, high or low part) for weight row r of the group

@@ -17,6 +17,14 @@ from test_gpu_parity import assert_close, dev, host
 pytestmark = pytest.mark.gpu
 
 
+@pytest.fixture(autouse=True)
+def _no_xr(monkeypatch):
+    """From 3 rows of x the x-resident matrix-core GEMV takes these products;
+    it is switched off here so that this kernel is the one tested at every M
+    (tests/test_gpu_xr.py covers the other)."""
+    monkeypatch.setenv("QG_GEMV_XR", "0")
+
+
 def bits(a):
     return np.ascontiguousarray(a).view(np.uint32)
 

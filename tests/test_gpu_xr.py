@@ -1,9 +1,11 @@
-"""The matrix-core Q4_0 / Q4_K GEMV with x in registers (from 3 rows of x, up
-to 8 per launch, K a multiple of 512 up to 4096) against the f64 oracle, and
-its stated equalities: the dual Q4_0 and the multi-part Q4_K products bitwise
-equal to single calls, each row of x independent of the others, Q4_0 blocks of
-codes 8 giving exactly zero, the hand-worked Q4_K super-block exactly.  The tuning
-switch QG_GEMV_XR=0 selects the FMA kernels, whose results must agree within
+"""The matrix-core GEMV with x in registers (Q4_0, Q4_K and affine codes with
+group size >= 64; from 3 rows of x, up to 8 per launch, K a multiple of 512 up
+to 4096) against the f64 oracle, and its stated equalities: the dual Q4_0 and
+the multi-part Q4_K products bitwise equal to single calls, packed affine codes
+bitwise equal to u8 codes, the fused q|k|v product bitwise equal to the
+product then the split, each row of x independent of the others, Q4_0 blocks
+of codes 8 giving exactly zero, the hand-worked Q4_K super-block exactly.  The tuning
+switch QG_GEMV_XR=0 selects the other kernels, whose results must agree within
 the same tolerance.  Shapes outside that range (K = 4160, 8192, 256) take the
 FMA kernels and are checked the same way."""
 import os
@@ -170,3 +172,45 @@ def test_q4_k_xr_hand_super_block_exact(lib):
     want = (x.astype(np.float64) @ oracle.decode_q4_k(w, n, k).T).astype(np.float32)
     assert np.array_equal(bits(y), bits(want))
     assert list(y[0]) == [fx["y_ones"], 0.0, fx["y_ones"]]
+
+
+# ------------------------------------------------------------------ affine codes
+AFF_CASES = [(3, 1, 512, 64, 15), (4, 17, 1024, 512, 255), (8, 33, 2048, 128, 15), (5, 100, 3072, 1024, 255),
+             (8, 300, 4096, 64, 15), (9, 40, 4096, 256, 255), (16, 15, 1024, 64, 15), (7, 600, 4096, 64, 255),
+             (4, 20, 1024, 32, 255), (3, 9, 8192, 64, 15), (6, 30, 1536, 64, 15)]
+
+
+@pytest.mark.parametrize("m,n,k,gs,code_max", AFF_CASES)
+def test_affine_xr_against_oracle_and_other_path(lib, m, n, k, gs, code_max):
+    x, q, s, b = synth.affine_case(10200 + m + n, m, n, k, gs, code_max)
+    dx, dq, ds, db = dev(x), dev(q), dev(s), dev(b)
+    y = host(lib.qmm_affine_t(dx, dq, ds, db, gs))
+    w64 = oracle.decode_affine(q, s, b, n, k, gs)
+    assert_close(y, w64, x, f"affine xr m{m} n{n} k{k} gs{gs}")
+    y_other = with_env("0", lambda: host(lib.qmm_affine_t(dx, dq, ds, db, gs)))
+    assert_close(y_other, w64, x, "other path")
+    assert np.array_equal(bits(y), bits(host(lib.qmm_affine_t(dx, dq, ds, db, gs))))
+
+
+@pytest.mark.parametrize("m,n,k,gs", [(3, 29, 512, 64), (8, 64, 4096, 64), (6, 31, 2048, 128), (12, 5, 1024, 1024)])
+def test_packed_xr_bitwise_equals_u8(lib, m, n, k, gs):
+    import torch
+    x, q, s, b = synth.affine_case(10300 + m + n, m, n, k, gs)
+    wp = torch.from_numpy(synth.pack_b4_u32(q).view(np.int32)).cuda()
+    dx, ds, db = dev(x), dev(s), dev(b)
+    y = host(lib.qmm_affine_t_packed(dx, wp, ds, db, gs))
+    assert np.array_equal(bits(y), bits(host(lib.qmm_affine_t(dx, dev(q), ds, db, gs))))
+    assert_close(y, oracle.decode_affine(q, s, b, n, k, gs), x, f"packed xr m{m}")
+
+
+@pytest.mark.parametrize("m", [3, 8, 11])
+def test_fused_qkv_xr_bitwise_equals_product_then_split(lib, m):
+    k, gs, qs, ks, vs = 1024, 64, 96, 40, 17
+    n = qs + ks + vs
+    x, q, s, b = synth.affine_case(10400 + m, m, n, k, gs)
+    dx, dq, ds, db = dev(x), dev(q), dev(s), dev(b)
+    got = [host(t) for t in lib.qmm_affine_t_qkv(dx, dq, ds, db, gs, qs, ks, vs)]
+    y = lib.qmm_affine_t(dx, dq, ds, db, gs)
+    for a, r in zip(got, lib.qkv_split_f32(y, m, qs, ks, vs)):
+        assert np.array_equal(bits(a), bits(host(r)))
+    assert_close(np.concatenate(got, axis=1), oracle.decode_affine(q, s, b, n, k, gs), x, f"fused qkv xr m{m}")
