@@ -41,9 +41,11 @@
  *    affine formats with group_size >= 64, K a multiple of 512 with K/512 in
  *    {1, 2, 4, 8} and codes aligned (16 bytes for u8, 8 for packed) run on
  *    the matrix cores in launches of up to 8 rows of x, with x split the
- *    same way and no scratch; so do Q4_0 and Q4_K for 3 <= M below that
- *    threshold with K a multiple of 512 up to 4096 and the weights 16-byte
- *    aligned.  The same tolerance and equalities hold.
+ *    same way and no scratch; from 3 <= M below that threshold Q4_0, Q4_K
+ *    and the affine formats (group_size >= 64) with K a multiple of 512 up
+ *    to 4096 and the weights 16-byte aligned run on the matrix cores with x
+ *    held in registers, also without scratch.  The same tolerance and
+ *    equalities hold.
  */
 #ifndef QGEMV_Q4_H
 #define QGEMV_Q4_H
