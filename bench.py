@@ -45,7 +45,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q4_k_gemv_4096_traffic.json")
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for rel in ("gemm_qgemv_q4_amd/csrc/kernels/gemv.hpp", "gemm_qgemv_q4_amd/csrc/kernels/common.hpp"):
+    for rel in ("gemm_qgemv_q4_amd/csrc/kernels/gemv.hpp", "gemm_qgemv_q4_amd/csrc/kernels/common.hpp",
+                "gemm_qgemv_q4_amd/csrc/api.hip"):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

@@ -120,7 +120,11 @@ GemvPlan plan_gemv(int64_t m, int64_t k, int nw) {
   GemvPlan pl{};
   const int64_t chunks = k / CH;
   pl.mt = m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : 8;
-  pl.l = Q4 ? 32 : (chunks >= 64 ? 64 : 32);
+  // Q4 formats: 32 lanes per row, except one x row with 64 to 256 chunks per
+  // row (K = 4096 .. 16384), where the K-sliced kernel takes 64 lanes and 8
+  // waves (one or more chunks for every lane): Q4_K 4096 x 4096 4.72 -> 4.50
+  // us, dual Q4_0 6.7 -> 6.2 us, multi-part q|k|v 6.7 -> 6.3 us.
+  pl.l = Q4 ? (pl.mt == 1 && chunks >= 64 && chunks <= 256 ? 64 : 32) : (chunks >= 64 ? 64 : 32);
   int r = 1;
   if (!Q4 && chunks >= 64 && (pl.mt * nw <= 2 || (nw == 1 && pl.mt == 8))) r = 2;
   auto lds_for = [&](int64_t kt) {
@@ -310,10 +314,13 @@ size_t ks_lds(int mt, int nw, int l, int r, int j, int wv) {
 // 8 waves are faster (2.35 vs 2.48 us).  Tuning override QG_GEMV_KS_WAVES=4|8
 // for the Q4 formats (same results either way).
 template <int FMT>
-int ks_waves(int64_t k) {
+int ks_waves(int64_t k, int l) {
   if constexpr (FMT != FMT_Q40 && FMT != FMT_Q4K) {
     return 8;
   } else {
+    // 64 lanes per row: always 8 waves (8 virtual lanes per wave and row; the
+    // kernel's butterfly across waves is not written for 16)
+    if (l == 64) return 8;
     if (const char* env = getenv("QG_GEMV_KS_WAVES")) {
       const int w = atoi(env);
       if (w == 4 || w == 8) return w;
@@ -325,7 +332,8 @@ int ks_waves(int64_t k) {
 // Chunks per lane the K-sliced kernel takes for this call (0: not eligible):
 // x in LDS for the whole K and the chunked kernel's shape (L, R) = (32, 1)
 // for the 64-weight chunks of Q4_0/Q4_K (one or two weight streams; one x row,
-// or tiles of 2 or 4 rows where 4 waves are used) or (64, 2) for the 32-code
+// or tiles of 2 or 4 rows where 4 waves are used), (64, 1) for them at one x
+// row with 64..256 chunks per row (8 waves), or (64, 2) for the 32-code
 // chunks of the affine formats (one x row).
 template <int FMT, int NW>
 int ks_chunks(const GemvPlan& pl, int64_t m, int64_t k) {
@@ -337,8 +345,8 @@ int ks_chunks(const GemvPlan& pl, int64_t m, int64_t k) {
   // tiles of 2 or 4 rows of x: the dual Q4_0 product at M = 4 takes 11.0 us
   // here against 14.1 us on the chunked kernel; at 8 rows (22.1 vs 18.5 us)
   // the chunked kernel stays
-  if (pl.mt > 1 && !(Q4 && pl.mt <= 4 && ks_waves<FMT>(k) == 4)) return 0;
-  if (Q4 ? !(pl.l == 32 && pl.r == 1) : !(pl.l == 64 && pl.r == 2)) return 0;
+  if (pl.mt > 1 && !(Q4 && pl.l == 32 && pl.mt <= 4 && ks_waves<FMT>(k, pl.l) == 4)) return 0;
+  if (Q4 ? !((pl.l == 32 || (pl.l == 64 && pl.mt == 1)) && pl.r == 1) : !(pl.l == 64 && pl.r == 2)) return 0;
   const int64_t j = cdiv(k / FmtTraits<FMT>::CH, pl.l);
   (void)m;
   return j >= 1 && j <= 4 ? (int)j : 0;
@@ -359,8 +367,9 @@ hipError_t launch_gemv_ks_lr(int j, const GemvParams& p, dim3 grid, hipStream_t 
 template <int FMT, int NW>
 hipError_t launch_gemv_ks(const GemvPlan& pl, int j, const GemvParams& p, dim3 grid, hipStream_t s) {
   if constexpr (FMT == FMT_Q40 || FMT == FMT_Q4K) {
+    if (pl.l == 64 && pl.r == 1 && pl.mt == 1) return launch_gemv_ks_lr<FMT, 1, NW, 64, 1, 8>(j, p, grid, s);
     if (!(pl.l == 32 && pl.r == 1)) return hipErrorInvalidValue;
-    const bool four = ks_waves<FMT>(p.k) == 4;
+    const bool four = ks_waves<FMT>(p.k, pl.l) == 4;
     switch (pl.mt) {
       case 1: return four ? launch_gemv_ks_lr<FMT, 1, NW, 32, 1, 4>(j, p, grid, s)
                           : launch_gemv_ks_lr<FMT, 1, NW, 32, 1, 8>(j, p, grid, s);
@@ -534,7 +543,7 @@ qg_status run_gemv(const char* op, const HostPart* parts, int nparts, const floa
   const int mma = NW == 1 ? mma_pairs<FMT>(parts, nparts, m, k, gs) : 0;
   const int ks = mma ? 0 : ks_chunks<FMT, NW>(pl, m, k);
   const GemvGrid gg = grid_gemv<FMT>(pl, parts, nparts);
-  const int ks_wv = ks ? ks_waves<FMT>(k) : 0;
+  const int ks_wv = ks ? ks_waves<FMT>(k, pl.l) : 0;
   const int rows_per_group = mma ? 16 : ks ? (int)(kWave / (pl.l / ks_wv) * pl.r) : (int)gg.groups_rows;
   GemvParams p{};
   int64_t groups = 0;
