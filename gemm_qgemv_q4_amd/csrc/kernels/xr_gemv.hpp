@@ -41,13 +41,14 @@ constexpr int kXrMaxWaves = 8;   // K <= 4096
 constexpr int kXrMaxM = 8;       // x rows per launch
 
 // Bytes of one weight row in a wave's 512-column slice, and the LDS stride of
-// its copy (chosen so that the 16 rows x 4 K pieces of one MFMA operand read
-// fall in distinct banks or, for 8-byte reads, distinct banks per half wave).
+// its copy: a stride of 2 mod 32 dwords puts the 16 rows of one MFMA operand
+// read (one or two dwords per lane) in distinct banks for every 16 or 32
+// lanes that the LDS serves together.
 template <int FMT> struct XrRow;
-template <> struct XrRow<FMT_Q40> { static constexpr int bytes = 288, lds = 304; };
-template <> struct XrRow<FMT_Q4K> { static constexpr int bytes = 288, lds = 304; };
-template <> struct XrRow<FMT_AFF> { static constexpr int bytes = 512, lds = 544; };
-template <> struct XrRow<FMT_AFF4> { static constexpr int bytes = 256, lds = 272; };
+template <> struct XrRow<FMT_Q40> { static constexpr int bytes = 288, lds = 392; };
+template <> struct XrRow<FMT_Q4K> { static constexpr int bytes = 288, lds = 392; };
+template <> struct XrRow<FMT_AFF> { static constexpr int bytes = 512, lds = 520; };
+template <> struct XrRow<FMT_AFF4> { static constexpr int bytes = 256, lds = 264; };
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -145,15 +146,17 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p)
       }
     }
   };
-  // The wave's LDS copy: row n at byte kRowLds n (a stride of 76 dwords puts
-  // the 16 rows x 4 pieces of one MFMA operand read in 64 distinct banks).
+  // The wave's LDS copy: row n at byte kRowLds n (stride chosen in XrRow).
   uint8_t* wl = reinterpret_cast<uint8_t*>(&wlds[wv][0]);
   auto stage = [&](const u32x4 (&gq)[LOADS]) {
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
       // lanes past piece 287 loaded piece 287 again and write the same bytes there
       const int i = lane + kWave * j < PIECES ? lane + kWave * j : PIECES - 1;
-      *reinterpret_cast<u32x4*>(wl + kRowLds * (i / PPR) + 16 * (i % PPR)) = gq[j];
+      // rows start 8-byte aligned (the stride is not a multiple of 16): two 8-byte writes
+      uint2* d = reinterpret_cast<uint2*>(wl + kRowLds * (i / PPR) + 16 * (i % PPR));
+      d[0] = uint2{gq[j][0], gq[j][1]};
+      d[1] = uint2{gq[j][2], gq[j][3]};
     }
     if constexpr (AF) {
       float* d = &sbl[wv][lane >> 5][(lane & 31) / 2][4 * (lane & 1)];
@@ -267,7 +270,8 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p)
 #pragma unroll
       for (int b = 0; b < NB / 8; ++b) {
         const uint8_t* sb = rl + 144 * b;
-        const u32x4 hd = *reinterpret_cast<const u32x4*>(sb);
+        const uint2 h0 = *reinterpret_cast<const uint2*>(sb), h1 = *reinterpret_cast<const uint2*>(sb + 8);
+        const u32x4 hd = {h0.x, h0.y, h1.x, h1.y};
         const float d = f16_bits_to_f32(hd[0]), dmin = f16_bits_to_f32(hd[0] >> 16);
         // 6-bit scales and mins of sub-blocks 0..3 and 4..7, one per byte
         const uint32_t sc03 = hd[1] & 0x3F3F3F3Fu, mn03 = hd[2] & 0x3F3F3F3Fu;
