@@ -14,20 +14,20 @@
 // to) 8 rows of x, rows 8..15 hold bf16(x - bf16(x)).  Both halves of x thus
 // ride in one MFMA, and the output's two partial sums are added at the end
 // (x carries 16 significant bits, relative error <= 2^-18 per element; the
-// codes 0..15 are exact in bf16 and the products exact in the f32
-// accumulator).  The block sums of x come from the same MFMA unit (x times a
-// column of -8 for Q4_0, of ones for Q4_K), so that a Q4_0 block of codes 8
-// gives exactly P - 8 X = 0.
+// codes, 0..15 or 0..255 for u8, are exact in bf16 and the products exact in
+// the f32 accumulator).  The block sums of x come from the same MFMA unit (x
+// times a column of -8 for Q4_0, of ones otherwise), so that a Q4_0 block of
+// codes 8 gives exactly P - 8 X = 0.
 //
 // Work split: a workgroup of K/512 waves owns 16 weight rows at a time; wave
 // w owns columns 512 w .. 512 w + 511, i.e. NB = 16 blocks (288 bytes of each
-// row).  The wave keeps its slice of x as 16 MFMA A operands (64 VGPRs) and
+// row for the block formats, 512 for u8 and 256 for packed codes).  The wave keeps its slice of x as 16 MFMA A operands (64 VGPRs) and
 // the block sums (64 VGPRs) for the whole launch, so after the first load x
 // costs no memory or LDS traffic.  The MFMA wants, in lane l, 4 code bytes of
 // weight row l % 16; loads that narrow touch 16 rows per instruction and
-// stream poorly, so the wave reads its 16 x 288 bytes with 16-byte loads
-// along the rows (18 lanes per row), writes them to its own LDS region and
-// reads the MFMA operands from there.  The loads of the next row group leave
+// stream poorly, so the wave reads its 16 rows with 16-byte loads along the
+// rows (18 lanes per row for the block formats), writes them to its own LDS
+// region and reads the MFMA operands from there.  The loads of the next row group leave
 // before the arithmetic on the current one.  The wave partials of an output
 // are added in a fixed order through LDS, one barrier per row group.
 #pragma once
