@@ -127,6 +127,10 @@ GemvPlan plan_gemv(int64_t m, int64_t k, int nw) {
   pl.l = Q4 ? (pl.mt == 1 && chunks >= 64 && chunks <= 256 ? 64 : 32) : (chunks >= 64 ? 64 : 32);
   int r = 1;
   if (!Q4 && chunks >= 64 && (pl.mt * nw <= 2 || (nw == 1 && pl.mt == 8))) r = 2;
+  // affine codes at one x row with 64 to 256 chunks per row (K = 2048 .. 8192):
+  // one row per lane on the K-sliced kernel (12288 x 4096 gs 64: u8 12.7 ->
+  // 12.1 us, packed 8.9 -> 8.6 us against two rows per lane)
+  if (!Q4 && pl.mt == 1 && chunks >= 64 && chunks <= 256) r = 1;
   auto lds_for = [&](int64_t kt) {
     const int64_t ct = kt / CH;
     return (size_t)(pl.mt * (CH / 4) * (ct + 1) * 16 + (SUMS ? pl.mt * ct * 8 : 0));
@@ -333,8 +337,8 @@ int ks_waves(int64_t k, int l) {
 // x in LDS for the whole K and the chunked kernel's shape (L, R) = (32, 1)
 // for the 64-weight chunks of Q4_0/Q4_K (one or two weight streams; one x row,
 // or tiles of 2 or 4 rows where 4 waves are used), (64, 1) for them at one x
-// row with 64..256 chunks per row (8 waves), or (64, 2) for the 32-code
-// chunks of the affine formats (one x row).
+// row with 64..256 chunks per row (8 waves), or (64, 1) / (64, 2) for the
+// 32-code chunks of the affine formats (one x row).
 template <int FMT, int NW>
 int ks_chunks(const GemvPlan& pl, int64_t m, int64_t k) {
   // tuning override (same results either way): QG_GEMV_KS=0 keeps the chunked kernel
@@ -346,7 +350,8 @@ int ks_chunks(const GemvPlan& pl, int64_t m, int64_t k) {
   // here against 14.1 us on the chunked kernel; at 8 rows (22.1 vs 18.5 us)
   // the chunked kernel stays
   if (pl.mt > 1 && !(Q4 && pl.l == 32 && pl.mt <= 4 && ks_waves<FMT>(k, pl.l) == 4)) return 0;
-  if (Q4 ? !((pl.l == 32 || (pl.l == 64 && pl.mt == 1)) && pl.r == 1) : !(pl.l == 64 && pl.r == 2)) return 0;
+  if (Q4 ? !((pl.l == 32 || (pl.l == 64 && pl.mt == 1)) && pl.r == 1) : !(pl.l == 64 && (pl.r == 1 || pl.r == 2)))
+    return 0;
   const int64_t j = cdiv(k / FmtTraits<FMT>::CH, pl.l);
   (void)m;
   return j >= 1 && j <= 4 ? (int)j : 0;
@@ -378,8 +383,9 @@ hipError_t launch_gemv_ks(const GemvPlan& pl, int j, const GemvParams& p, dim3 g
     }
     return hipErrorInvalidValue;
   } else if constexpr (NW == 1) {
-    return pl.l == 64 && pl.r == 2 && pl.mt == 1 ? launch_gemv_ks_lr<FMT, 1, NW, 64, 2, 8>(j, p, grid, s)
-                                                 : hipErrorInvalidValue;
+    if (pl.l != 64 || pl.mt != 1) return hipErrorInvalidValue;
+    return pl.r == 1 ? launch_gemv_ks_lr<FMT, 1, NW, 64, 1, 8>(j, p, grid, s)
+                     : pl.r == 2 ? launch_gemv_ks_lr<FMT, 1, NW, 64, 2, 8>(j, p, grid, s) : hipErrorInvalidValue;
   } else {
     return hipErrorInvalidValue;
   }

@@ -602,7 +602,9 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams p) {
 // A workgroup walks row groups of 64/LW*R rows; x stays in LDS between them.
 template <int FMT, int MT, int NW, int L, int R, int J, int WV, bool MULTI>
 __global__ void __launch_bounds__(512) gemv_ks_kernel(GemvParams p) {
-  static_assert((L == 32 || L == 64) && (WV == 4 || WV == 8) && L / WV >= 4, "4 or 8 waves of 4 or 8 virtual lanes");
+  // the in-wave part of the butterfly below covers 4 or 8 virtual lanes
+  static_assert((L == 32 || L == 64) && (WV == 4 || WV == 8) && (L / WV == 4 || L / WV == 8),
+                "4 or 8 waves of 4 or 8 virtual lanes");
   constexpr int CH = FmtTraits<FMT>::CH;
   constexpr int NE4 = CH / 4;
   constexpr int LW = L / WV;             // lanes of a row inside one wave
