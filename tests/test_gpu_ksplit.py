@@ -38,9 +38,10 @@ def both(call):
     return a, b
 
 
-# K from one super-block to 32 (one to four chunks per lane, ragged last lanes)
+# K from one super-block to 64 (one to four chunks per lane, ragged last lanes;
+# from K = 4096 on, 64 lanes per row and 8 waves)
 @pytest.mark.parametrize("n,k", [(1, 256), (15, 512), (17, 1024), (33, 2304), (300, 4096),
-                                 (70, 5888), (40, 8192), (4099, 4096)])
+                                 (70, 5888), (40, 8192), (4099, 4096), (25, 12544), (11, 16384)])
 def test_q4_k_ksplit_equals_chunked(lib, n, k):
     w, x = synth.q4_k_case(8100 + n, 1, n, k)
     dw, dx = dev(w), dev(x)
@@ -49,7 +50,7 @@ def test_q4_k_ksplit_equals_chunked(lib, n, k):
     assert_close(a, oracle.decode_q4_k(w, n, k), x, f"q4_k ksplit n{n} k{k}")
 
 
-@pytest.mark.parametrize("n,k", [(3, 64), (257, 4096), (31, 8128)])
+@pytest.mark.parametrize("n,k", [(3, 64), (257, 4096), (31, 8128), (20, 12288), (9, 16384)])
 def test_q4_0_ksplit_equals_chunked(lib, n, k):
     w, x = synth.q4_0_case(8200 + n, 1, n, k)
     dw, dx = dev(w), dev(x)
@@ -58,7 +59,7 @@ def test_q4_0_ksplit_equals_chunked(lib, n, k):
     assert_close(a, oracle.decode_q4_0(w, n, k), x, f"q4_0 ksplit n{n} k{k}")
 
 
-@pytest.mark.parametrize("n,k", [(50, 4096), (19, 2048 + 64)])
+@pytest.mark.parametrize("n,k", [(50, 4096), (19, 2048 + 64), (21, 16384)])
 def test_dual_ksplit_equals_chunked_and_single_calls(lib, n, k):
     """The dual product on the K-sliced kernel equals the chunked kernel and
     two single calls, bit for bit."""
