@@ -120,11 +120,12 @@ GemvPlan plan_gemv(int64_t m, int64_t k, int nw) {
   GemvPlan pl{};
   const int64_t chunks = k / CH;
   pl.mt = m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : 8;
-  // Q4 formats: 32 lanes per row, except one x row with 64 to 256 chunks per
-  // row (K = 4096 .. 16384), where the K-sliced kernel takes 64 lanes and 8
-  // waves (one or more chunks for every lane): Q4_K 4096 x 4096 4.72 -> 4.50
-  // us, dual Q4_0 6.7 -> 6.2 us, multi-part q|k|v 6.7 -> 6.3 us.
-  pl.l = Q4 ? (pl.mt == 1 && chunks >= 64 && chunks <= 256 ? 64 : 32) : (chunks >= 64 ? 64 : 32);
+  // Q4 formats: 32 lanes per row, except one or two x rows with 64 to 256
+  // chunks per row (K = 4096 .. 16384), where the K-sliced kernel takes 64
+  // lanes and 8 waves (one or more chunks for every lane): Q4_K 4096 x 4096
+  // 4.72 -> 4.50 us, dual Q4_0 6.7 -> 6.2 us, multi-part q|k|v 6.7 -> 6.3 us;
+  // at two x rows Q4_0 4096 x 4096 6.3 -> 5.6 us, 14336 x 4096 12.8 -> 11.5 us.
+  pl.l = Q4 ? (pl.mt <= 2 && chunks >= 64 && chunks <= 256 ? 64 : 32) : (chunks >= 64 ? 64 : 32);
   int r = 1;
   if (!Q4 && chunks >= 64 && (pl.mt * nw <= 2 || (nw == 1 && pl.mt == 8))) r = 2;
   // affine codes at one x row with 64 to 256 chunks per row (K = 2048 .. 8192):
@@ -336,8 +337,8 @@ int ks_waves(int64_t k, int l) {
 // Chunks per lane the K-sliced kernel takes for this call (0: not eligible):
 // x in LDS for the whole K and the chunked kernel's shape (L, R) = (32, 1)
 // for the 64-weight chunks of Q4_0/Q4_K (one or two weight streams; one x row,
-// or tiles of 2 or 4 rows where 4 waves are used), (64, 1) for them at one x
-// row with 64..256 chunks per row (8 waves), or (64, 1) / (64, 2) for the
+// or tiles of 2 or 4 rows where 4 waves are used), (64, 1) for them at one or
+// two x rows with 64..256 chunks per row (8 waves), or (64, 1) / (64, 2) for the
 // 32-code chunks of the affine formats (one x row).
 template <int FMT, int NW>
 int ks_chunks(const GemvPlan& pl, int64_t m, int64_t k) {
@@ -349,8 +350,9 @@ int ks_chunks(const GemvPlan& pl, int64_t m, int64_t k) {
   // tiles of 2 or 4 rows of x: the dual Q4_0 product at M = 4 takes 11.0 us
   // here against 14.1 us on the chunked kernel; at 8 rows (22.1 vs 18.5 us)
   // the chunked kernel stays
-  if (pl.mt > 1 && !(Q4 && pl.l == 32 && pl.mt <= 4 && ks_waves<FMT>(k, pl.l) == 4)) return 0;
-  if (Q4 ? !((pl.l == 32 || (pl.l == 64 && pl.mt == 1)) && pl.r == 1) : !(pl.l == 64 && (pl.r == 1 || pl.r == 2)))
+  if (pl.mt > 1 && !(Q4 && ((pl.l == 32 && pl.mt <= 4 && ks_waves<FMT>(k, pl.l) == 4) || (pl.l == 64 && pl.mt == 2))))
+    return 0;
+  if (Q4 ? !((pl.l == 32 || (pl.l == 64 && pl.mt <= 2)) && pl.r == 1) : !(pl.l == 64 && (pl.r == 1 || pl.r == 2)))
     return 0;
   const int64_t j = cdiv(k / FmtTraits<FMT>::CH, pl.l);
   (void)m;
@@ -373,6 +375,7 @@ template <int FMT, int NW>
 hipError_t launch_gemv_ks(const GemvPlan& pl, int j, const GemvParams& p, dim3 grid, hipStream_t s) {
   if constexpr (FMT == FMT_Q40 || FMT == FMT_Q4K) {
     if (pl.l == 64 && pl.r == 1 && pl.mt == 1) return launch_gemv_ks_lr<FMT, 1, NW, 64, 1, 8>(j, p, grid, s);
+    if (pl.l == 64 && pl.r == 1 && pl.mt == 2) return launch_gemv_ks_lr<FMT, 2, NW, 64, 1, 8>(j, p, grid, s);
     if (!(pl.l == 32 && pl.r == 1)) return hipErrorInvalidValue;
     const bool four = ks_waves<FMT>(p.k, pl.l) == 4;
     switch (pl.mt) {

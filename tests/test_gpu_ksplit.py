@@ -155,7 +155,8 @@ def test_q4_k_ksplit_waves_do_not_change_bits(lib, k):
 
 
 # two to four rows of x (tiles of 2 or 4 rows, 4 waves per workgroup at K >= 2048)
-@pytest.mark.parametrize("m,n,k", [(2, 33, 2048), (3, 300, 4096), (4, 70, 8192), (4, 4099, 4096)])
+@pytest.mark.parametrize("m,n,k", [(2, 33, 2048), (3, 300, 4096), (4, 70, 8192), (4, 4099, 4096),
+                                   (2, 4099, 4096), (2, 17, 16384)])
 def test_q4_k_ksplit_rows_of_x_equal_chunked(lib, m, n, k):
     w, x = synth.q4_k_case(9700 + m + n, m, n, k)
     dw, dx = dev(w), dev(x)
