@@ -371,7 +371,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); "
-              "the path shards by output rows, see DESIGN.md", file=sys.stderr)
+              "the path shards by output rows: each GPU would hold N/G rows of the weights", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -25,7 +25,7 @@ HIP_FLAGS = [
     f"--offload-arch={ARCH}",
     "-ffp-contract=off",                 # every fused multiply-add is written out explicitly
     "-mcode-object-version=5",
-    # packed FP32 instructions are kept out of the device code
+    # packed FP32 instructions (v_pk_*_f32) are kept out of the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]

@@ -15,14 +15,16 @@ What it computes, and where the pages define it:
   GGML block formats.
 * ``block_q4_0``: fp16 ``d`` then 16 nibble bytes, value ``(nibble - 8) * d``
   (mlx-native ``fused_dual_proj_q4_0.rs``, preconditions of
-  ``dispatch_fused_dual_proj_q4_0``: "sizeof(half) + 16 nibbles").  Which
-  nibble is which element is not on the pages; the reading used (low nibble of
-  byte j = element j, high nibble = element j+16) is listed in the design doc.
+  ``dispatch_fused_dual_proj_q4_0``: an fp16 scale followed by 16 bytes of
+  nibbles).  Which nibble is which element is not on the pages; the reading
+  used here is the low nibble of byte j for element j and the high nibble for
+  element j+16.
 * ``block_q4_K``: 144 bytes per 256 weights, row-major ``[N][K/256]``
   (ferrum-kernels ``q4_k_gemv_v2.rs``, module doc and ``nb01``).  The field
-  layout is not on the pages; the reading used is listed in the design doc.
+  layout is not on the pages; the reading used is the GGML ``block_q4_K``
+  layout written out below.
 * The fused dual projection equals two single Q4_0 products
-  (mlx-native ``fused_dual_proj_q4_0.rs``, module doc: the math contract).
+  (mlx-native ``fused_dual_proj_q4_0.rs``, module doc: what the kernel computes).
 * ``qkv_split_f32`` copies columns ``[0,q_sp)``, ``[q_sp,q_sp+k_sp)`` and
   ``[q_sp+k_sp, qkv_ch)`` of each token row into q, k, v
   (mlx-native ``qkv_split.rs``, module doc and ``dispatch_qkv_split_f32``).

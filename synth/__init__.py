@@ -5,7 +5,8 @@ weight encodings made from them.  It holds no decoding and no products; the
 oracle (``oracle/``) and the HIP library (``gemm_qgemv_q4_amd``) each decode
 the bytes written here with code of their own.
 
-Encodings written here (byte layouts; the readings are stated in the design doc):
+Encodings written here (byte layouts; where the pages are silent these are
+readings of them, the same ones the oracle uses):
 
 * ``block_q4_0`` -- 18 bytes per 32 weights: little-endian fp16 ``d`` then 16
   bytes ``qs``; the low nibble of ``qs[j]`` is element ``j``, the high nibble is
