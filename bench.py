@@ -370,7 +370,7 @@ def main():
                          "byte counters of the profiles are scaled by")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); "
+        print(f"bench.py: measures one GPU only (got --gpus {args.gpus}); "
               "the path shards by output rows: each GPU would hold N/G rows of the weights", file=sys.stderr)
         sys.exit(2)
 

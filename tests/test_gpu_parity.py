@@ -151,7 +151,7 @@ def test_affine_full_byte_codes(lib):
 
 def test_affine_page_sincos_inputs(lib):
     """Input recipe of the page's qmm_affine_t test (sin of a ramp, modular codes,
-    ramped scales and biases), m8 n16 k64 gs32, held to this build's tolerance."""
+    ramped scales and biases), m8 n16 k64 gs32, held to the library's tolerance."""
     m, n, k, gs = 8, 16, 64, 32
     i = np.arange(m * k, dtype=np.float32)
     x = (np.sin(i * np.float32(0.013) - np.float32(0.4)) * np.float32(0.6)).astype(np.float32).reshape(m, k)
