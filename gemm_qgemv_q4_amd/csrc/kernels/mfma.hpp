@@ -11,7 +11,7 @@
 //
 // Precision: the codes (0..255) are exact in bf16.  x is split once into
 // x_hi = bf16(x) and x_lo = bf16(x - x_hi), so x_hi + x_lo carries 16
-// significant bits (relative error <= 2^-18); bf16 x bf16 products are exact
+// significant bits (relative error <= 2^-17); bf16 x bf16 products are exact
 // in the f32 MFMA accumulator.  Each group's partial product P_g = (x_hi +
 // x_lo) . q is accumulated by two v_mfma_f32_16x16x32_bf16 per 32 columns and
 // scaled in f32 (acc += s * P_g).  The bias term is a product over the group

@@ -10,7 +10,7 @@
 // row of x; here the per-weight work is the code conversion, and the
 // products run on v_mfma_f32_16x16x32_bf16 with the x rows as the MFMA rows
 // and 16 weight rows as its columns.  x is split into x_hi = bf16(x) and
-// x_lo = bf16(x - x_hi) as in the prefill path (relative error <= 2^-18 per
+// x_lo = bf16(x - x_hi) as in the prefill path (relative error <= 2^-17 per
 // element, codes exact in bf16, products exact in the f32 accumulator); the
 // column sums X stay in f32.
 //

@@ -13,7 +13,7 @@
 // 16 weight rows and whose 16 rows are x: rows 0..7 hold bf16(x) of the (up
 // to) 8 rows of x, rows 8..15 hold bf16(x - bf16(x)).  Both halves of x thus
 // ride in one MFMA, and the output's two partial sums are added at the end
-// (x carries 16 significant bits, relative error <= 2^-18 per element; the
+// (x carries 16 significant bits, relative error <= 2^-17 per element; the
 // codes, 0..15 or 0..255 for u8, are exact in bf16 and the products exact in
 // the f32 accumulator).  The block sums of x come from the same MFMA unit (x
 // times a column of -8 for Q4_0, of ones otherwise), so that a Q4_0 block of
