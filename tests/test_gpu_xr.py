@@ -214,3 +214,25 @@ def test_fused_qkv_xr_bitwise_equals_product_then_split(lib, m):
     for a, r in zip(got, lib.qkv_split_f32(y, m, qs, ks, vs)):
         assert np.array_equal(bits(a), bits(host(r)))
     assert_close(np.concatenate(got, axis=1), oracle.decode_affine(q, s, b, n, k, gs), x, f"fused qkv xr m{m}")
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q4_k", "affine"])
+def test_xr_unaligned_x_gives_the_same_bits(lib, fmt):
+    """x at a 4-byte (not 16-byte) aligned address: the x loads are dword-aligned
+    vector loads, so the result is the same bits as with aligned x."""
+    import torch
+    m, n, k, gs = 5, 37, 2048, 64
+    if fmt == "q4_0":
+        w, x = synth.q4_0_case(10500, m, n, k)
+        call = lambda dx: lib.qgemv_q4_0(dev(w), dx, n, k)
+    elif fmt == "q4_k":
+        w, x = synth.q4_k_case(10501, m, n, k)
+        call = lambda dx: lib.qgemv_q4_k(dev(w), dx, n, k)
+    else:
+        x, q, s, b = synth.affine_case(10502, m, n, k, gs)
+        call = lambda dx: lib.qmm_affine_t(dx, dev(q), dev(s), dev(b), gs)
+    buf = torch.zeros(x.size + 1, dtype=torch.float32, device="cuda")
+    xu = buf[1:].view(m, k)
+    xu.copy_(torch.from_numpy(x).cuda())
+    assert xu.data_ptr() % 16 == 4
+    assert np.array_equal(bits(host(call(xu))), bits(host(call(dev(x)))))
