@@ -284,6 +284,32 @@ def test_linearity_in_x():
     assert np.array_equal(y2, 2 * y1)
 
 
+def test_abs_bound_hand_worked():
+    """bound = sum_k |x w| term by term, worked by hand (tests/golden/abs_bound_hand.json):
+    a bound of |sum_k x w| (entry (0, 1): y = 0, bound 4), a transposed
+    operand (shape [2, 3]) or a dropped |.| on either factor fails it."""
+    fx = _load("abs_bound_hand.json")
+    x = np.array(fx["x"], np.float32)
+    w64 = np.array(fx["w"], np.float64)
+    bound = oracle.abs_bound(w64, x)
+    assert bound.shape == (2, 3)
+    assert np.array_equal(bound, np.array(fx["bound"]))
+    assert np.array_equal(oracle.gemv_f64(w64, x), np.array(fx["y"], np.float32))
+
+
+def test_abs_bound_q4_0_zero_rows():
+    """A Q4_0 row whose weights are all zero (codes 8 with d != 0, or d = 0)
+    has bound 0 and product exactly 0; one code 9 gives bound = |y| = d x[k]."""
+    fx = _load("abs_bound_hand.json")
+    w = np.stack([np.frombuffer(bytes.fromhex(h), np.uint8) for h in fx["q4_0_rows_hex"]])
+    x = (np.arange(64, dtype=np.float32) + 1)[None, :]
+    w64 = oracle.decode_q4_0(w, 2, 64)
+    assert np.array_equal(oracle.abs_bound(w64, x)[0], np.array(fx["q4_0_bound"]))
+    y = oracle.qgemv_q4_0(w, x, 1, 2, 64)[0]
+    assert np.array_equal(y, np.array(fx["q4_0_y"], np.float32))
+    assert y[1] == 0.0 and not np.signbit(y[1])
+
+
 def test_abs_bound_dominates_result():
     x, q, s, b = synth.affine_case(43, 2, 9, 128, 32)
     w64 = oracle.decode_affine(q, s, b, 9, 128, 32)
