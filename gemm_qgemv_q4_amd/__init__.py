@@ -22,6 +22,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("QG_LIB_PATH", os.path.join(_HERE, "lib", "libqgemv_q4.so"))
 
 QG_OK, QG_EINVAL, QG_ELAUNCH = 0, 1, 2
+# bits of qg_set_kernel_mask (include/qgemv_q4.h)
+QG_KERNEL_KSLICED, QG_KERNEL_XR, QG_KERNEL_MMA = 1, 2, 4
+QG_KERNEL_ALL = QG_KERNEL_KSLICED | QG_KERNEL_XR | QG_KERNEL_MMA
 
 # Entry points declared in include/qgemv_q4.h: name -> (restype, argtypes)
 _P = ctypes.c_void_p
@@ -38,6 +41,8 @@ SIGNATURES = {
     "qmm_affine_t_qkv": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "qg_set_mfma_min_m": (ctypes.c_int, [_I]),
     "qg_get_mfma_min_m": (ctypes.c_int64, []),
+    "qg_set_kernel_mask": (ctypes.c_int, [ctypes.c_uint32]),
+    "qg_get_kernel_mask": (ctypes.c_uint32, []),
 }
 
 
@@ -276,6 +281,35 @@ def qg_set_mfma_min_m(m: int) -> None:
 
 def qg_get_mfma_min_m() -> int:
     return int(_lib.qg_get_mfma_min_m())
+
+
+def qg_set_kernel_mask(mask: int) -> None:
+    _check(_lib.qg_set_kernel_mask(mask))
+
+
+def qg_get_kernel_mask() -> int:
+    return int(_lib.qg_get_kernel_mask())
+
+
+class kernels:
+    """Context manager that sets the kernel mask (and optionally the matrix-core
+    threshold) for the calls inside it and restores both afterwards."""
+
+    def __init__(self, mask: int | None = None, mfma_min_m: int | None = None):
+        self.mask, self.min_m = mask, mfma_min_m
+
+    def __enter__(self):
+        self.old = (qg_get_kernel_mask(), qg_get_mfma_min_m())
+        if self.mask is not None:
+            qg_set_kernel_mask(self.mask)
+        if self.min_m is not None:
+            qg_set_mfma_min_m(self.min_m)
+        return self
+
+    def __exit__(self, *exc):
+        qg_set_kernel_mask(self.old[0])
+        qg_set_mfma_min_m(self.old[1])
+        return False
 
 
 raw = _lib  # the loaded C library, for callers that pass raw pointers

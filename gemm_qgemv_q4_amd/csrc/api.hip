@@ -2,12 +2,13 @@
 // kernel-variant choice and launches on the caller's stream.
 //
 // Every product entry point reduces to a list of "parts": weight tensors of
-// one format that share x, each with its rows and its output slice.  A part
-// list runs either on the GEMV kernel (small M) or, from qg_get_mfma_min_m()
-// rows of x on, on the matrix-core kernel.  Which of the two runs depends only
-// on the format, M, K, the group size and pointer alignment, never on how the
-// rows are split into parts, so single, dual, multi-part and fused-split calls
-// agree bit for bit.
+// one format that share x, each with its rows and its output slice.  The
+// kernel that computes a weight tensor (its "path") is chosen from the format,
+// M, K, the group size, that tensor's own alignment and size, and the two
+// process-wide settings (matrix-core threshold, kernel mask), read once per
+// call.  Parts whose paths differ run in separate launches, so a dual,
+// multi-part or fused-split call computes every weight tensor exactly as the
+// single call on that tensor would, bit for bit.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -29,6 +30,15 @@ namespace {
 
 thread_local char g_err[512] = "";
 std::atomic<int64_t> g_mfma_min_m{64};
+constexpr uint32_t kAllKernels = QG_KERNEL_KSLICED | QG_KERNEL_XR | QG_KERNEL_MMA;
+std::atomic<uint32_t> g_kernel_mask{kAllKernels};
+
+// The process-wide settings as one call sees them (read once per call).
+struct CallCfg {
+  int64_t mfma_min_m;
+  uint32_t mask;
+};
+CallCfg call_cfg() { return {g_mfma_min_m.load(), g_kernel_mask.load()}; }
 
 qg_status fail(const char* fmt, ...) {
   va_list ap;
@@ -95,12 +105,82 @@ template <> int64_t row_bytes_of<FMT_Q4K>(int64_t k) { return k / 256 * 144; }
 template <> int64_t row_bytes_of<FMT_AFF>(int64_t k) { return k; }
 template <> int64_t row_bytes_of<FMT_AFF4>(int64_t k) { return k / 2; }
 
+// ------------------------------------------------------------------ paths
+// The kernel that computes one weight tensor.  Plain: one thread per output
+// (shapes and alignments the vector loaders do not take).  FMA: the chunked or
+// the K-sliced GEMV (same bits).  XR: the x-resident matrix-core GEMV (3 rows
+// of x up to the threshold).  MMA: the streamed matrix-core GEMV for affine
+// codes (2 rows of x up to the threshold, or where XR does not apply).  MFMA:
+// the matrix-core GEMM from the threshold on.
+enum Path { P_PLAIN, P_FMA, P_XR, P_MMA, P_MFMA };
+
+// Matrix-core GEMM: M at the threshold, K a whole number of 64-column stages,
+// group size 32..512, the weights aligned for its vector loads and below 2 GiB
+// (32-bit offsets), x below 2^31 elements.
+template <int FMT>
+bool mfma_ok(const CallCfg& cfg, int64_t m, int64_t k, int64_t gs, const void* w, int64_t n) {
+  if (m < cfg.mfma_min_m || k % 64 != 0 || gs < 32 || gs > 512) return false;
+  if (m * k >= k2G) return false;
+  const uintptr_t al = FMT == FMT_AFF || FMT == FMT_Q4K ? 16 : FMT == FMT_AFF4 ? 8 : 4;
+  return aligned(w, al) && n * row_bytes_of<FMT>(k) < k2G;
+}
+
+// The chunked loaders take 64-weight chunks of Q4_0 (4-byte aligned), 16-byte
+// aligned Q4_K rows, and 32-code chunks of 16-byte aligned affine codes inside
+// one group.
+template <int FMT>
+bool plain_needed(int64_t k, int64_t gs, const void* w) {
+  if constexpr (FMT == FMT_Q40) return k % 64 != 0;
+  else if constexpr (FMT == FMT_Q4K) return !aligned(w, 16);
+  else return k % 32 != 0 || gs < 32 || !aligned(w, 16);
+}
+
+// x-resident matrix-core GEMV: from 3 rows of x, K a multiple of 512 up to
+// 4096 (one wave per 512 columns), 16-byte aligned weights, affine group size
+// >= 64.  Measured (graph replay, K = 4096): at 2 rows the K-sliced FMA kernel
+// is ahead (N = 4096: 6.2 vs 7.4 us), from 3 rows this one (N = 14336: 19.4 vs
+// 13.9 us at 3 rows, 50.1 vs 15.4 us at 8).
+template <int FMT>
+bool xr_ok(const CallCfg& cfg, int64_t m, int64_t k, int64_t gs, const void* w) {
+  if (!(cfg.mask & QG_KERNEL_XR)) return false;
+  if (m < 3 || k % 512 != 0 || k > 512 * kXrMaxWaves) return false;
+  if ((FMT == FMT_AFF || FMT == FMT_AFF4) && gs < 64) return false;
+  return aligned(w, 16);
+}
+
+// Streamed matrix-core GEMV for the affine formats from 2 rows of x: group
+// size >= 64, K a multiple of 512 with K/512 in {1, 2, 4, 8} (up to 8 pairs of
+// 32-column blocks per wave, so x of 8 rows fits in LDS), codes aligned for
+// its vector loads.
+template <int FMT>
+bool mma_ok(const CallCfg& cfg, int64_t m, int64_t k, int64_t gs, const void* w) {
+  if constexpr (FMT != FMT_AFF && FMT != FMT_AFF4) {
+    return false;
+  } else {
+    if (!(cfg.mask & QG_KERNEL_MMA)) return false;
+    if (m < 2 || gs < 64 || k % 512 != 0) return false;
+    const int64_t np = k / 512;
+    if (np != 1 && np != 2 && np != 4 && np != 8) return false;
+    return aligned(w, FMT == FMT_AFF ? 16 : 8);
+  }
+}
+
+// The path of one weight tensor of n rows at w (the whole fused weight for the
+// fused split, whose parts are row ranges of it).
+template <int FMT>
+Path path_of(const CallCfg& cfg, int64_t m, int64_t k, int64_t gs, const void* w, int64_t n) {
+  if (mfma_ok<FMT>(cfg, m, k, gs, w, n)) return P_MFMA;
+  if (plain_needed<FMT>(k, gs, w)) return P_PLAIN;
+  if (xr_ok<FMT>(cfg, m, k, gs, w)) return P_XR;
+  if (mma_ok<FMT>(cfg, m, k, gs, w)) return P_MMA;
+  return P_FMA;
+}
+
 // ------------------------------------------------------------------ GEMV
 struct GemvPlan {
   int mt, l, r, kt;
   size_t lds;
   bool persistent;
-  int waves_env, bpc_env;  // tuning override (0: automatic)
 };
 
 // Launch shape of the chunked GEMV kernel that fixes its arithmetic: rows of
@@ -132,22 +212,11 @@ GemvPlan plan_gemv(int64_t m, int64_t k, int nw) {
   // one row per lane on the K-sliced kernel (12288 x 4096 gs 64: u8 12.7 ->
   // 12.1 us, packed 8.9 -> 8.6 us against two rows per lane)
   if (!Q4 && pl.mt == 1 && chunks >= 64 && chunks <= 256) r = 1;
+  pl.r = r;
   auto lds_for = [&](int64_t kt) {
     const int64_t ct = kt / CH;
     return (size_t)(pl.mt * (CH / 4) * (ct + 1) * 16 + (SUMS ? pl.mt * ct * 8 : 0));
   };
-  // Tuning override "L,R,W,B" (0 keeps the automatic choice; W = waves per
-  // workgroup, B = workgroups per CU of the persistent grid), e.g.
-  // QG_GEMV_PLAN=32,1,8,0
-  int el = 0, er = 0, ew = 0, eb = 0;
-  if (const char* env = getenv("QG_GEMV_PLAN")) {
-    if (sscanf(env, "%d,%d,%d,%d", &el, &er, &ew, &eb) < 1) el = er = ew = eb = 0;
-  }
-  if (el == 8 || el == 16 || el == 32 || el == 64) pl.l = el;
-  if (er == 1 || (er == 2 && (pl.mt * nw <= 2 || (nw == 1 && pl.mt == 8))) || (er == 4 && pl.mt * nw == 1)) r = er;
-  pl.r = r;
-  pl.waves_env = (ew == 1 || ew == 2 || ew == 4 || ew == 8) ? ew : 0;
-  pl.bpc_env = (eb >= 1 && eb <= 8) ? eb : 0;
   pl.persistent = lds_for(k) <= kLdsPersistent;
   if (pl.persistent) {
     pl.kt = (int)k;
@@ -184,7 +253,7 @@ GemvGrid grid_gemv(const GemvPlan& pl, const HostPart* parts, int nparts) {
   const int pref = ((FMT == FMT_AFF || FMT == FMT_AFF4) && pl.mt <= 2) ? 4 : 8;
   GemvGrid best{};
   if (!pl.persistent) {
-    best.waves = pl.waves_env ? pl.waves_env : 4;
+    best.waves = 4;
     best.groups_rows = (int64_t)best.waves * (64 / pl.l) * pl.r;
     best.grid = groups_for(best.groups_rows);
     return best;
@@ -192,16 +261,13 @@ GemvGrid grid_gemv(const GemvPlan& pl, const HostPart* parts, int nparts) {
   double best_eff = -1.0;
   const int cand[2] = {pref, pref == 8 ? 4 : 8};
   for (int ci = 0; ci < 2; ++ci) {
-    const int w = pl.waves_env ? pl.waves_env : cand[ci];
-    if (ci == 1 && pl.waves_env) break;
+    const int w = cand[ci];
     const int64_t rpg = (int64_t)w * (64 / pl.l) * pl.r;
     const int64_t groups = groups_for(rpg);
     int fit = (int)(kLdsMax / (pl.lds ? pl.lds : 1));
     const int cap_b = w == 8 ? 1 : 4;
     fit = fit < 1 ? 1 : fit > cap_b ? cap_b : fit;
-    int b_lo = 1, b_hi = fit;
-    if (pl.bpc_env && (size_t)pl.bpc_env * pl.lds <= kLdsMax) b_lo = b_hi = pl.bpc_env;
-    for (int b = b_hi; b >= b_lo; --b) {
+    for (int b = fit; b >= 1; --b) {
       const int64_t slots = cus * b;
       const int64_t used = groups < slots ? groups : slots;
       const double eff = (double)groups / (double)(cdiv(groups, slots) * used);
@@ -216,6 +282,16 @@ GemvGrid grid_gemv(const GemvPlan& pl, const HostPart* parts, int nparts) {
   return best;
 }
 
+// Kernels whose LDS exceeds the default 64 KB need the limit raised once.
+template <typename K>
+hipError_t allow_lds(K kern, size_t lds, std::atomic<bool>& raised) {
+  if (lds <= 64 * 1024 || raised.load()) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax);
+  if (e == hipSuccess) raised.store(true);
+  return e;
+}
+
 template <int FMT, int MT, int NW, int L, int R>
 hipError_t launch_gemv_t(const GemvParams& p, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
   // multi-part variants exist for the formats whose entry points take parts
@@ -223,46 +299,32 @@ hipError_t launch_gemv_t(const GemvParams& p, dim3 grid, dim3 block, size_t lds,
   if constexpr (kHasMulti) {
     if (p.parts > 1) {
       auto kern = gemv_kernel<FMT, MT, NW, L, R, true>;
-      if (lds > 64 * 1024) {
-        static std::atomic<bool> raised{false};
-        if (!raised.load()) {
-          hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax);
-          if (e != hipSuccess) return e;
-          raised.store(true);
-        }
-      }
+      static std::atomic<bool> raised{false};
+      const hipError_t e = allow_lds(kern, lds, raised);
+      if (e != hipSuccess) return e;
       hipLaunchKernelGGL(kern, grid, block, lds, s, p);
       return hipSuccess;
     }
   }
   if (p.parts != 1) return hipErrorInvalidValue;
   auto kern = gemv_kernel<FMT, MT, NW, L, R, false>;
-  if (lds > 64 * 1024) {
-    static std::atomic<bool> raised{false};
-    if (!raised.load()) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax);
-      if (e != hipSuccess) return e;
-      raised.store(true);
-    }
-  }
+  static std::atomic<bool> raised{false};
+  const hipError_t e = allow_lds(kern, lds, raised);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, grid, block, lds, s, p);
   return hipSuccess;
 }
 
 template <int FMT, int MT, int NW, int L>
 hipError_t launch_gemv_r(int r, const GemvParams& p, dim3 g, dim3 b, size_t lds, hipStream_t s) {
-  // row sets per wave that fit the 256-VGPR budget of a 512-thread workgroup
-  switch (r) {
-    case 4:
-      if constexpr (MT * NW == 1) return launch_gemv_t<FMT, MT, NW, L, 4>(p, g, b, lds, s);
-      break;
-    case 2:
+  // two row sets per wave where plan_gemv takes them (affine codes)
+  if constexpr (FMT == FMT_AFF || FMT == FMT_AFF4) {
+    if (r == 2) {
       if constexpr (MT * NW <= 2 || (NW == 1 && MT == 8)) return launch_gemv_t<FMT, MT, NW, L, 2>(p, g, b, lds, s);
-      break;
-    case 1: return launch_gemv_t<FMT, MT, NW, L, 1>(p, g, b, lds, s);
+      return hipErrorInvalidValue;
+    }
   }
+  if (r == 1) return launch_gemv_t<FMT, MT, NW, L, 1>(p, g, b, lds, s);
   return hipErrorInvalidValue;
 }
 
@@ -271,8 +333,6 @@ hipError_t launch_gemv_l(int l, int r, const GemvParams& p, dim3 g, dim3 b, size
   switch (l) {
     case 64: return launch_gemv_r<FMT, MT, NW, 64>(r, p, g, b, lds, s);
     case 32: return launch_gemv_r<FMT, MT, NW, 32>(r, p, g, b, lds, s);
-    case 16: return launch_gemv_r<FMT, MT, NW, 16>(r, p, g, b, lds, s);
-    case 8: return launch_gemv_r<FMT, MT, NW, 8>(r, p, g, b, lds, s);
   }
   return hipErrorInvalidValue;
 }
@@ -308,43 +368,35 @@ size_t ks_lds(int mt, int nw, int l, int r, int j, int wv) {
   const size_t ne4 = FmtTraits<FMT>::CH / 4;
   const size_t u = (size_t)(l / wv) * j;
   const size_t rows = (size_t)(kWave / (l / wv)) * r;
-  return (size_t)mt * (wv * ne4 * (u + 1) * 16 + wv * 2 * u * 4 + 2 * (size_t)nw * wv * rows * 4);
+  const size_t sums = FmtTraits<FMT>::SUMS ? wv * 2 * u * 4 : 0;
+  return (size_t)mt * (wv * ne4 * (u + 1) * 16 + sums + 2 * (size_t)nw * wv * rows * 4);
 }
 
-// Waves per workgroup of the K-sliced kernel.  The affine formats use 8.  For
-// the 64-weight chunks of Q4_0/Q4_K, 4 waves of 8 virtual lanes (row groups of
-// 8 rows, twice the workgroups) measured faster where every virtual lane has a
-// chunk (K >= 2048): 6.6 vs 7.0 us for the multi-part q|k|v product, 11.5 vs
-// 12.3 us for its three separate calls, a tie at 4096 x 4096; at K = 1024
-// 8 waves are faster (2.35 vs 2.48 us).  Tuning override QG_GEMV_KS_WAVES=4|8
-// for the Q4 formats (same results either way).
+// Waves per workgroup of the K-sliced kernel (the arithmetic is the same
+// either way).  The affine formats use 8.  For the 64-weight chunks of
+// Q4_0/Q4_K, 4 waves of 8 virtual lanes (row groups of 8 rows, twice the
+// workgroups) measured faster where every virtual lane has a chunk (K >=
+// 2048): 6.6 vs 7.0 us for the multi-part q|k|v product, 11.5 vs 12.3 us for
+// its three separate calls, a tie at 4096 x 4096; at K = 1024 8 waves are
+// faster (2.35 vs 2.48 us).  64 lanes per row always take 8 waves (8 virtual
+// lanes per wave and row).
 template <int FMT>
 int ks_waves(int64_t k, int l) {
-  if constexpr (FMT != FMT_Q40 && FMT != FMT_Q4K) {
-    return 8;
-  } else {
-    // 64 lanes per row: always 8 waves (8 virtual lanes per wave and row; the
-    // kernel's butterfly across waves is not written for 16)
-    if (l == 64) return 8;
-    if (const char* env = getenv("QG_GEMV_KS_WAVES")) {
-      const int w = atoi(env);
-      if (w == 4 || w == 8) return w;
-    }
-    return k / 64 >= 32 ? 4 : 8;
-  }
+  if constexpr (FMT != FMT_Q40 && FMT != FMT_Q4K) return 8;
+  if (l == 64) return 8;
+  return k / 64 >= 32 ? 4 : 8;
 }
 
-// Chunks per lane the K-sliced kernel takes for this call (0: not eligible):
-// x in LDS for the whole K and the chunked kernel's shape (L, R) = (32, 1)
-// for the 64-weight chunks of Q4_0/Q4_K (one or two weight streams; one x row,
-// or tiles of 2 or 4 rows where 4 waves are used), (64, 1) for them at one or
-// two x rows with 64..256 chunks per row (8 waves), or (64, 1) / (64, 2) for the
-// 32-code chunks of the affine formats (one x row).
+// Chunks per lane the K-sliced kernel takes for this call (0: the chunked
+// kernel runs instead): x in LDS for the whole K and the chunked kernel's
+// shape (L, R) = (32, 1) for the 64-weight chunks of Q4_0/Q4_K (one or two
+// weight streams; one x row, or tiles of 2 or 4 rows where 4 waves are used),
+// (64, 1) for them at one or two x rows with 64..256 chunks per row (8 waves),
+// or (64, 1) / (64, 2) for the 32-code chunks of the affine formats (one x
+// row).
 template <int FMT, int NW>
-int ks_chunks(const GemvPlan& pl, int64_t m, int64_t k) {
-  // tuning override (same results either way): QG_GEMV_KS=0 keeps the chunked kernel
-  if (const char* env = getenv("QG_GEMV_KS"))
-    if (env[0] == '0') return 0;
+int ks_chunks(const CallCfg& cfg, const GemvPlan& pl, int64_t k) {
+  if (!(cfg.mask & QG_KERNEL_KSLICED)) return 0;
   constexpr bool Q4 = FMT == FMT_Q40 || FMT == FMT_Q4K;
   if (!pl.persistent) return 0;
   // tiles of 2 or 4 rows of x: the dual Q4_0 product at M = 4 takes 11.0 us
@@ -355,7 +407,6 @@ int ks_chunks(const GemvPlan& pl, int64_t m, int64_t k) {
   if (Q4 ? !((pl.l == 32 || (pl.l == 64 && pl.mt <= 2)) && pl.r == 1) : !(pl.l == 64 && (pl.r == 1 || pl.r == 2)))
     return 0;
   const int64_t j = cdiv(k / FmtTraits<FMT>::CH, pl.l);
-  (void)m;
   return j >= 1 && j <= 4 ? (int)j : 0;
 }
 
@@ -394,41 +445,13 @@ hipError_t launch_gemv_ks(const GemvPlan& pl, int j, const GemvParams& p, dim3 g
   }
 }
 
-// Matrix-core GEMV for 2..8 rows of x per launch and the affine formats:
-// group size >= 64, K a multiple of 512 with K/512 in {1, 2, 4, 8} (up to 8
-// pairs of 32-column blocks per wave, so x of 8 rows fits in LDS), codes
-// aligned for their vector loads.  Returns the pairs per wave (0: not taken).
-template <int FMT>
-int mma_pairs(const HostPart* parts, int nparts, int64_t m, int64_t k, int64_t gs) {
-  if constexpr (FMT != FMT_AFF && FMT != FMT_AFF4) {
-    return 0;
-  } else {
-    // tuning override (different rounding, same tolerance): QG_GEMV_MMA=0 keeps the FMA kernels
-    if (const char* env = getenv("QG_GEMV_MMA"))
-      if (env[0] == '0') return 0;
-    if (m < 2 || gs < 64 || k % 512 != 0) return 0;
-    const int64_t np = k / 512;
-    if (np != 1 && np != 2 && np != 4 && np != 8) return 0;
-    for (int pi = 0; pi < nparts; ++pi)
-      if (!aligned(parts[pi].w[0], FMT == FMT_AFF ? 16 : 8)) return 0;
-    return (int)np;
-  }
-}
-
 template <int FMT, int NP>
 hipError_t launch_gemv_mma_np(const GemvParams& p, dim3 grid, hipStream_t s) {
   constexpr size_t lds = (size_t)mma_lds_bytes(NP);
   auto kern = p.parts > 1 ? gemv_mma_kernel<FMT, NP, true> : gemv_mma_kernel<FMT, NP, false>;
-  if constexpr (lds > 64 * 1024) {
-    static std::atomic<bool> raised[2] = {false, false};
-    const int which = p.parts > 1 ? 1 : 0;
-    if (!raised[which].load()) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-      raised[which].store(true);
-    }
-  }
+  static std::atomic<bool> raised[2] = {false, false};
+  const hipError_t e = allow_lds(kern, lds, raised[p.parts > 1 ? 1 : 0]);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, grid, dim3(512), lds, s, p);
   return hipSuccess;
 }
@@ -448,260 +471,211 @@ hipError_t launch_gemv_mma(int np, const GemvParams& p, dim3 grid, hipStream_t s
   }
 }
 
-// Q4_0, Q4_K and the affine formats (group size >= 64) from 3 rows of x on
-// the matrix cores with x held in registers (gemv_xr_kernel): K a multiple of
-// 512 up to 4096 (one wave per 512 columns), weights 16-byte aligned.  Every weight stream of the part list
-// (both of a dual product) becomes one part of the launch.
-template <int FMT>
-bool xr_ok(const HostPart* parts, int nparts, int nw, int64_t m, int64_t k, int64_t gs) {
-  // tuning override (different rounding, same tolerance): QG_GEMV_XR=0 keeps the FMA kernels,
-  // QG_GEMV_XR=M takes this kernel from M rows of x on
-  // Measured (graph replay, K = 4096): at 2 rows the K-sliced FMA kernel is
-  // ahead (N = 4096: 6.2 vs 7.4 us), from 3 rows this one (N = 14336: 19.4 vs
-  // 13.9 us at 3 rows, 50.1 vs 15.4 us at 8).
-  int64_t min_m = 3;
-  if (const char* env = getenv("QG_GEMV_XR")) {
-    if (env[0] == '0') return false;
-    if (atoi(env) > 0) min_m = atoi(env);
-  }
-  if (m < min_m || k % 512 != 0 || k > 512 * kXrMaxWaves) return false;
-  if ((FMT == FMT_AFF || FMT == FMT_AFF4) && gs < 64) return false;
-  if (nparts * nw > kMaxParts) return false;
-  for (int pi = 0; pi < nparts; ++pi)
-    for (int st = 0; st < nw; ++st)
-      if (!aligned(parts[pi].w[st], 16)) return false;
-  return true;
-}
-
-template <int FMT>
-qg_status run_gemv_xr(const char* op, const HostPart* parts, int nparts, int nw, const float* x, int64_t m,
-                      int64_t k, int gs, hipStream_t s) {
+// Part table of a GEMV launch: every weight stream of the part list, with row
+// groups of `rows_per_group` rows numbered part after part.  `split_streams`
+// (the x-resident kernel) makes each stream of a dual part a part of its own.
+GemvParams gemv_params(const HostPart* parts, int nparts, int nw, bool split_streams, int64_t rows_per_group,
+                       int64_t k, int gs, int64_t row_bytes) {
   GemvParams p{};
   int64_t groups = 0;
   int np = 0;
   for (int pi = 0; pi < nparts; ++pi) {
-    for (int st = 0; st < nw; ++st) {
+    const int ns = split_streams ? nw : 1;
+    for (int st = 0; st < ns; ++st) {
       GemvPart& gp = p.part[np++];
-      gp.w[0] = gp.w[1] = static_cast<const uint8_t*>(parts[pi].w[st]);
-      gp.y[0] = gp.y[1] = parts[pi].y[st];
+      for (int j = 0; j < 2; ++j) {
+        const int src = split_streams ? st : j;
+        gp.w[j] = static_cast<const uint8_t*>(parts[pi].w[src] ? parts[pi].w[src] : parts[pi].w[0]);
+        gp.y[j] = parts[pi].y[src] ? parts[pi].y[src] : parts[pi].y[0];
+      }
       gp.scales = parts[pi].scales;
       gp.biases = parts[pi].biases;
       gp.ldy = parts[pi].ldy;
       gp.n = (int)parts[pi].n;
       gp.group0 = (int)groups;
-      groups += cdiv(parts[pi].n, 16);
+      groups += cdiv(parts[pi].n, rows_per_group);
     }
   }
   p.parts = np;
   p.n_groups = (int)groups;
-  p.row_bytes = row_bytes_of<FMT>(k);
+  p.row_bytes = row_bytes;
   p.k = (int)k;
   p.gs = gs;
+  return p;
+}
+
+// The m-tile of rows m0.. of a launch: x and every output pointer advanced.
+GemvParams m_tile(const GemvParams& p, const float* x, int64_t m0, int64_t m, int64_t k, int mt) {
+  GemvParams q = p;
+  q.x = x + m0 * k;
+  for (int pi = 0; pi < p.parts; ++pi)
+    for (int st = 0; st < 2; ++st) q.part[pi].y[st] = p.part[pi].y[st] + m0 * p.part[pi].ldy;
+  q.m_rows = (int)(m - m0 < mt ? m - m0 : mt);
+  return q;
+}
+
+// x-resident matrix-core GEMV: every weight stream of the part list (both of a
+// dual product) becomes one part of the launch.
+template <int FMT>
+qg_status run_gemv_xr(const char* op, const HostPart* parts, int nparts, int nw, const float* x, int64_t m,
+                      int64_t k, int gs, hipStream_t s) {
+  if (nparts * nw > kMaxParts) return fail("%s: too many weight streams for one launch", op);
+  (void)hipGetLastError();
+  const GemvParams p = gemv_params(parts, nparts, nw, true, 16, k, gs, row_bytes_of<FMT>(k));
   // x of a workgroup lives in its waves' registers: one workgroup per CU for
   // K = 4096, more for shorter rows
   const int waves = (int)(k / 512);
-  int64_t cap = (int64_t)device_cus() * (kXrMaxWaves / waves);
-  if (const char* env = getenv("QG_GEMV_XR_GRID"))  // tuning override: workgroups
-    if (atoi(env) > 0) cap = atoi(env);
-  const int64_t grid = groups < cap ? groups : cap;
-  auto kern = np > 1 ? gemv_xr_kernel<FMT, true> : gemv_xr_kernel<FMT, false>;
-  for (int64_t m0 = 0; m0 < m; m0 += kXrMaxM) {
-    GemvParams q = p;
-    q.x = x + m0 * k;
-    for (int pi = 0; pi < np; ++pi) q.part[pi].y[0] = q.part[pi].y[1] = p.part[pi].y[0] + m0 * p.part[pi].ldy;
-    q.m_rows = (int)(m - m0 < kXrMaxM ? m - m0 : kXrMaxM);
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * waves), 0, s, q);
+  const int64_t cap = (int64_t)device_cus() * (kXrMaxWaves / waves);
+  const int64_t grid = p.n_groups < cap ? p.n_groups : cap;
+  auto kern = p.parts > 1 ? gemv_xr_kernel<FMT, true> : gemv_xr_kernel<FMT, false>;
+  for (int64_t m0 = 0; m0 < m; m0 += kXrMaxM)
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * waves), 0, s, m_tile(p, x, m0, m, k, kXrMaxM));
+  return launch_status(op);
+}
+
+// Streamed matrix-core GEMV (affine codes, one stream per part).
+template <int FMT>
+qg_status run_gemv_mma(const char* op, const HostPart* parts, int nparts, const float* x, int64_t m, int64_t k,
+                       int gs, hipStream_t s) {
+  (void)hipGetLastError();
+  const GemvParams p = gemv_params(parts, nparts, 1, false, 16, k, gs, row_bytes_of<FMT>(k));
+  // one workgroup per CU (the x tile fills most of the LDS), walking row groups
+  const int64_t grid = p.n_groups < device_cus() ? p.n_groups : device_cus();
+  for (int64_t m0 = 0; m0 < m; m0 += kMmaMaxM) {
+    const hipError_t e = launch_gemv_mma<FMT>((int)(k / 512), m_tile(p, x, m0, m, k, kMmaMaxM),
+                                              dim3((unsigned)grid), s);
+    if (e != hipSuccess) return launch_error(op, "launch setup failed", e);
   }
   return launch_status(op);
 }
 
-// Runs a part list on the chunked GEMV kernel (or on the plain one when
-// `plain`), over all m-tiles of x.
+// Plain kernel: one launch per part and m-chunk.
 template <int FMT, int NW>
-qg_status run_gemv(const char* op, const HostPart* parts, int nparts, const float* x, int64_t m, int64_t k,
-                   int gs, bool plain, hipStream_t s) {
+qg_status run_plain(const char* op, const HostPart* parts, int nparts, const float* x, int64_t m, int64_t k,
+                    int gs, hipStream_t s) {
   (void)hipGetLastError();
   const int64_t rb = row_bytes_of<FMT>(k);
-  if (plain) {
-    const dim3 block(256);
-    for (int pi = 0; pi < nparts; ++pi) {
-      const HostPart& hp = parts[pi];
-      for (int64_t m0 = 0; m0 < m; m0 += 65535) {
-        const int64_t mc = m - m0 < 65535 ? m - m0 : 65535;
-        PlainParams q{};
-        for (int st = 0; st < 2; ++st) {
-          q.w[st] = static_cast<const uint8_t*>(hp.w[st] ? hp.w[st] : hp.w[0]);
-          q.y[st] = (hp.y[st] ? hp.y[st] : hp.y[0]) + m0 * hp.ldy;
-        }
-        q.scales = hp.scales;
-        q.biases = hp.biases;
-        q.x = x + m0 * k;
-        q.ldy = hp.ldy;
-        q.row_bytes = rb;
-        q.n = (int)hp.n;
-        q.k = (int)k;
-        q.gs = gs;
-        const dim3 grid((unsigned)cdiv(hp.n, 256), (unsigned)mc);
-        hipLaunchKernelGGL((gemv_plain_kernel<FMT, NW>), grid, block, 0, s, q, (int)mc);
-      }
-    }
-    return launch_status(op);
-  }
-  if (xr_ok<FMT>(parts, nparts, NW, m, k, gs)) return run_gemv_xr<FMT>(op, parts, nparts, NW, x, m, k, gs, s);
-  const GemvPlan pl = plan_gemv<FMT>(m, k, NW);
-  const int mma = NW == 1 ? mma_pairs<FMT>(parts, nparts, m, k, gs) : 0;
-  const int ks = mma ? 0 : ks_chunks<FMT, NW>(pl, m, k);
-  const GemvGrid gg = grid_gemv<FMT>(pl, parts, nparts);
-  const int ks_wv = ks ? ks_waves<FMT>(k, pl.l) : 0;
-  const int rows_per_group = mma ? 16 : ks ? (int)(kWave / (pl.l / ks_wv) * pl.r) : (int)gg.groups_rows;
-  GemvParams p{};
-  int64_t groups = 0;
+  const dim3 block(256);
   for (int pi = 0; pi < nparts; ++pi) {
-    GemvPart& gp = p.part[pi];
-    for (int st = 0; st < 2; ++st) {
-      gp.w[st] = static_cast<const uint8_t*>(parts[pi].w[st] ? parts[pi].w[st] : parts[pi].w[0]);
-      gp.y[st] = parts[pi].y[st] ? parts[pi].y[st] : parts[pi].y[0];
-    }
-    gp.scales = parts[pi].scales;
-    gp.biases = parts[pi].biases;
-    gp.ldy = parts[pi].ldy;
-    gp.n = (int)parts[pi].n;
-    gp.group0 = (int)groups;
-    groups += cdiv(parts[pi].n, rows_per_group);
-  }
-  p.parts = nparts;
-  p.n_groups = (int)groups;
-  p.row_bytes = rb;
-  p.k = (int)k;
-  p.gs = gs;
-  p.kt = pl.kt;
-  if (mma) {
-    // one workgroup per CU (the x tile fills most of the LDS), walking row groups
-    const int64_t grid = groups < device_cus() ? groups : device_cus();
-    for (int64_t m0 = 0; m0 < m; m0 += kMmaMaxM) {
-      GemvParams q = p;
+    const HostPart& hp = parts[pi];
+    for (int64_t m0 = 0; m0 < m; m0 += 65535) {
+      const int64_t mc = m - m0 < 65535 ? m - m0 : 65535;
+      PlainParams q{};
+      for (int st = 0; st < 2; ++st) {
+        q.w[st] = static_cast<const uint8_t*>(hp.w[st] ? hp.w[st] : hp.w[0]);
+        q.y[st] = (hp.y[st] ? hp.y[st] : hp.y[0]) + m0 * hp.ldy;
+      }
+      q.scales = hp.scales;
+      q.biases = hp.biases;
       q.x = x + m0 * k;
-      for (int pi = 0; pi < nparts; ++pi) q.part[pi].y[0] = p.part[pi].y[0] + m0 * p.part[pi].ldy;
-      q.m_rows = (int)(m - m0 < kMmaMaxM ? m - m0 : kMmaMaxM);
-      const hipError_t e = launch_gemv_mma<FMT>(mma, q, dim3((unsigned)grid), s);
-      if (e != hipSuccess) return launch_error(op, "launch setup failed", e);
+      q.ldy = hp.ldy;
+      q.row_bytes = rb;
+      q.n = (int)hp.n;
+      q.k = (int)k;
+      q.gs = gs;
+      const dim3 grid((unsigned)cdiv(hp.n, 256), (unsigned)mc);
+      hipLaunchKernelGGL((gemv_plain_kernel<FMT, NW>), grid, block, 0, s, q, (int)mc);
     }
-    return launch_status(op);
   }
+  return launch_status(op);
+}
+
+// FMA GEMV: the K-sliced kernel where it applies, else the chunked one (same
+// bits), over all m-tiles of x.
+template <int FMT, int NW>
+qg_status run_gemv_fma(const char* op, const CallCfg& cfg, const HostPart* parts, int nparts, const float* x,
+                       int64_t m, int64_t k, int gs, hipStream_t s) {
+  (void)hipGetLastError();
+  const GemvPlan pl = plan_gemv<FMT>(m, k, NW);
+  const int ks = ks_chunks<FMT, NW>(cfg, pl, k);
   if (ks) {
     // Up to 16 waves per CU (two 8-wave or four 4-wave workgroups; they are
     // resident together where the kernel stays within 128 VGPRs), walking row
     // groups beyond that.  Measured on Q4_K K = 4096 at N = 6144 ... 28672
-    // rows: 3-12% faster than 8 waves per CU.  Tuning override QG_GEMV_KS=B
-    // (B times 8 waves per CU; 0 keeps the chunked kernel).
-    int64_t bpc = 2;
-    if (const char* env = getenv("QG_GEMV_KS")) bpc = atoi(env) > 0 ? atoi(env) : 2;
-    const int64_t cap = bpc * (8 / ks_wv) * device_cus();
-    const int64_t grid = groups < cap ? groups : cap;
+    // rows: 3-12% faster than 8 waves per CU.
+    const int ks_wv = ks_waves<FMT>(k, pl.l);
+    const int64_t rows_per_group = kWave / (pl.l / ks_wv) * pl.r;
+    GemvParams p = gemv_params(parts, nparts, NW, false, rows_per_group, k, gs, row_bytes_of<FMT>(k));
+    p.kt = pl.kt;
+    const int64_t cap = 2 * (8 / ks_wv) * device_cus();
+    const int64_t grid = p.n_groups < cap ? p.n_groups : cap;
     for (int64_t m0 = 0; m0 < m; m0 += pl.mt) {
-      GemvParams q = p;
-      q.x = x + m0 * k;
-      for (int pi = 0; pi < nparts; ++pi)
-        for (int st = 0; st < 2; ++st) q.part[pi].y[st] = p.part[pi].y[st] + m0 * p.part[pi].ldy;
-      q.m_rows = (int)(m - m0 < pl.mt ? m - m0 : pl.mt);
-      const hipError_t e = launch_gemv_ks<FMT, NW>(pl, ks, q, dim3((unsigned)grid), s);
+      const hipError_t e = launch_gemv_ks<FMT, NW>(pl, ks, m_tile(p, x, m0, m, k, pl.mt), dim3((unsigned)grid), s);
       if (e != hipSuccess) return launch_error(op, "launch setup failed", e);
     }
     return launch_status(op);
   }
-  const int64_t grid = gg.grid;
+  const GemvGrid gg = grid_gemv<FMT>(pl, parts, nparts);
+  GemvParams p = gemv_params(parts, nparts, NW, false, gg.groups_rows, k, gs, row_bytes_of<FMT>(k));
+  p.kt = pl.kt;
   const dim3 block(64 * gg.waves);
   for (int64_t m0 = 0; m0 < m; m0 += pl.mt) {
-    GemvParams q = p;
-    q.x = x + m0 * k;
-    for (int pi = 0; pi < nparts; ++pi)
-      for (int st = 0; st < 2; ++st) q.part[pi].y[st] = p.part[pi].y[st] + m0 * p.part[pi].ldy;
-    q.m_rows = (int)(m - m0 < pl.mt ? m - m0 : pl.mt);
-    const hipError_t e = launch_gemv_mt<FMT, NW>(pl, q, dim3((unsigned)grid), block, s);
+    const hipError_t e = launch_gemv_mt<FMT, NW>(pl, m_tile(p, x, m0, m, k, pl.mt), dim3((unsigned)gg.grid), block, s);
     if (e != hipSuccess) return launch_error(op, "launch setup failed", e);
   }
   return launch_status(op);
 }
 
 // ------------------------------------------------------------------ MFMA
-// The matrix-core path takes a part list when M reaches the threshold, K is a
-// whole number of 64-column stages, the group size is 32..512 and the weights
-// are aligned for its vector loads.
+// Bytes of the matrix-core path's scratch for M rows of x: x_hi and x_lo as
+// bf16 [M, K], and (formats with a bias term) the group sums of x as bf16 hi
+// and lo [M, K/gs], each array 256-byte aligned.
 template <int FMT>
-bool mfma_ok(const HostPart* parts, int nparts, int64_t m, int64_t k, int64_t gs) {
-  if (m < g_mfma_min_m.load() || k % 64 != 0 || gs < 32 || gs > 512) return false;
-  if (m * k >= k2G) return false;
-  const uintptr_t al = FMT == FMT_AFF || FMT == FMT_Q4K ? 16 : FMT == FMT_AFF4 ? 8 : 4;
-  for (int pi = 0; pi < nparts; ++pi) {
-    if (!aligned(parts[pi].w[0], al)) return false;
-    if (parts[pi].n * row_bytes_of<FMT>(k) >= k2G) return false;
-  }
-  return true;
+size_t mfma_scratch_bytes(int64_t m, int64_t k, int64_t gs) {
+  auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  const size_t bx = up((size_t)m * k * sizeof(__bf16));
+  const size_t bs = FMT == FMT_Q40 ? 0 : up((size_t)m * (k / gs) * sizeof(__bf16));
+  return 2 * bx + 2 * bs;
 }
 
-// x -> (x_hi, x_lo, group sums) in stream-ordered scratch, then one launch of
-// the matrix-core kernel over every part's column tiles.
+// x -> (x_hi, x_lo, group sums) in `scratch` (mfma_scratch_bytes, 256-byte
+// aligned), then one launch of the matrix-core kernel over every weight
+// stream's column tiles (both streams of a dual part are two parts of it).
 template <int FMT>
-qg_status run_mfma(const char* op, const HostPart* parts, int nparts, const float* x, int64_t m, int64_t k,
-                   int gs, hipStream_t s) {
+qg_status launch_mfma(const char* op, const HostPart* parts, int nparts, int nw, const float* x, int64_t m,
+                      int64_t k, int gs, void* scratch, hipStream_t s) {
+  if (nparts * nw > kMaxParts) return fail("%s: too many weight streams for one launch", op);
+  auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
   const int64_t groups = k / gs;
-  const size_t bytes_x = (size_t)m * k * sizeof(__bf16);
-  const size_t bytes_s = (size_t)m * groups * sizeof(__bf16);
-  const size_t bytes = 2 * bytes_x + 2 * bytes_s + 512;
-  (void)hipGetLastError();
-  void* scratch = nullptr;
-  hipError_t e = hipMallocAsync(&scratch, bytes, s);
-  if (e != hipSuccess) {
-    snprintf(g_err, sizeof(g_err), "%s: scratch allocation of %zu bytes failed: %s", op, bytes,
-             hipGetErrorString(e));
-    return QG_ELAUNCH;
-  }
-  auto align256 = [](void* p) {
-    return reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(p) + 255) & ~(uintptr_t)255);
-  };
   __bf16* xh = static_cast<__bf16*>(scratch);
-  __bf16* xl = xh + (size_t)m * k;
-  __bf16* sh = static_cast<__bf16*>(align256(xl + (size_t)m * k));
-  __bf16* sl = static_cast<__bf16*>(align256(sh + (size_t)m * groups));
+  __bf16* xl = reinterpret_cast<__bf16*>(reinterpret_cast<char*>(xh) + up((size_t)m * k * sizeof(__bf16)));
+  __bf16* sh = nullptr;
+  __bf16* sl = nullptr;
+  if constexpr (FMT != FMT_Q40) {
+    sh = reinterpret_cast<__bf16*>(reinterpret_cast<char*>(xl) + up((size_t)m * k * sizeof(__bf16)));
+    sl = reinterpret_cast<__bf16*>(reinterpret_cast<char*>(sh) + up((size_t)m * groups * sizeof(__bf16)));
+  }
   const int64_t items = m * (k / 8);
   hipLaunchKernelGGL(affine_prep_kernel, dim3((unsigned)cdiv(items, 256)), dim3(256), 0, s, x, xh, xl, sh, sl,
                      (int)m, (int)k, gs);
-  // Tile shape: 128x128 (16 waves) while that gives every other CU a tile,
-  // else 64x128 (8 waves, two workgroups per CU); both run four waves per
-  // SIMD.  Measured on MI355X: Q4_0 512x4096x4096 takes 107 us on 128 tiles
-  // of 128x128 and 100 us on 256 tiles of 64x128; the affine 512x8192x2048
-  // product 64 us on 256 tiles of 128x128 and 72 us on 512 of 64x128.  The
-  // arithmetic of an output does not depend on the shape.
-  const int64_t cus = device_cus();
-  auto tiles_for = [&](int sm) {
-    int64_t tn = 0;
-    for (int pi = 0; pi < nparts; ++pi) tn += cdiv(parts[pi].n, 128);
-    return cdiv(m, 64 * sm) * tn;
-  };
-  int sm = 2 * tiles_for(2) > cus ? 2 : 1;
-  // tuning override (same results either way): QG_MFMA_TILE=0 (128x128) or 1 (64x128)
-  if (const char* env = getenv("QG_MFMA_TILE")) {
-    const int t = atoi(env);
-    if (t == 0 || t == 1) sm = 2 - t;
-  }
   MfmaParams mp{};
   mp.xh = xh;
   mp.xl = xl;
   mp.sh = sh;
   mp.sl = sl;
   int64_t tiles_n = 0;
+  int np = 0;
   for (int pi = 0; pi < nparts; ++pi) {
-    MfmaPart& q = mp.part[pi];
-    q.w = static_cast<const uint8_t*>(parts[pi].w[0]);
-    q.scales = parts[pi].scales;
-    q.biases = parts[pi].biases;
-    q.y = parts[pi].y[0];
-    q.ldy = parts[pi].ldy;
-    q.n = (int)parts[pi].n;
-    q.tile0 = (int)tiles_n;
-    tiles_n += cdiv(parts[pi].n, 128);
+    for (int st = 0; st < nw; ++st) {
+      MfmaPart& q = mp.part[np++];
+      q.w = static_cast<const uint8_t*>(parts[pi].w[st]);
+      q.scales = parts[pi].scales;
+      q.biases = parts[pi].biases;
+      q.y = parts[pi].y[st];
+      q.ldy = parts[pi].ldy;
+      q.n = (int)parts[pi].n;
+      q.tile0 = (int)tiles_n;
+      tiles_n += cdiv(parts[pi].n, 128);
+    }
   }
-  mp.parts = nparts;
+  // Tile shape: 128x128 (16 waves) while that gives every other CU a tile,
+  // else 64x128 (8 waves, two workgroups per CU); both run four waves per
+  // SIMD.  Measured on MI355X: Q4_0 512x4096x4096 takes 107 us on 128 tiles
+  // of 128x128 and 100 us on 256 tiles of 64x128; the affine 512x8192x2048
+  // product 64 us on 256 tiles of 128x128 and 72 us on 512 of 64x128.  The
+  // arithmetic of an output does not depend on the shape.
+  const int sm = 2 * cdiv(m, 128) * tiles_n > device_cus() ? 2 : 1;
+  mp.parts = np;
   mp.row_bytes = row_bytes_of<FMT>(k);
   mp.m = (int)m;
   mp.k = (int)k;
@@ -711,7 +685,7 @@ qg_status run_mfma(const char* op, const HostPart* parts, int nparts, const floa
   const dim3 grid((unsigned)(mp.tiles_m * mp.tiles_n));
   // 128x128 runs as 4 x 2 wave pairs of 32x64 sub-tiles, 64x128 as 2 x 2
   const dim3 block((unsigned)(512 * sm));
-  const bool multi = nparts > 1;
+  const bool multi = np > 1;
   if (sm == 2) {
     if (multi) hipLaunchKernelGGL((qmm_mfma_kernel<FMT, true, 4, 2, 2>), grid, block, 0, s, mp);
     else hipLaunchKernelGGL((qmm_mfma_kernel<FMT, false, 4, 2, 2>), grid, block, 0, s, mp);
@@ -719,10 +693,67 @@ qg_status run_mfma(const char* op, const HostPart* parts, int nparts, const floa
     if (multi) hipLaunchKernelGGL((qmm_mfma_kernel<FMT, true, 2, 2, 2>), grid, block, 0, s, mp);
     else hipLaunchKernelGGL((qmm_mfma_kernel<FMT, false, 2, 2, 2>), grid, block, 0, s, mp);
   }
-  const qg_status ls = launch_status(op);
+  return launch_status(op);
+}
+
+// The matrix-core path with stream-ordered scratch, allocated and released on
+// the caller's stream for this call.
+template <int FMT>
+qg_status run_mfma(const char* op, const HostPart* parts, int nparts, int nw, const float* x, int64_t m, int64_t k,
+                   int gs, hipStream_t s) {
+  const size_t bytes = mfma_scratch_bytes<FMT>(m, k, gs);
+  (void)hipGetLastError();
+  void* scratch = nullptr;
+  hipError_t e = hipMallocAsync(&scratch, bytes, s);
+  if (e != hipSuccess) {
+    snprintf(g_err, sizeof(g_err), "%s: scratch allocation of %zu bytes failed: %s", op, bytes,
+             hipGetErrorString(e));
+    return QG_ELAUNCH;
+  }
+  const qg_status ls = launch_mfma<FMT>(op, parts, nparts, nw, x, m, k, gs, scratch, s);
   e = hipFreeAsync(scratch, s);
   if (ls == QG_OK && e != hipSuccess) return launch_error(op, "scratch release failed", e);
   return ls;
+}
+
+// Runs one part list whose weight streams all take `path`.
+template <int FMT, int NW>
+qg_status run_path(const char* op, Path path, const CallCfg& cfg, const HostPart* parts, int nparts,
+                   const float* x, int64_t m, int64_t k, int gs, hipStream_t s) {
+  switch (path) {
+    case P_MFMA: return run_mfma<FMT>(op, parts, nparts, NW, x, m, k, gs, s);
+    case P_PLAIN: return run_plain<FMT, NW>(op, parts, nparts, x, m, k, gs, s);
+    case P_XR: return run_gemv_xr<FMT>(op, parts, nparts, NW, x, m, k, gs, s);
+    case P_MMA:
+      if constexpr (NW == 1) return run_gemv_mma<FMT>(op, parts, nparts, x, m, k, gs, s);
+      break;
+    case P_FMA: return run_gemv_fma<FMT, NW>(op, cfg, parts, nparts, x, m, k, gs, s);
+  }
+  snprintf(g_err, sizeof(g_err), "%s: no kernel for this path", op);
+  return QG_ELAUNCH;
+}
+
+// A part list of single-stream parts: each part takes the path its single
+// call would take; parts of one path share a launch.
+template <int FMT>
+qg_status run_parts(const char* op, const CallCfg& cfg, const HostPart* parts, int nparts, const float* x,
+                    int64_t m, int64_t k, int gs, hipStream_t s) {
+  Path path[kMaxParts];
+  for (int pi = 0; pi < nparts; ++pi) path[pi] = path_of<FMT>(cfg, m, k, gs, parts[pi].w[0], parts[pi].n);
+  bool done[kMaxParts] = {};
+  for (int pi = 0; pi < nparts; ++pi) {
+    if (done[pi]) continue;
+    HostPart group[kMaxParts];
+    int ng = 0;
+    for (int pj = pi; pj < nparts; ++pj)
+      if (!done[pj] && path[pj] == path[pi]) {
+        group[ng++] = parts[pj];
+        done[pj] = true;
+      }
+    const qg_status st = run_path<FMT, 1>(op, path[pi], cfg, group, ng, x, m, k, gs, s);
+    if (st != QG_OK) return st;
+  }
+  return QG_OK;
 }
 
 // ------------------------------------------------------------------ checks
@@ -779,17 +810,6 @@ HostPart single_part(const void* w, const float* scales, const float* biases, fl
   return hp;
 }
 
-// The affine product over a part list (u8 or packed codes).
-template <int FMT>
-qg_status run_affine(const char* op, const HostPart* parts, int nparts, const float* x, int64_t m, int64_t k,
-                     int64_t gs, hipStream_t s) {
-  if (mfma_ok<FMT>(parts, nparts, m, k, gs)) return run_mfma<FMT>(op, parts, nparts, x, m, k, (int)gs, s);
-  // the chunked kernel takes 32-code chunks inside one group
-  bool plain = (k % 32 != 0) || gs < 32;
-  for (int pi = 0; pi < nparts; ++pi) plain = plain || !aligned(parts[pi].w[0], 16);
-  return run_gemv<FMT, 1>(op, parts, nparts, x, m, k, (int)gs, plain, s);
-}
-
 }  // namespace
 
 extern "C" {
@@ -804,15 +824,22 @@ qg_status qg_set_mfma_min_m(int64_t m) {
 
 int64_t qg_get_mfma_min_m(void) { return g_mfma_min_m.load(); }
 
+qg_status qg_set_kernel_mask(uint32_t mask) {
+  if (mask & ~kAllKernels) return fail("qg_set_kernel_mask: unknown bits 0x%x", (unsigned)(mask & ~kAllKernels));
+  g_kernel_mask.store(mask);
+  return QG_OK;
+}
+
+uint32_t qg_get_kernel_mask(void) { return g_kernel_mask.load(); }
+
 qg_status qgemv_q4_0(const void* w, const float* x, float* y, int64_t M, int64_t N, int64_t K,
                      void* stream) {
   const char* op = "qgemv_q4_0";
   qg_status st = q40_common(op, w, x, y, M, N, K);
   if (st != QG_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  const CallCfg cfg = call_cfg();
   const HostPart hp = single_part(w, nullptr, nullptr, y, N, N);
-  if (mfma_ok<FMT_Q40>(&hp, 1, M, K, 32)) return run_mfma<FMT_Q40>(op, &hp, 1, x, M, K, 32, s);
-  return run_gemv<FMT_Q40, 1>(op, &hp, 1, x, M, K, 32, K % 64 != 0, s);
+  return run_parts<FMT_Q40>(op, cfg, &hp, 1, x, M, K, 32, static_cast<hipStream_t>(stream));
 }
 
 qg_status qgemv_dual_q4_0(const void* w_a, const void* w_b, const float* x, float* y_a, float* y_b,
@@ -824,14 +851,22 @@ qg_status qgemv_dual_q4_0(const void* w_a, const void* w_b, const float* x, floa
   if (st != QG_OK) return st;
   if (y_a == y_b) return fail("%s: dst_a and dst_b must be different buffers", op);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const HostPart two[2] = {single_part(w_a, nullptr, nullptr, y_a, N, N),
+  const CallCfg cfg = call_cfg();
+  const HostPart one[2] = {single_part(w_a, nullptr, nullptr, y_a, N, N),
                            single_part(w_b, nullptr, nullptr, y_b, N, N)};
-  // matrix cores: both weights as two parts of one launch (one x preparation)
-  if (mfma_ok<FMT_Q40>(two, 2, M, K, 32)) return run_mfma<FMT_Q40>(op, two, 2, x, M, K, 32, s);
-  HostPart hp = two[0];
+  const Path pa = path_of<FMT_Q40>(cfg, M, K, 32, w_a, N);
+  const Path pb = path_of<FMT_Q40>(cfg, M, K, 32, w_b, N);
+  // the two weights on different paths (e.g. one of them not 16-byte
+  // aligned): each runs as its single call would
+  if (pa != pb) {
+    st = run_path<FMT_Q40, 1>(op, pa, cfg, &one[0], 1, x, M, K, 32, s);
+    return st != QG_OK ? st : run_path<FMT_Q40, 1>(op, pb, cfg, &one[1], 1, x, M, K, 32, s);
+  }
+  // one pass over x for both weights
+  HostPart hp = one[0];
   hp.w[1] = w_b;
   hp.y[1] = y_b;
-  return run_gemv<FMT_Q40, 2>(op, &hp, 1, x, M, K, 32, K % 64 != 0, s);
+  return run_path<FMT_Q40, 2>(op, pa, cfg, &hp, 1, x, M, K, 32, s);
 }
 
 qg_status qgemv_q4_k(const void* w, const float* x, float* y, int64_t M, int64_t N, int64_t K,
@@ -843,10 +878,9 @@ qg_status qgemv_q4_k(const void* w, const float* x, float* y, int64_t M, int64_t
   if (!w) return fail("%s: null weight pointer", op);
   st = check_xy(op, x, y);
   if (st != QG_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  const CallCfg cfg = call_cfg();
   const HostPart hp = single_part(w, nullptr, nullptr, y, N, N);
-  if (mfma_ok<FMT_Q4K>(&hp, 1, M, K, 32)) return run_mfma<FMT_Q4K>(op, &hp, 1, x, M, K, 32, s);
-  return run_gemv<FMT_Q4K, 1>(op, &hp, 1, x, M, K, 32, !aligned(w, 16), s);
+  return run_parts<FMT_Q4K>(op, cfg, &hp, 1, x, M, K, 32, static_cast<hipStream_t>(stream));
 }
 
 qg_status qgemv_q4_k_multi(const void* const* w, float* const* y, const int64_t* n, const int64_t* ldy,
@@ -860,7 +894,6 @@ qg_status qgemv_q4_k_multi(const void* const* w, float* const* y, const int64_t*
   if (K % 256 != 0) return fail("%s: K (%lld) must be a multiple of 256", op, (long long)K);
   if (!x || !aligned(x, 4)) return fail("%s: x must be a non-null 4-byte aligned pointer", op);
   HostPart hp[kMaxParts];
-  bool misaligned = false;
   for (int64_t p = 0; p < parts; ++p) {
     if (n[p] < 1 || n[p] > kMaxDim)
       return fail("%s: part %lld: rows must be in [1, 2^30]; got %lld", op, (long long)p, (long long)n[p]);
@@ -870,13 +903,10 @@ qg_status qgemv_q4_k_multi(const void* const* w, float* const* y, const int64_t*
     if (!w[p]) return fail("%s: part %lld: null weight pointer", op, (long long)p);
     st = check_xy(op, x, y[p]);
     if (st != QG_OK) return st;
-    misaligned = misaligned || !aligned(w[p], 16);
     hp[p] = single_part(w[p], nullptr, nullptr, y[p], ldy[p], n[p]);
   }
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int np = (int)parts;
-  if (mfma_ok<FMT_Q4K>(hp, np, M, K, 32)) return run_mfma<FMT_Q4K>(op, hp, np, x, M, K, 32, s);
-  return run_gemv<FMT_Q4K, 1>(op, hp, np, x, M, K, 32, misaligned, s);
+  // each part on the path of its own single call; parts of one path share a launch
+  return run_parts<FMT_Q4K>(op, call_cfg(), hp, (int)parts, x, M, K, 32, static_cast<hipStream_t>(stream));
 }
 
 qg_status qmm_affine_t(const float* x, const uint8_t* q, const float* scales, const float* biases,
@@ -891,7 +921,7 @@ qg_status qmm_affine_t(const float* x, const uint8_t* q, const float* scales, co
   st = check_xy(op, x, y);
   if (st != QG_OK) return st;
   const HostPart hp = single_part(q, scales, biases, y, N, N);
-  return run_affine<FMT_AFF>(op, &hp, 1, x, M, K, group_size, static_cast<hipStream_t>(stream));
+  return run_parts<FMT_AFF>(op, call_cfg(), &hp, 1, x, M, K, (int)group_size, static_cast<hipStream_t>(stream));
 }
 
 qg_status qmm_affine_t_packed(const float* x, const uint32_t* w_packed, const float* scales,
@@ -909,7 +939,7 @@ qg_status qmm_affine_t_packed(const float* x, const uint32_t* w_packed, const fl
   st = check_xy(op, x, y);
   if (st != QG_OK) return st;
   const HostPart hp = single_part(w_packed, scales, biases, y, N, N);
-  return run_affine<FMT_AFF4>(op, &hp, 1, x, M, K, group_size, static_cast<hipStream_t>(stream));
+  return run_parts<FMT_AFF4>(op, call_cfg(), &hp, 1, x, M, K, (int)group_size, static_cast<hipStream_t>(stream));
 }
 
 qg_status qmm_affine_t_qkv(const float* x, const uint8_t* q, const float* scales, const float* biases,
@@ -939,7 +969,10 @@ qg_status qmm_affine_t_qkv(const float* x, const uint8_t* q, const float* scales
     hp[i] = single_part(q + row0 * K, scales + row0 * groups, biases + row0 * groups, outs[i], span[i], span[i]);
     row0 += span[i];
   }
-  return run_affine<FMT_AFF>(op, hp, 3, x, M, K, group_size, static_cast<hipStream_t>(stream));
+  // the path of the product of the whole fused weight, which the result must equal
+  const CallCfg cfg = call_cfg();
+  const Path path = path_of<FMT_AFF>(cfg, M, K, group_size, q, N);
+  return run_path<FMT_AFF, 1>(op, path, cfg, hp, 3, x, M, K, (int)group_size, static_cast<hipStream_t>(stream));
 }
 
 qg_status qkv_split_f32(const float* qkv, float* q, float* k, float* v, int64_t seq, int64_t q_sp,

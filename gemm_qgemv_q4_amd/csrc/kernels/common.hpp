@@ -40,6 +40,24 @@ __device__ __forceinline__ float ubyte_f32(uint32_t v) {
   else return (float)((v >> (8 * I)) & 0xFFu);
 }
 
+// Four signed codes, one int8 per byte, as floats (v_cvt_f32_i32 with a
+// sign-extended byte source).
+__device__ __forceinline__ void signed_codes_f32(uint32_t v, float& q0, float& q1, float& q2, float& q3) {
+  q0 = (float)(int8_t)(v);
+  q1 = (float)(int8_t)(v >> 8);
+  q2 = (float)(int8_t)(v >> 16);
+  q3 = (float)(int8_t)(v >> 24);
+}
+
+// Q4_0 nibbles as signed int8 bytes 16 (q - 8), exact: flipping the top bit
+// of a 4-bit code q gives q - 8 in 4-bit two's complement, and placed in the
+// top half of a byte that reads as the int8 16 (q - 8).  The factor 16 is
+// taken out of the block scale (d / 16 is exact), so a block of codes 8
+// contributes exactly 0 and the sum is d * sum x (q - 8) as the format
+// defines it.
+__device__ __forceinline__ uint32_t q40_hi16(uint32_t q) { return (q ^ 0x88888888u) & 0xF0F0F0F0u; }
+__device__ __forceinline__ uint32_t q40_lo16(uint32_t q) { return ((q ^ 0x88888888u) << 4) & 0xF0F0F0F0u; }
+
 // DPP lane moves (gfx9 encodings): quad_perm [1,0,3,2], quad_perm [2,3,0,1],
 // row_half_mirror, row_mirror.
 template <int CTRL>

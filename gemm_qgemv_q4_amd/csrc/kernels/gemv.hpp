@@ -27,9 +27,11 @@
 //     float4 columns [m][e4][chunk] (e4 = which 4 elements of the chunk), so
 //     the lanes of a wave read consecutive 16-byte words (no bank conflicts)
 //     and every x word read feeds R*NW rows.  The per-32 sums of x are staged
-//     too, which lets the block offset (-8*d, -dmin*m, or the affine bias b)
-//     and the affine scale be applied once per 32 weights instead of once per
-//     weight: the inner loop is one code conversion and one FMA per weight.
+//     too, which lets the block offset (-dmin*m, or the affine bias b) and the
+//     scale be applied once per 32 weights instead of once per weight: the
+//     inner loop is one code conversion and one FMA per weight.  Q4_0 codes
+//     are converted as the signed values q - 8 (times 16, taken out of d), so
+//     its blocks need no offset term and a block of codes 8 adds exactly 0.
 //   * The lanes of a row are summed with a fixed xor butterfly: no atomics,
 //     and the arithmetic of one output does not depend on R, NW, MT, the
 //     number of waves or which part a row belongs to, which makes the dual
@@ -74,8 +76,11 @@ struct GemvParams {
 static_assert(offsetof(GemvParams, part) + offsetof(GemvPart, scales) == 64,
               "x, row_bytes, k, n_groups and part 0's w, y, n, group0 share the first 64 bytes");
 
+// CH: weights per chunk; SUMS: the format needs the per-32 sums of x (a
+// block offset or bias multiplies them).  Q4_0 decodes its codes as signed
+// values (q - 8) and has no offset term.
 template <int FMT> struct FmtTraits;
-template <> struct FmtTraits<FMT_Q40> { static constexpr int CH = 64; static constexpr bool SUMS = true; };
+template <> struct FmtTraits<FMT_Q40> { static constexpr int CH = 64; static constexpr bool SUMS = false; };
 template <> struct FmtTraits<FMT_Q4K> { static constexpr int CH = 64; static constexpr bool SUMS = true; };
 template <> struct FmtTraits<FMT_AFF> { static constexpr int CH = 32; static constexpr bool SUMS = true; };
 template <> struct FmtTraits<FMT_AFF4> { static constexpr int CH = 32; static constexpr bool SUMS = true; };
@@ -162,13 +167,15 @@ __device__ __forceinline__ void small_codes_f32(uint32_t v, float& q0, float& q1
 }
 
 // Per-half (32-weight) scale factors of a chunk: y += A0*dot0 + B0*sumx0 + A1*dot1 + B1*sumx1
+// (Q4_0: B = 0, not applied.)
 struct HalfScales { float a0, b0, a1, b1; };
 
 __device__ __forceinline__ HalfScales q40_scales(const ChunkQ40& c) {
-  // block 2t: d in bytes 0..1; block 2t+1: d in bytes 18..19 (high half of dword 4)
-  const float d0 = f16_bits_to_f32(c.a.x);
-  const float d1 = f16_bits_to_f32(c.b.x >> 16);
-  return {d0, -8.0f * d0, d1, -8.0f * d1};
+  // block 2t: d in bytes 0..1; block 2t+1: d in bytes 18..19 (high half of dword 4);
+  // the codes are read as 16 (q - 8)
+  const float d0 = f16_bits_to_f32(c.a.x) * 0.0625f;
+  const float d1 = f16_bits_to_f32(c.b.x >> 16) * 0.0625f;
+  return {d0, 0.0f, d1, 0.0f};
 }
 
 // Sub-blocks 2c and 2c+1 of a Q4_K super-block.  The 12 scale bytes S0 (bytes
@@ -190,9 +197,10 @@ __device__ __forceinline__ HalfScales q4k_scales(const ChunkQ4K& c, int cc) {
   return {d * ubyte_f32<0>(scp), -(dmin * ubyte_f32<0>(mp)), d * ubyte_f32<1>(scp), -(dmin * ubyte_f32<1>(mp))};
 }
 
-// The 8 dwords of nibble values (each byte 0..15) of half h (32 weights) of a
-// 64-weight chunk, in element order: dword i holds elements 4i .. 4i+3 of the
-// half.  Unpacking one half at a time keeps half the nibble registers live.
+// The 8 dwords of code bytes of half h (32 weights) of a 64-weight chunk, in
+// element order: dword i holds elements 4i .. 4i+3 of the half.  Q4_0: int8
+// bytes 16 (q - 8); Q4_K: nibble values 0..15.  Unpacking one half at a time
+// keeps half the code registers live.
 __device__ __forceinline__ void unpack_q40(const ChunkQ40& c, int h, uint32_t (&v)[8]) {
   const uint32_t d[9] = {c.a.x, c.a.y, c.a.z, c.a.w, c.b.x, c.b.y, c.b.z, c.b.w, c.c};
 #pragma unroll
@@ -200,8 +208,8 @@ __device__ __forceinline__ void unpack_q40(const ChunkQ40& c, int h, uint32_t (&
     // block 2t: nibble bytes start at byte 2 -> realign across dwords 0..4;
     // block 2t+1: nibbles at bytes 20..35 = dwords 5..8
     const uint32_t q = h == 0 ? __builtin_amdgcn_alignbyte(d[i + 1], d[i], 2) : d[5 + i];
-    v[i] = opaque(q & 0x0F0F0F0Fu);             // elements 4i..4i+3 of the block
-    v[4 + i] = opaque((q >> 4) & 0x0F0F0F0Fu);  // elements 16+4i.. of the block
+    v[i] = q40_lo16(q);      // elements 4i..4i+3 of the block (low nibbles)
+    v[4 + i] = q40_hi16(q);  // elements 16+4i.. of the block (high nibbles)
   }
 }
 
@@ -217,13 +225,17 @@ __device__ __forceinline__ void unpack_q4k(const ChunkQ4K& c, int h, uint32_t (&
 // before any of them is used: all reads are in flight together instead of two
 // at a time, so a wave waits for LDS once per chunk.  (Only the timing of the
 // reads changes.)
-template <int NE4>
+template <int NE4, bool SUMS>
 __device__ __forceinline__ void preload_x(const f32x4* xs, const float* xsum, int ctp, int t, f32x4 (&xall)[NE4],
                                           float (&sall)[2]) {
 #pragma unroll
   for (int e4 = 0; e4 < NE4; ++e4) xall[e4] = xs[e4 * ctp + t];
-  sall[0] = xsum[t * 2];
-  sall[1] = NE4 > 8 ? xsum[t * 2 + 1] : 0.0f;  // 32-element chunks have one sum
+  if constexpr (SUMS) {
+    sall[0] = xsum[t * 2];
+    sall[1] = NE4 > 8 ? xsum[t * 2 + 1] : 0.0f;  // 32-element chunks have one sum
+  } else {
+    sall[0] = sall[1] = 0.0f;
+  }
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -250,7 +262,7 @@ __device__ __forceinline__ void compute_chunk(const typename ChunkOf<FMT>::T (&c
         for (int m = 0; m < MT; ++m) sub[s][r][m] = 0.0f;
     f32x4 xall[MT == 1 ? NE4 : 1];
     float sall[2];
-    if constexpr (MT == 1) preload_x<NE4>(xs, xsum, ctp, t, xall, sall);
+    if constexpr (MT == 1) preload_x<NE4, true>(xs, xsum, ctp, t, xall, sall);
 #pragma unroll
     for (int e4 = 0; e4 < NE4; ++e4) {
       f32x4 xv[MT];
@@ -301,9 +313,10 @@ __device__ __forceinline__ void compute_chunk(const typename ChunkOf<FMT>::T (&c
         if constexpr (FMT == FMT_Q40) hs[s][r] = q40_scales(ch[s][r]);
         else hs[s][r] = q4k_scales(ch[s][r], tg & 3);
       }
+    constexpr bool SUMS = FmtTraits<FMT>::SUMS;
     f32x4 xall[MT == 1 ? NE4 : 1];
     float sall[2];
-    if constexpr (MT == 1) preload_x<NE4>(xs, xsum, ctp, t, xall, sall);
+    if constexpr (MT == 1) preload_x<NE4, SUMS>(xs, xsum, ctp, t, xall, sall);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       uint32_t nib[NW][R][8];
@@ -332,7 +345,8 @@ __device__ __forceinline__ void compute_chunk(const typename ChunkOf<FMT>::T (&c
 #pragma unroll
           for (int r = 0; r < R; ++r) {
             float q0, q1, q2, q3;
-            small_codes_f32(nib[s][r][e], q0, q1, q2, q3);
+            if constexpr (FMT == FMT_Q40) signed_codes_f32(nib[s][r][e], q0, q1, q2, q3);
+            else small_codes_f32(nib[s][r][e], q0, q1, q2, q3);
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
               float a = sub[s][r][m];
@@ -344,10 +358,11 @@ __device__ __forceinline__ void compute_chunk(const typename ChunkOf<FMT>::T (&c
             }
           }
       }
-      // fold this 32-weight half: acc += A*dot + B*sum(x)
+      // fold this 32-weight half: acc += A*dot + B*sum(x)  (Q4_0: acc += A*dot)
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        const float sx = MT == 1 ? sall[h] : xsum[(m * ct_max + t) * 2 + h];
+        float sx = 0.0f;
+        if constexpr (SUMS) sx = MT == 1 ? sall[h] : xsum[(m * ct_max + t) * 2 + h];
 #pragma unroll
         for (int s = 0; s < NW; ++s)
 #pragma unroll
@@ -356,7 +371,7 @@ __device__ __forceinline__ void compute_chunk(const typename ChunkOf<FMT>::T (&c
             const float B = h == 0 ? hs[s][r].b0 : hs[s][r].b1;
             float a = acc[s][r][m];
             a = __builtin_fmaf(A, sub[s][r][m], a);
-            a = __builtin_fmaf(B, sx, a);
+            if constexpr (SUMS) a = __builtin_fmaf(B, sx, a);
             acc[s][r][m] = a;
           }
       }
@@ -614,6 +629,8 @@ __global__ void __launch_bounds__(512) gemv_ks_kernel(GemvParams p) {
   constexpr int XP = U + 1;              // LDS pitch in float4s (odd: spreads banks on the staging writes)
   constexpr int XS = LW * NE4 / kWave;   // float4s of x per lane and chunk slice
   static_assert(XS >= 1 && XS * kWave == LW * NE4, "whole float4s of x per lane");
+  constexpr bool SUMS = FmtTraits<FMT>::SUMS;
+  constexpr int NSUM = SUMS ? MT * 2 * U : 0;  // per-32 sums of x per wave
   using Chunk = typename ChunkOf<FMT>::T;
 
   extern __shared__ f32x4 smem[];
@@ -623,9 +640,9 @@ __global__ void __launch_bounds__(512) gemv_ks_kernel(GemvParams p) {
   const int c = lane % LW;
   const int vl = LW * wv + c;
   const int n_chunks = p.k / CH;
-  f32x4* xs = smem + wv * (MT * NE4 * XP);                                                // [m][e4][u] of this wave
-  float* xsum = reinterpret_cast<float*>(smem + WV * MT * NE4 * XP) + wv * (MT * 2 * U);  // [m][u][2]
-  float* red = reinterpret_cast<float*>(smem + WV * MT * NE4 * XP) + WV * MT * 2 * U;     // [2][NW][WV][ROWS][MT]
+  f32x4* xs = smem + wv * (MT * NE4 * XP);                                         // [m][e4][u] of this wave
+  float* xsum = reinterpret_cast<float*>(smem + WV * MT * NE4 * XP) + wv * NSUM;  // [m][u][2]
+  float* red = reinterpret_cast<float*>(smem + WV * MT * NE4 * XP) + WV * NSUM;   // [2][NW][WV][ROWS][MT]
 
   // Weights and rows of group g for this lane (rows are clamped for the
   // loads; rows past the part's end are not stored).
@@ -703,9 +720,11 @@ __global__ void __launch_bounds__(512) gemv_ks_kernel(GemvParams p) {
         const int e4 = li % NE4;
         const int u = LW * (j / XS) + li / NE4;
         if (f < n4) xs[(m * NE4 + e4) * XP + u] = xv[m][j];
-        // sum of each 32-element half: 8 consecutive float4s on 8 consecutive lanes
-        const float sm = group_sum(((xv[m][j].x + xv[m][j].y) + xv[m][j].z) + xv[m][j].w, 8);
-        if (f < n4 && (e4 & 7) == 0) xsum[(m * U + u) * 2 + (e4 >> 3)] = sm;
+        if constexpr (SUMS) {
+          // sum of each 32-element half: 8 consecutive float4s on 8 consecutive lanes
+          const float sm = group_sum(((xv[m][j].x + xv[m][j].y) + xv[m][j].z) + xv[m][j].w, 8);
+          if (f < n4 && (e4 & 7) == 0) xsum[(m * U + u) * 2 + (e4 >> 3)] = sm;
+        }
       }
     // LDS operations of one wave complete in order; this only keeps the
     // compiler from moving the reads above the writes.
@@ -784,8 +803,10 @@ __global__ void __launch_bounds__(512) gemv_ks_kernel(GemvParams p) {
 // ---------------------------------------------------------------------------
 // Plain kernel for shapes and alignments the chunked kernel does not take
 // (K not a multiple of 64 for Q4_0, misaligned Q4_K rows, affine K % 32 != 0,
-// group_size < 32 or misaligned codes): one thread per output, sequential f32
-// sum over K.  Launched once per part.
+// group_size < 32 or misaligned codes): one thread per output.  Launched once
+// per part.  The sum over K is split so that no serial f32 chain is longer
+// than 64 terms: a sequential chain over each 32-element piece of K, the piece
+// sums added 64 at a time into the next level, and so on, in a fixed order.
 struct PlainParams {
   const uint8_t* w[2];
   const float* scales;
@@ -797,6 +818,38 @@ struct PlainParams {
   int n, k, gs;
 };
 
+// Weight k of a row of the plain kernel's format, decoded to f32 (Q4_0: exactly
+// d (q - 8); Q4_K: one rounding of d sc q - dmin m; affine: one rounding of s q + b).
+template <int FMT>
+__device__ __forceinline__ float plain_weight(const PlainParams& p, const uint8_t* row, int n, int k) {
+  if constexpr (FMT == FMT_Q40) {
+    const uint8_t* blk = row + 18 * (k / 32);
+    const uint32_t d = blk[0] | ((uint32_t)blk[1] << 8);
+    const int j = k % 32;
+    const uint32_t byte = blk[2 + (j & 15)];
+    const int nib = j < 16 ? (int)(byte & 15u) : (int)(byte >> 4);
+    return f16_bits_to_f32(d) * (float)(nib - 8);
+  } else if constexpr (FMT == FMT_Q4K) {
+    const uint8_t* sb = row + 144 * (k / 256);
+    const int e = k % 256;
+    const int j = e / 32;
+    const float d = f16_bits_to_f32(sb[0] | ((uint32_t)sb[1] << 8));
+    const float dmin = f16_bits_to_f32(sb[2] | ((uint32_t)sb[3] << 8));
+    int sc, mn;
+    q4k_sc_m(sb + 4, j, sc, mn);
+    const uint32_t byte = sb[16 + 32 * (e / 64) + (e % 32)];
+    const int q = (e % 64) < 32 ? (int)(byte & 15u) : (int)(byte >> 4);
+    return __builtin_fmaf(d * (float)sc, (float)q, -(dmin * (float)mn));
+  } else {
+    const int groups = p.k / p.gs;
+    const size_t gi = (size_t)n * groups + k / p.gs;
+    uint32_t code;
+    if constexpr (FMT == FMT_AFF) code = row[k];
+    else code = (row[k >> 1] >> (4 * (k & 1))) & 15u;
+    return __builtin_fmaf(p.scales[gi], (float)code, p.biases[gi]);
+  }
+}
+
 template <int FMT, int NW>
 __global__ void __launch_bounds__(256) gemv_plain_kernel(PlainParams p, int m_count) {
   const int n = blockIdx.x * blockDim.x + threadIdx.x;
@@ -806,38 +859,27 @@ __global__ void __launch_bounds__(256) gemv_plain_kernel(PlainParams p, int m_co
 #pragma unroll
   for (int s = 0; s < NW; ++s) {
     const uint8_t* row = p.w[s] + (size_t)n * (size_t)p.row_bytes;
-    float a = 0.0f;
-    for (int k = 0; k < p.k; ++k) {
-      float w;
-      if constexpr (FMT == FMT_Q40) {
-        const uint8_t* blk = row + 18 * (k / 32);
-        const uint32_t d = blk[0] | ((uint32_t)blk[1] << 8);
-        const int j = k % 32;
-        const uint32_t byte = blk[2 + (j & 15)];
-        const int nib = j < 16 ? (int)(byte & 15u) : (int)(byte >> 4);
-        w = f16_bits_to_f32(d) * (float)(nib - 8);
-      } else if constexpr (FMT == FMT_Q4K) {
-        const uint8_t* sb = row + 144 * (k / 256);
-        const int e = k % 256;
-        const int j = e / 32;
-        const float d = f16_bits_to_f32(sb[0] | ((uint32_t)sb[1] << 8));
-        const float dmin = f16_bits_to_f32(sb[2] | ((uint32_t)sb[3] << 8));
-        int sc, mn;
-        q4k_sc_m(sb + 4, j, sc, mn);
-        const uint32_t byte = sb[16 + 32 * (e / 64) + (e % 32)];
-        const int q = (e % 64) < 32 ? (int)(byte & 15u) : (int)(byte >> 4);
-        w = __builtin_fmaf(d * (float)sc, (float)q, -(dmin * (float)mn));
-      } else {
-        const int groups = p.k / p.gs;
-        const size_t gi = (size_t)n * groups + k / p.gs;
-        uint32_t code;
-        if constexpr (FMT == FMT_AFF) code = row[k];
-        else code = (row[k >> 1] >> (4 * (k & 1))) & 15u;
-        w = __builtin_fmaf(p.scales[gi], (float)code, p.biases[gi]);
+    // s1 adds up to 64 piece sums, s2 up to 64 values of s1, ... (K < 2^31
+    // needs five levels)
+    float s1 = 0.0f, s2 = 0.0f, s3 = 0.0f, s4 = 0.0f, s5 = 0.0f;
+    int c1 = 0, c2 = 0, c3 = 0, c4 = 0;
+    for (int k0 = 0; k0 < p.k; k0 += 32) {
+      const int k1 = p.k - k0 < 32 ? p.k : k0 + 32;
+      float a = 0.0f;
+      for (int k = k0; k < k1; ++k) a = __builtin_fmaf(xr[k], plain_weight<FMT>(p, row, n, k), a);
+      s1 += a;
+      if (++c1 == 64) {
+        s2 += s1, s1 = 0.0f, c1 = 0;
+        if (++c2 == 64) {
+          s3 += s2, s2 = 0.0f, c2 = 0;
+          if (++c3 == 64) {
+            s4 += s3, s3 = 0.0f, c3 = 0;
+            if (++c4 == 64) s5 += s4, s4 = 0.0f, c4 = 0;
+          }
+        }
       }
-      a = __builtin_fmaf(xr[k], w, a);
     }
-    p.y[s][(size_t)m * p.ldy + n] = a;
+    p.y[s][(size_t)m * p.ldy + n] = (((s5 + s4) + s3) + s2) + s1;
   }
 }
 

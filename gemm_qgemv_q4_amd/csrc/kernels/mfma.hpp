@@ -5,11 +5,13 @@
 // with X_g[m] = sum_{k in g} x[m,k]:
 //   affine (u8 or packed codes): s, b from the scale and bias tensors
 //                                         [mlx-native qmm_affine.rs]
-//   Q4_0: groups of 32, s = d, b = -8 d   [mlx-native fused_dual_proj_q4_0.rs]
+//   Q4_0: groups of 32 with the signed codes 16 (q - 8), s = d / 16, no bias
+//                                         [mlx-native fused_dual_proj_q4_0.rs]
 //   Q4_K: groups of 32 (sub-blocks), s = d * sc_j, b = -dmin * m_j
 //                                         [ferrum-kernels q4_k_gemv_v2.rs]
 //
-// Precision: the codes (0..255) are exact in bf16.  x is split once into
+// Precision: the codes (0..255, or -128..112 for Q4_0) are exact in bf16, so
+// a Q4_0 block of codes 8 adds exactly 0.  x is split once into
 // x_hi = bf16(x) and x_lo = bf16(x - x_hi), so x_hi + x_lo carries 16
 // significant bits (relative error <= 2^-17); bf16 x bf16 products are exact
 // in the f32 MFMA accumulator.  Each group's partial product P_g = (x_hi +
@@ -35,9 +37,10 @@ namespace qg {
 
 // ---------------------------------------------------------------------------
 // x -> (x_hi, x_lo) bf16 and per-group sums X_g, the sums also split into
-// bf16 hi/lo (they feed the bias product on the matrix cores).  Each thread
-// converts 8 consecutive elements; the gs/8 threads of a group (gs <= 512)
-// combine their partial sums with a fixed-order DPP reduction.
+// bf16 hi/lo (they feed the bias product on the matrix cores; sh == nullptr:
+// no sums, for formats without a bias).  Each thread converts 8 consecutive
+// elements; the gs/8 threads of a group (gs <= 512) combine their partial sums
+// with a fixed-order DPP reduction.
 __global__ void __launch_bounds__(256) affine_prep_kernel(const float* __restrict__ x,
                                                           __bf16* __restrict__ xh,
                                                           __bf16* __restrict__ xl,
@@ -75,6 +78,7 @@ __global__ void __launch_bounds__(256) affine_prep_kernel(const float* __restric
     *reinterpret_cast<bf16x8*>(xh + base) = hv;
     *reinterpret_cast<bf16x8*>(xl + base) = lv;
   }
+  if (sh == nullptr) return;  // uniform across the grid
   const int lanes = gs / 8;  // threads per group (4..64)
   s = group_sum(s, lanes);
   if (ok && (c8 % lanes) == 0) {
@@ -120,8 +124,9 @@ __device__ __forceinline__ float group_scale(const MfmaPart& pt, long long row_b
   if constexpr (F == FMT_AFF || F == FMT_AFF4) {
     return pt.scales[(size_t)row * groups + g];
   } else if constexpr (F == FMT_Q40) {
+    // the codes enter as 16 (q - 8): d / 16 is exact
     const uint16_t d = *(const uint16_t*)(pt.w + (size_t)row * row_bytes + 18 * (size_t)g);
-    return f16_bits_to_f32(d);
+    return f16_bits_to_f32(d) * 0.0625f;
   } else {
     const uint8_t* sb = pt.w + (size_t)row * row_bytes + 144 * (size_t)(g >> 3);
     int sc, mn;
@@ -132,11 +137,9 @@ __device__ __forceinline__ float group_scale(const MfmaPart& pt, long long row_b
 template <int F>
 __device__ __forceinline__ float group_bias(const MfmaPart& pt, long long row_bytes, int groups, int row,
                                             int g) {
+  static_assert(F != FMT_Q40, "Q4_0 has no bias term");
   if constexpr (F == FMT_AFF || F == FMT_AFF4) {
     return pt.biases[(size_t)row * groups + g];
-  } else if constexpr (F == FMT_Q40) {
-    const uint16_t d = *(const uint16_t*)(pt.w + (size_t)row * row_bytes + 18 * (size_t)g);
-    return -8.0f * f16_bits_to_f32(d);
   } else {
     const uint8_t* sb = pt.w + (size_t)row * row_bytes + 144 * (size_t)(g >> 3);
     int sc, mn;
@@ -334,11 +337,16 @@ __global__ void __launch_bounds__(128 * SM * SN, 8 / TI) qmm_mfma_kernel(MfmaPar
       } else {
         nb[0] = b.x; nb[1] = b.y; nb[2] = b.z; nb[3] = b.w;
       }
-      // Q4_0: low nibbles are elements 0..15 of the block, high ones 16..31;
-      // Q4_K: low nibbles are the first sub-block of the chunk, high the second
-      const bool high = F == FMT_Q40 ? (kc & 1) : (kc >> 1);
+      // Q4_0: low nibbles are elements 0..15 of the block, high ones 16..31,
+      // as int8 bytes 16 (q - 8); Q4_K: low nibbles are the first sub-block of
+      // the chunk, high the second
+      if constexpr (F == FMT_Q40) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) cw[i] = high ? (nb[i] >> 4) & 0x0F0F0F0Fu : nb[i] & 0x0F0F0F0Fu;
+        for (int i = 0; i < 4; ++i) cw[i] = (kc & 1) ? q40_hi16(nb[i]) : q40_lo16(nb[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cw[i] = (kc >> 1) ? (nb[i] >> 4) & 0x0F0F0F0Fu : nb[i] & 0x0F0F0F0Fu;
+      }
     }
   };
   auto store = [&](int st, const Regs& r, int buf) {
@@ -352,15 +360,20 @@ __global__ void __launch_bounds__(128 * SM * SN, 8 / TI) qmm_mfma_kernel(MfmaPar
 #pragma unroll
     for (int i = 0; i < IB; ++i) {
       if (!b_mine) break;
-      // 16 codes -> 16 bf16 (exact: integers below 256)
+      // 16 codes -> 16 bf16 (exact: integers below 256, or the int8 Q4_0 codes)
       uint32_t cw[4];
       code_words(r.b[i], r.b4[i], b_kc[i], cw);
       bf16x8 lo, hi;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t wlo = cw[e >> 2], whi = cw[2 + (e >> 2)];
-        lo[e] = (__bf16)(float)((wlo >> (8 * (e & 3))) & 0xFFu);
-        hi[e] = (__bf16)(float)((whi >> (8 * (e & 3))) & 0xFFu);
+        const uint32_t wlo = cw[e >> 2] >> (8 * (e & 3)), whi = cw[2 + (e >> 2)] >> (8 * (e & 3));
+        if constexpr (F == FMT_Q40) {
+          lo[e] = (__bf16)(float)(int8_t)wlo;
+          hi[e] = (__bf16)(float)(int8_t)whi;
+        } else {
+          lo[e] = (__bf16)(float)(wlo & 0xFFu);
+          hi[e] = (__bf16)(float)(whi & 0xFFu);
+        }
       }
       *(bf16x8*)(sB[buf] + b_n[i] * kPitch + b_kc[i] * 16) = lo;
       *(bf16x8*)(sB[buf] + b_n[i] * kPitch + b_kc[i] * 16 + 8) = hi;
@@ -427,9 +440,10 @@ __global__ void __launch_bounds__(128 * SM * SN, 8 / TI) qmm_mfma_kernel(MfmaPar
   __syncthreads();
 
   // ---- bias term: acc += X[m, g] * b[n, g] over all groups, as a K = groups
-  // product on the matrix cores with X and b split into bf16 hi + lo
+  // product on the matrix cores with X and b split into bf16 hi + lo (Q4_0
+  // has none)
   constexpr int BR = BM > BN ? BM : BN;
-  for (int g0 = 0; g0 < groups; g0 += 32) {
+  if constexpr (F != FMT_Q40) for (int g0 = 0; g0 < groups; g0 += 32) {
     __bf16* xh_s = sA[1];  // [BM m][32 g], pitch kPitch
     __bf16* xl_s = sA[1] + A_ELEMS;
     __bf16* bh_s = sB[0];  // [BN n][32 g]

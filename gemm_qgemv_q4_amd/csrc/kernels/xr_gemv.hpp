@@ -1,7 +1,8 @@
 // Q4_0, Q4_K and affine-code products at 3..8 rows of x on the gfx950 matrix
 // cores, with x held in registers for the whole launch.
 //
-// Q4_0: y[m, n] = sum_b d[n, b] (P[m, n, b] - 8 X[m, b])      [GGML block_q4_0: w = d (q - 8)]
+// Q4_0: y[m, n] = sum_b d[n, b] P[m, n, b] with P over x (q - 8)
+//                                               [GGML block_q4_0: w = d (q - 8)]
 // Q4_K: y[m, n] = sum_j (d sc_j)[n] P[m, n, j] - (dmin m_j)[n] X[m, j]
 //                                               [GGML block_q4_K: w = d sc_j q - dmin m_j]
 // affine: y[m, n] = sum_b s[n, g(b)] P[m, n, b] + b[n, g(b)] X[m, b]
@@ -14,10 +15,11 @@
 // to) 8 rows of x, rows 8..15 hold bf16(x - bf16(x)).  Both halves of x thus
 // ride in one MFMA, and the output's two partial sums are added at the end
 // (x carries 16 significant bits, relative error <= 2^-17 per element; the
-// codes, 0..15 or 0..255 for u8, are exact in bf16 and the products exact in
-// the f32 accumulator).  The block sums of x come from the same MFMA unit (x
-// times a column of -8 for Q4_0, of ones otherwise), so that a Q4_0 block of
-// codes 8 gives exactly P - 8 X = 0.
+// codes are exact in bf16 -- Q4_0 as 16 (q - 8), -128..112, the others as
+// 0..15 or 0..255 -- and the products exact in the f32 accumulator).  A Q4_0
+// block of codes 8 therefore adds exactly 0.  The block sums of x that Q4_K
+// and the affine formats need come from the same MFMA unit (x times a column
+// of ones).
 //
 // Work split: a workgroup of K/512 waves owns 16 weight rows at a time; wave
 // w owns columns 512 w .. 512 w + 511, i.e. NB = 16 blocks (288 bytes of each
@@ -183,15 +185,12 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p)
   // formats take the weights in order; affine codes take them as
   // [0, 2, 4, 6, 1, 3, 5, 7], the order of the even and odd nibbles of a
   // packed word (u8 codes use the same order, so both give the same bits).
+  constexpr bool XSUM = FMT != FMT_Q40;  // the format has an offset or bias term
   bf16x8 a[NB];
-  f32x4 xs[NB];  // Q4_0: -8 X, else X, of this lane's MFMA rows 4kp .. 4kp+3
+  f32x4 xs[XSUM ? NB : 1];  // X of this lane's MFMA rows 4kp .. 4kp+3
   {
-    // Q4_0: x times a column of -8 is exactly -8 times the block sum (a
-    // power-of-two scale commutes with the rounding), so that P + xs is
-    // exactly 0 for a block of codes 8
-    const float cs = FMT == FMT_Q40 ? -8.0f : 1.0f;
-    const bf16x8 m8 = {(__bf16)cs, (__bf16)cs, (__bf16)cs, (__bf16)cs,
-                       (__bf16)cs, (__bf16)cs, (__bf16)cs, (__bf16)cs};
+    const bf16x8 ones = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
+                         (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
     const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int s = 0; s < NB; ++s) {
@@ -211,7 +210,7 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p)
       else
         av = lo_row ? u32x4{r01, r23, l01, l23} : u32x4{h01, h23, r01, r23};
       a[s] = __builtin_bit_cast(bf16x8, av);
-      xs[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], m8, z, 0, 0, 0);
+      if constexpr (XSUM) xs[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], ones, z, 0, 0, 0);
     }
   }
 
@@ -233,7 +232,9 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p)
       // Block s of row r sits at byte 18 s of the row's copy.  Even blocks start
       // 4-byte aligned: code bytes 4kp.. at 2 + 4kp, read as two dwords; odd
       // blocks have them in one dword.  The scale is the low (even) or high
-      // (odd) half of the dword holding the block start.
+      // (odd) half of the dword holding the block start.  The codes enter the
+      // MFMA as the exact bf16 values 16 (q - 8) (int8 bytes, q40_lo16 /
+      // q40_hi16), and d / 16 scales the block's product.
       auto product = [&](int s, uint32_t& db) -> f32x4 {
         uint32_t v;
         const uint8_t* blk = rl + 18 * s;
@@ -246,7 +247,12 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p)
           v = *reinterpret_cast<const uint32_t*>(blk + 2 + 4 * kp);
           db = *reinterpret_cast<const uint32_t*>(blk - 2) >> 16;
         }
-        return mfma(s, v & 0x0F0F0F0Fu, (v >> 4) & 0x0F0F0F0Fu);
+        float c[8];
+        signed_codes_f32(q40_lo16(v), c[0], c[1], c[2], c[3]);  // elements 4kp .. 4kp+3
+        signed_codes_f32(q40_hi16(v), c[4], c[5], c[6], c[7]);  // elements 16+4kp ..
+        const u32x4 bv = {pk_bf16(c[0], c[1]), pk_bf16(c[2], c[3]), pk_bf16(c[4], c[5]), pk_bf16(c[6], c[7])};
+        const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], __builtin_bit_cast(bf16x8, bv), z, 0, 0, 0);
       };
       // block s + 1 is multiplied before block s is scaled into acc
       uint32_t db0;
@@ -256,9 +262,9 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p)
         uint32_t db1 = 0;
         f32x4 P1 = P0;
         if (s + 1 < NB) P1 = product(s + 1, db1);
-        const float d = f16_bits_to_f32(db0);
+        const float d = f16_bits_to_f32(db0) * 0.0625f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(d, P0[i] + xs[s][i], acc[i]);
+        for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(d, P0[i], acc[i]);
         P0 = P1;
         db0 = db1;
       }

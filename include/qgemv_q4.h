@@ -31,12 +31,9 @@
  *    Q4_0 -- and for the affine formats 32 <= group_size <= 512) a product
  *    runs on the matrix cores.  x is split into two bf16 terms so the f32
  *    tolerance above still holds.  That path takes stream-ordered scratch
- *    (hipMallocAsync / hipFreeAsync on `stream`) of M*K*4 + M*(K/gs)*4 bytes
- *    plus alignment (gs = 32 for Q4_0 and Q4_K).  The choice of path depends
- *    on the format, M, K, the group size and alignment only, so the
- *    equalities stated below (dual = two singles, multi-part = one call per
- *    part, packed = unpacked, fused split = product then split) hold bit for
- *    bit on both paths.
+ *    (hipMallocAsync / hipFreeAsync on `stream`) of 4*M*K bytes, plus
+ *    4*M*(K/gs) bytes for the formats with an offset or bias term (Q4_K: gs =
+ *    32; affine), each array rounded up to 256 bytes.
  *  - Few rows on the matrix cores: for 2 <= M below that threshold, the
  *    affine formats with group_size >= 64, K a multiple of 512 with K/512 in
  *    {1, 2, 4, 8} and codes aligned (16 bytes for u8, 8 for packed) run on
@@ -44,8 +41,15 @@
  *    same way and no scratch; from 3 <= M below that threshold Q4_0, Q4_K
  *    and the affine formats (group_size >= 64) with K a multiple of 512 up
  *    to 4096 and the weights 16-byte aligned run on the matrix cores with x
- *    held in registers, also without scratch.  The same tolerance and
- *    equalities hold.
+ *    held in registers, also without scratch.  The same tolerance holds.
+ *  - Which kernel computes a weight tensor depends on the format, M, K, the
+ *    group size, that tensor's own alignment and size, and the two settings
+ *    at the end of this header as the call reads them; never on the other
+ *    tensors of the call.  So the equalities stated below (dual = two
+ *    singles, multi-part = one call per part, packed = unpacked, fused split
+ *    = product then split) hold bit for bit for every accepted alignment.
+ *  - Q4_0 blocks whose codes are all 8 (weights 0) contribute exactly 0 on
+ *    every path: a row of such blocks gives +0 or -0 for any finite x.
  */
 #ifndef QGEMV_Q4_H
 #define QGEMV_Q4_H
@@ -97,7 +101,8 @@ qg_status qgemv_q4_k(const void* w, const float* x, float* y,
  * Defined by: mlx-native `fused_dual_proj_q4_0.rs` (module doc: two weight
  * matrices of the same shape share one input; the result is byte-identical
  * to two single Q4_0 products).  Here: bitwise equal to two qgemv_q4_0
- * calls with the same M, N, K.
+ * calls with the same M, N, K, for any alignment of each weight (when the
+ * two weights take different kernels, each runs as its single call would).
  *   w_a, w_b : as `w` of qgemv_q4_0, same shape;  x : [M, K] f32;
  *   y_a, y_b : [M, N] f32.
  * Errors: as qgemv_q4_0 for both weights; y_a == y_b.
@@ -133,8 +138,9 @@ qg_status qmm_affine_t(const float* x, const uint8_t* q, const float* scales,
  *                W_p[j,k] for j < n[p].  For one shared output Y[M, N_total]
  *                pass y[p] = Y + (first column of part p), ldy[p] = N_total.
  *   x : [M, K] f32 shared by all parts.
- * Each part's result is bitwise equal to qgemv_q4_k on that part alone.
- * Output slices must not overlap each other or x.
+ * Each part's result is bitwise equal to qgemv_q4_k on that part alone, for
+ * any alignment of each part's weights (parts on different kernels run in
+ * separate launches).  Output slices must not overlap each other or x.
  * Errors: parts outside 1..8; M, K, n[p] < 1; K % 256 != 0; ldy[p] < n[p];
  *         null pointers; x or y[p] not 4-byte aligned.
  */
@@ -194,11 +200,29 @@ qg_status qkv_split_f32(const float* qkv, float* q, float* k, float* v,
                         void* stream);
 
 /*
- * Tuning knob: smallest M at which the product calls use the matrix-core path
- * (default 64).  Process-wide.  qg_set_mfma_min_m returns QG_EINVAL for m < 1.
+ * Settings (process-wide; each product call reads both once, at its start).
+ * Changing one changes which kernels later calls run, and so their rounding
+ * within the stated tolerance; the bitwise equalities above hold between
+ * calls made under the same settings.  Calls that run while another thread
+ * changes a setting may see either value.
+ *
+ * qg_set_mfma_min_m: smallest M at which the product calls use the
+ *   matrix-core GEMM (default 64).  QG_EINVAL for m < 1.
+ * qg_set_kernel_mask: which of the optional kernels may run (default: all).
+ *   QG_KERNEL_KSLICED  the K-sliced GEMV at few rows of x; without it the
+ *                      chunked GEMV runs, which gives the same bits.
+ *   QG_KERNEL_XR       the x-resident matrix-core GEMV (3 rows of x up to
+ *                      the threshold); without it the FMA or streamed
+ *                      matrix-core GEMV runs.
+ *   QG_KERNEL_MMA      the streamed matrix-core GEMV for affine codes (2 rows
+ *                      of x up to the threshold); without it the FMA GEMV.
+ *   QG_EINVAL for other bits.
  */
+enum { QG_KERNEL_KSLICED = 1, QG_KERNEL_XR = 2, QG_KERNEL_MMA = 4 };
 qg_status qg_set_mfma_min_m(int64_t m);
 int64_t qg_get_mfma_min_m(void);
+qg_status qg_set_kernel_mask(uint32_t mask);
+uint32_t qg_get_kernel_mask(void);
 
 #ifdef __cplusplus
 }

@@ -115,6 +115,22 @@ def test_mfma_threshold_knob():
         qg.qg_set_mfma_min_m(old)
 
 
+def test_kernel_mask_knob():
+    old = qg.qg_get_kernel_mask()
+    assert old == qg.QG_KERNEL_ALL
+    try:
+        qg.qg_set_kernel_mask(qg.QG_KERNEL_XR)
+        assert qg.qg_get_kernel_mask() == qg.QG_KERNEL_XR
+        with pytest.raises(qg.QGError, match="unknown bits"):
+            qg.qg_set_kernel_mask(8)
+        assert qg.qg_get_kernel_mask() == qg.QG_KERNEL_XR
+        with qg.kernels(mask=0, mfma_min_m=5):
+            assert (qg.qg_get_kernel_mask(), qg.qg_get_mfma_min_m()) == (0, 5)
+        assert qg.qg_get_kernel_mask() == qg.QG_KERNEL_XR
+    finally:
+        qg.qg_set_kernel_mask(old)
+
+
 def test_error_message_is_per_call():
     _err(qg.raw.qgemv_q4_0(A, B, C, 1, 1, 48, None))
     assert "QK4_0" in qg.last_error()

@@ -1,9 +1,8 @@
 """The K-sliced GEMV (one x row: Q4_0, Q4_K, u8 and packed affine codes,
 single and multi-part) against the chunked GEMV it replaces at M = 1: the two
 kernels make the same additions in the same order, so their outputs must agree
-bit for bit (the tuning switch QG_GEMV_KS=0 selects the chunked kernel), and
+bit for bit (without QG_KERNEL_KSLICED in the kernel mask the chunked kernel runs), and
 both against the f64 oracle."""
-import os
 
 import numpy as np
 import pytest
@@ -20,21 +19,13 @@ def bits(a):
 
 
 def both(call):
-    """(K-sliced result, chunked result) of one call.  The matrix-core Q4_0
-    GEMV, which takes Q4_0 from 2 rows of x on, is switched off for both."""
-    old = {v: os.environ.get(v) for v in ("QG_GEMV_KS", "QG_GEMV_XR")}
-    try:
-        os.environ["QG_GEMV_XR"] = "0"
-        os.environ["QG_GEMV_KS"] = "1"
+    """(K-sliced result, chunked result) of one call.  The matrix-core GEMVs,
+    which take products from 2 or 3 rows of x on, are switched off for both."""
+    import gemm_qgemv_q4_amd as qg
+    with qg.kernels(mask=qg.QG_KERNEL_KSLICED):
         a = call()
-        os.environ["QG_GEMV_KS"] = "0"
+    with qg.kernels(mask=0):
         b = call()
-    finally:
-        for v, o in old.items():
-            if o is None:
-                os.environ.pop(v, None)
-            else:
-                os.environ[v] = o
     return a, b
 
 
@@ -132,28 +123,6 @@ def test_fused_qkv_ksplit_equals_chunked_and_split(lib):
         assert np.array_equal(bits(got), bits(host(ref)))
 
 
-@pytest.mark.parametrize("k", [1024, 4096])
-def test_q4_k_ksplit_waves_do_not_change_bits(lib, k):
-    """4 or 8 waves per workgroup (8 or 4 virtual lanes per wave) regroup the
-    same additions; the outputs agree bit for bit, multi-part included."""
-    ns = (96, 40, 17)
-    ws, x = synth.q4_k_multi_case(8900 + k, 1, ns, k)
-    dws, dx = [dev(w) for w in ws], dev(x)
-    out = {}
-    old = os.environ.get("QG_GEMV_KS_WAVES")
-    try:
-        for wv in ("4", "8"):
-            os.environ["QG_GEMV_KS_WAVES"] = wv
-            out[wv] = (host(lib.qgemv_q4_k_multi(dws, dx, list(ns), k)), host(lib.qgemv_q4_k(dws[0], dx, ns[0], k)))
-    finally:
-        if old is None:
-            os.environ.pop("QG_GEMV_KS_WAVES", None)
-        else:
-            os.environ["QG_GEMV_KS_WAVES"] = old
-    for a, b in zip(out["4"], out["8"]):
-        assert np.array_equal(bits(a), bits(b))
-
-
 # two to four rows of x (tiles of 2 or 4 rows, 4 waves per workgroup at K >= 2048)
 @pytest.mark.parametrize("m,n,k", [(2, 33, 2048), (3, 300, 4096), (4, 70, 8192), (4, 4099, 4096),
                                    (2, 4099, 4096), (2, 17, 16384)])
@@ -166,15 +135,14 @@ def test_q4_k_ksplit_rows_of_x_equal_chunked(lib, m, n, k):
 
 
 @pytest.mark.parametrize("m", [2, 4])
-def test_dual_and_multi_ksplit_rows_of_x_equal_chunked(lib, monkeypatch, m):
-    # the single call below runs on the same FMA kernels as the dual product
-    monkeypatch.setenv("QG_GEMV_XR", "0")
+def test_dual_and_multi_ksplit_rows_of_x_equal_chunked(lib, m):
     n, k = 40, 4096
     wa, wb, x = synth.dual_q4_0_case(9800 + m, m, n, k)
     dwa, dwb, dx = dev(wa), dev(wb), dev(x)
     (a0, a1), (b0, b1) = both(lambda: tuple(host(t) for t in lib.qgemv_dual_q4_0(dwa, dwb, dx, n, k)))
     assert np.array_equal(bits(a0), bits(b0)) and np.array_equal(bits(a1), bits(b1))
-    assert np.array_equal(bits(a0), bits(host(lib.qgemv_q4_0(dwa, dx, n, k))))
+    with lib.kernels(mask=lib.QG_KERNEL_KSLICED):  # the single call on the dual's kernels
+        assert np.array_equal(bits(a0), bits(host(lib.qgemv_q4_0(dwa, dx, n, k))))
     assert_close(a1, oracle.decode_q4_0(wb, n, k), x, f"dual ksplit m{m}")
     ns = (96, 40, 17)
     ws, xm = synth.q4_k_multi_case(9850 + m, m, ns, k)

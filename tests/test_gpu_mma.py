@@ -2,11 +2,9 @@
 codes, group size >= 64, K a multiple of 512 with K/512 in {1, 2, 4, 8})
 against the f64 oracle, and its stated equalities: packed codes bitwise equal
 to u8 codes, the fused q|k|v product bitwise equal to the product then the
-split.  The tuning switch QG_GEMV_MMA=0 selects the FMA kernels, whose results
-must agree within the same tolerance.  Shapes outside that range (group size
+split.  Without QG_KERNEL_MMA in the kernel mask the FMA kernels run, whose
+results must agree within the same tolerance.  Shapes outside that range (group size
 32, K = 256 or 1536) take the FMA kernels and are checked the same way."""
-import os
-
 import numpy as np
 import pytest
 
@@ -18,27 +16,22 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.fixture(autouse=True)
-def _no_xr(monkeypatch):
+def _no_xr(lib):
     """From 3 rows of x the x-resident matrix-core GEMV takes these products;
     it is switched off here so that this kernel is the one tested at every M
     (tests/test_gpu_xr.py covers the other)."""
-    monkeypatch.setenv("QG_GEMV_XR", "0")
+    with lib.kernels(mask=lib.QG_KERNEL_ALL & ~lib.QG_KERNEL_XR):
+        yield
 
 
 def bits(a):
     return np.ascontiguousarray(a).view(np.uint32)
 
 
-def with_env(val, call):
-    old = os.environ.get("QG_GEMV_MMA")
-    try:
-        os.environ["QG_GEMV_MMA"] = val
+def fma_only(lib, call):
+    """The call with the FMA kernels only (no matrix-core GEMV)."""
+    with lib.kernels(mask=lib.QG_KERNEL_KSLICED):
         return call()
-    finally:
-        if old is None:
-            os.environ.pop("QG_GEMV_MMA", None)
-        else:
-            os.environ["QG_GEMV_MMA"] = old
 
 
 # M from 2 to 40 (one to five launches of up to 8 rows), K from one pair of
@@ -56,7 +49,7 @@ def test_affine_mma_against_oracle_and_fma_path(lib, m, n, k, gs, code_max):
     y = host(lib.qmm_affine_t(dx, dq, ds, db, gs))
     w64 = oracle.decode_affine(q, s, b, n, k, gs)
     assert_close(y, w64, x, f"affine mma m{m} n{n} k{k} gs{gs}")
-    y_fma = with_env("0", lambda: host(lib.qmm_affine_t(dx, dq, ds, db, gs)))
+    y_fma = fma_only(lib, lambda: host(lib.qmm_affine_t(dx, dq, ds, db, gs)))
     assert_close(y_fma, w64, x, "fma path")
     # a second call gives the same bits (no state carried between calls)
     assert np.array_equal(bits(y), bits(host(lib.qmm_affine_t(dx, dq, ds, db, gs))))

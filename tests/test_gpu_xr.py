@@ -4,9 +4,9 @@ to 4096) against the f64 oracle, and its stated equalities: the dual Q4_0 and
 the multi-part Q4_K products bitwise equal to single calls, packed affine codes
 bitwise equal to u8 codes, the fused q|k|v product bitwise equal to the
 product then the split, each row of x independent of the others, Q4_0 blocks
-of codes 8 giving exactly zero, the hand-worked Q4_K super-block exactly.  The tuning
-switch QG_GEMV_XR=0 selects the other kernels, whose results must agree within
-the same tolerance.  Shapes outside that range (K = 4160, 8192, 256) take the
+of codes 8 giving exactly zero, the hand-worked Q4_K super-block exactly.
+Without QG_KERNEL_XR in the kernel mask the other kernels run, whose results
+must agree within the same tolerance.  Shapes outside that range (K = 4160, 8192, 256) take the
 FMA kernels and are checked the same way."""
 import os
 
@@ -24,16 +24,10 @@ def bits(a):
     return np.ascontiguousarray(a).view(np.uint32)
 
 
-def with_env(val, call):
-    old = os.environ.get("QG_GEMV_XR")
-    try:
-        os.environ["QG_GEMV_XR"] = val
+def without_xr(lib, call):
+    """The call with the x-resident matrix-core GEMV switched off."""
+    with lib.kernels(mask=lib.QG_KERNEL_ALL & ~lib.QG_KERNEL_XR):
         return call()
-    finally:
-        if old is None:
-            os.environ.pop("QG_GEMV_XR", None)
-        else:
-            os.environ["QG_GEMV_XR"] = old
 
 
 # M from 3 to 40 (one to five launches of up to 8 rows), K from one wave (512)
@@ -51,7 +45,7 @@ def test_q4_0_xr_against_oracle_and_fma_path(lib, m, n, k):
     y = host(lib.qgemv_q4_0(dw, dx, n, k))
     w64 = oracle.decode_q4_0(w, n, k)
     assert_close(y, w64, x, f"q4_0 xr m{m} n{n} k{k}")
-    y_fma = with_env("0", lambda: host(lib.qgemv_q4_0(dw, dx, n, k)))
+    y_fma = without_xr(lib, lambda: host(lib.qgemv_q4_0(dw, dx, n, k)))
     assert_close(y_fma, w64, x, "fma path")
     # a second call gives the same bits (no state carried between calls)
     assert np.array_equal(bits(y), bits(host(lib.qgemv_q4_0(dw, dx, n, k))))
@@ -134,7 +128,7 @@ def test_q4_k_xr_against_oracle_and_fma_path(lib, m, n, k):
     y = host(lib.qgemv_q4_k(dw, dx, n, k))
     w64 = oracle.decode_q4_k(w, n, k)
     assert_close(y, w64, x, f"q4_k xr m{m} n{n} k{k}")
-    y_fma = with_env("0", lambda: host(lib.qgemv_q4_k(dw, dx, n, k)))
+    y_fma = without_xr(lib, lambda: host(lib.qgemv_q4_k(dw, dx, n, k)))
     assert_close(y_fma, w64, x, "fma path")
     assert np.array_equal(bits(y), bits(host(lib.qgemv_q4_k(dw, dx, n, k))))
 
@@ -187,7 +181,7 @@ def test_affine_xr_against_oracle_and_other_path(lib, m, n, k, gs, code_max):
     y = host(lib.qmm_affine_t(dx, dq, ds, db, gs))
     w64 = oracle.decode_affine(q, s, b, n, k, gs)
     assert_close(y, w64, x, f"affine xr m{m} n{n} k{k} gs{gs}")
-    y_other = with_env("0", lambda: host(lib.qmm_affine_t(dx, dq, ds, db, gs)))
+    y_other = without_xr(lib, lambda: host(lib.qmm_affine_t(dx, dq, ds, db, gs)))
     assert_close(y_other, w64, x, "other path")
     assert np.array_equal(bits(y), bits(host(lib.qmm_affine_t(dx, dq, ds, db, gs))))
 
