@@ -35,6 +35,7 @@ SIGNATURES = {
     "qgemv_q4_k": (ctypes.c_int, [_P, _P, _P, _I, _I, _I, _P]),
     "qgemv_dual_q4_0": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _P]),
     "qmm_affine_t": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
+    "qmm_affine_t_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "qkv_split_f32": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "qgemv_q4_k_multi": (ctypes.c_int, [_P, _P, _P, _P, _I, _P, _I, _I, _P]),
     "qmm_affine_t_packed": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
@@ -171,6 +172,26 @@ def qmm_affine_t(x: torch.Tensor, q: torch.Tensor, scales: torch.Tensor, biases:
     y = _out("y", y, (m, n), x)
     _check(_lib.qmm_affine_t(px, pq, ps, pb, ctypes.c_void_p(y.data_ptr()), m, n, k, group_size,
                              _stream(x)))
+    return y
+
+
+def qmm_affine_t_noalloc(x: torch.Tensor, q: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor,
+                         group_size: int, y: torch.Tensor):
+    """qmm_affine_t without any allocation: the caller passes the output y[M, N],
+    and the matrix-core path uses the library's static scratch (16 MiB per GPU)."""
+    if q.dim() != 2:
+        raise ValueError("q must be [N, K]")
+    n, k = q.shape
+    m = _mk(x, k)
+    if group_size <= 0 or k % group_size:
+        raise ValueError("K must be divisible by group_size")
+    g = n * (k // group_size)
+    px = _dev("x", x, torch.float32, numel=m * k)
+    pq = _dev("q_int", q, torch.uint8, numel=n * k)
+    ps = _dev("scales", scales, torch.float32, numel=g)
+    pb = _dev("biases", biases, torch.float32, numel=g)
+    py = _dev("y", y, torch.float32, numel=m * n)
+    _check(_lib.qmm_affine_t_noalloc(px, pq, ps, pb, py, m, n, k, group_size, _stream(x)))
     return y
 
 

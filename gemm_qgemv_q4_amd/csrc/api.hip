@@ -16,6 +16,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "qgemv_q4.h"
 #include "kernels/gemv.hpp"
@@ -799,6 +800,50 @@ qg_status q40_common(const char* op, const void* w, const float* x, float* y, in
   return check_xy(op, x, y);
 }
 
+qg_status affine_args(const char* op, const float* x, const uint8_t* q, const float* scales, const float* biases,
+                      const float* y, int64_t m, int64_t n, int64_t k, int64_t group_size) {
+  qg_status st = check_mnk(op, m, n, k);
+  if (st != QG_OK) return st;
+  st = check_group(op, k, group_size);
+  if (st != QG_OK) return st;
+  if (!q || !scales || !biases) return fail("%s: null pointer", op);
+  if (!aligned(scales, 4) || !aligned(biases, 4)) return fail("%s: scales/biases must be 4-byte aligned", op);
+  return check_xy(op, x, y);
+}
+
+// ------------------------------------------------------------------ static scratch
+// Scratch of the allocation-free entry point (qmm_affine_t_noalloc): one
+// array per GPU, in the code object's device memory, resident until the
+// process ends.  Host code never passes `g_scratch` itself (on the host it
+// names a stand-in, not device memory): the device address is looked up once
+// per device with hipGetSymbolAddress, on that device, and kept in
+// g_scratch_dev.  Every call on a GPU shares that GPU's array; the matrix-core
+// path writes all of the scratch it reads (x_hi, x_lo and the group sums)
+// before reading it, so nothing needs clearing, and calls that overlap on one
+// GPU race.
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) uint8_t g_scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+qg_status static_scratch(const char* op, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return launch_error(op, "hipGetDevice", e);
+  if (dev < 0 || dev >= kMaxDevices) return fail("%s: device %d outside 0..%d", op, dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_scratch));
+    if (e != hipSuccess || p == nullptr) return launch_error(op, "device address of the static scratch", e);
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return QG_OK;
+}
+
 HostPart single_part(const void* w, const float* scales, const float* biases, float* y, int64_t ldy, int64_t n) {
   HostPart hp{};
   hp.w[0] = w;
@@ -912,16 +957,33 @@ qg_status qgemv_q4_k_multi(const void* const* w, float* const* y, const int64_t*
 qg_status qmm_affine_t(const float* x, const uint8_t* q, const float* scales, const float* biases,
                        float* y, int64_t M, int64_t N, int64_t K, int64_t group_size, void* stream) {
   const char* op = "qmm_affine_t";
-  qg_status st = check_mnk(op, M, N, K);
-  if (st != QG_OK) return st;
-  st = check_group(op, K, group_size);
-  if (st != QG_OK) return st;
-  if (!q || !scales || !biases) return fail("%s: null pointer", op);
-  if (!aligned(scales, 4) || !aligned(biases, 4)) return fail("%s: scales/biases must be 4-byte aligned", op);
-  st = check_xy(op, x, y);
+  const qg_status st = affine_args(op, x, q, scales, biases, y, M, N, K, group_size);
   if (st != QG_OK) return st;
   const HostPart hp = single_part(q, scales, biases, y, N, N);
   return run_parts<FMT_AFF>(op, call_cfg(), &hp, 1, x, M, K, (int)group_size, static_cast<hipStream_t>(stream));
+}
+
+qg_status qmm_affine_t_noalloc(const float* x, const uint8_t* q, const float* scales, const float* biases,
+                               float* y, int64_t M, int64_t N, int64_t K, int64_t group_size, void* stream) {
+  const char* op = "qmm_affine_t_noalloc";
+  qg_status st = affine_args(op, x, q, scales, biases, y, M, N, K, group_size);
+  if (st != QG_OK) return st;
+  const CallCfg cfg = call_cfg();
+  const HostPart hp = single_part(q, scales, biases, y, N, N);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Path path = path_of<FMT_AFF>(cfg, M, K, group_size, q, N);
+  // the other paths use no scratch
+  if (path != P_MFMA) return run_path<FMT_AFF, 1>(op, path, cfg, &hp, 1, x, M, K, (int)group_size, s);
+  const size_t need = mfma_scratch_bytes<FMT_AFF>(M, K, group_size);
+  if (need > kStaticScratchBytes)
+    return fail("%s: M = %lld, K = %lld, group_size = %lld needs %zu bytes of scratch on the matrix-core path; "
+                "the static buffer holds %zu (use qmm_affine_t, which allocates)",
+                op, (long long)M, (long long)K, (long long)group_size, need, kStaticScratchBytes);
+  void* scr = nullptr;
+  st = static_scratch(op, &scr);
+  if (st != QG_OK) return st;
+  (void)hipGetLastError();
+  return launch_mfma<FMT_AFF>(op, &hp, 1, 1, x, M, K, (int)group_size, scr, s);
 }
 
 qg_status qmm_affine_t_packed(const float* x, const uint32_t* w_packed, const float* scales,

@@ -127,6 +127,27 @@ qg_status qmm_affine_t(const float* x, const uint8_t* q, const float* scales,
                        void* stream);
 
 /*
+ * qmm_affine_t_noalloc -- qmm_affine_t that allocates nothing.
+ * For callers that cannot allocate device memory during the call: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, kernels and results as qmm_affine_t (bit for bit under the
+ * same settings).  Where qmm_affine_t would take stream-ordered scratch (the
+ * matrix-core path, from M >= qg_get_mfma_min_m()), this call uses a static
+ * device array of 16 MiB per GPU instead, which the library holds on every
+ * GPU it runs on until the process ends; the device address is looked up on
+ * a device's first call (no allocation).  The scratch needed is 4*M*K bytes
+ * plus 4*M*(K/group_size), each rounded up to 256 bytes; a call on that path
+ * needing more than 16 MiB returns QG_EINVAL before any launch.  Calls that
+ * overlap on one GPU (several streams or threads) share the array and race:
+ * order them on one stream.  The caller passes every input and output.
+ * Errors: as qmm_affine_t; scratch beyond the 16 MiB limit.
+ */
+qg_status qmm_affine_t_noalloc(const float* x, const uint8_t* q, const float* scales,
+                               const float* biases, float* y,
+                               int64_t M, int64_t N, int64_t K, int64_t group_size,
+                               void* stream);
+
+/*
  * qgemv_q4_k_multi -- the parts of a fused projection in one launch.
  * Defined by: ferrum-kernels `q4_k_gemv_v2.rs` (doc of
  * dispatch_gemv_q4k_v2_offset: each part of a fused projection has its own
