@@ -90,8 +90,18 @@ def build_cases(qg, torch, only=None):
     cases = []
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
+    # groups of workloads by the config they come from, and the workloads of each
+    groups = {"q4_k_gemv_4096": ["q4_k_gemv_4096"], "q4_0_gemv_1024": ["q4_0_gemv_1024"],
+              "dual_q4_0_4096": [f"dual_q4_0_4096_m{m}" for m in (1, 4, 8)],
+              "affine_12288x4096_gs64": [f"affine_12288x4096_gs64_m{m}" for m in (1, 8)],
+              "prefill_qkv_512x2048": ["prefill_gemm_512x8192x2048", "qkv_split_512x8192"],
+              "q4_k_qkv_multi_4096": ["q4_k_qkv_multi_4096", "q4_k_qkv_separate_4096"],
+              "affine_b4_12288x4096_gs64": [f"affine_b4_12288x4096_gs64_m{m}" for m in (1, 8)],
+              "q4_0_prefill_512x4096": ["q4_0_prefill_512x4096"],
+              "prefill_qkv_fused_512x2048": ["prefill_qkv_fused_512x2048"]}
+
     def want(n):
-        return only is None or n == only or n.startswith(only)
+        return only is None or n.startswith(only) or any(c.startswith(only) for c in groups[n])
 
     def rot(t, r):
         # r distinct device copies of one tensor (HBM does not deduplicate)
@@ -270,7 +280,8 @@ def build_cases(qg, torch, only=None):
                           oracle=lambda x=x, q=q, s=s, b=b, c=c:
                           _orc().qmm_affine_t_qkv(x, q, s, b, c["m"], c["k"], c["gs"], c["q_sp"], c["k_sp"],
                                                   c["v_sp"])))
-    return cases
+    # a workload name selects that workload alone
+    return [c for c in cases if only is None or c.name.startswith(only)] or cases
 
 
 def _replay_timing(torch, launch, calls, warmup, reps_n=None):
