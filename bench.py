@@ -23,7 +23,8 @@ full headline calls.  `roofline.traffic` comes from the committed rocprofv3
 counter summary when it was taken on the current kernel source.
 
 Workloads: Q4_0 GEMV 1024^2, Q4_K GEMV 4096^2, dual Q4_0 at M = 1/4/8, affine
-12288x4096 at M = 1/8, prefill affine GEMM 512x8192x2048 + qkv split, and the
+12288x4096 at M = 1/8, prefill affine GEMM 512x8192x2048 (also through the
+allocation-free entry point) + qkv split, and the
 follow-on paths: multi-part Q4_K, packed 4-bit affine, Q4_0 prefill on the
 matrix cores, the fused projection + split.
 
@@ -94,7 +95,8 @@ def build_cases(qg, torch, only=None):
     groups = {"q4_k_gemv_4096": ["q4_k_gemv_4096"], "q4_0_gemv_1024": ["q4_0_gemv_1024"],
               "dual_q4_0_4096": [f"dual_q4_0_4096_m{m}" for m in (1, 4, 8)],
               "affine_12288x4096_gs64": [f"affine_12288x4096_gs64_m{m}" for m in (1, 8)],
-              "prefill_qkv_512x2048": ["prefill_gemm_512x8192x2048", "qkv_split_512x8192"],
+              "prefill_qkv_512x2048": ["prefill_gemm_512x8192x2048", "prefill_gemm_512x8192x2048_noalloc",
+                                       "qkv_split_512x8192"],
               "q4_k_qkv_multi_4096": ["q4_k_qkv_multi_4096", "q4_k_qkv_separate_4096"],
               "affine_b4_12288x4096_gs64": [f"affine_b4_12288x4096_gs64_m{m}" for m in (1, 8)],
               "q4_0_prefill_512x4096": ["q4_0_prefill_512x4096"],
@@ -182,6 +184,14 @@ def build_cases(qg, torch, only=None):
                           bound="mfma",
                           oracle=lambda x=x, q=q, s=s, b=b, c=c:
                           _orc().qmm_affine_t(x, q, s, b, c["m"], c["n"], c["k"], c["gs"])))
+        # the same product through the allocation-free entry point (static
+        # scratch instead of a stream-ordered allocation per call)
+        cases.append(Case("prefill_gemm_512x8192x2048_noalloc",
+                          "affine gs64 M=512 N=8192 K=2048 (MFMA), allocation-free entry point", nb,
+                          2 * c["m"] * c["n"] * c["k"], r,
+                          lambda i, qs_=qs_, ss_=ss_, bs_=bs_, dx=dx, qkv=qkv, r=r, gs=c["gs"]:
+                          qg.qmm_affine_t_noalloc(dx, qs_[i % r], ss_[i % r], bs_[i % r], gs, qkv),
+                          bound="mfma"))
         qkv_r = rot(qkv, max(2, min(64, -(-ROTATE_BYTES // (qkv.numel() * 4)))))
         rr = len(qkv_r)
         qo = torch.empty((c["m"], c["q_sp"]), dtype=torch.float32, device="cuda")

@@ -690,6 +690,7 @@ __global__ void __launch_bounds__(512) gemv_ks_kernel(GemvParams p) {
   if (g >= p.n_groups) return;
   View cv;
   view_of(g, cv);
+  int grid;
 
   // x of this wave's chunks, for each of the MT rows of x: float4
   // NE4 * (LW*w + L*j) + lane covers chunks LW*w + L*j .. +LW-1.  The loads go
@@ -711,6 +712,11 @@ __global__ void __launch_bounds__(512) gemv_ks_kernel(GemvParams p) {
         }
       }
     fetch_all(cv);
+    // The grid size lives in the hidden kernel arguments, a scalar-cache line
+    // of its own: read it while the first loads are in flight instead of after
+    // the arithmetic, where its latency would add to every launch.
+    grid = (int)gridDim.x;
+    asm volatile("" ::"s"(grid));
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -762,7 +768,7 @@ __global__ void __launch_bounds__(512) gemv_ks_kernel(GemvParams p) {
           if (c == 0) rb[((s * WV + wv) * ROWS + rset + RS * r) * MT + m] = v;
         }
     const int g_done = g;
-    g += (int)gridDim.x;
+    g += grid;
     if (g < p.n_groups) {
       view_of(g, cv);
       fetch_all(cv);

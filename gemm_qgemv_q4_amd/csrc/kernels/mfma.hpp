@@ -40,7 +40,9 @@ namespace qg {
 // bf16 hi/lo (they feed the bias product on the matrix cores; sh == nullptr:
 // no sums, for formats without a bias).  Each thread converts 8 consecutive
 // elements; the gs/8 threads of a group (gs <= 512) combine their partial sums
-// with a fixed-order DPP reduction.
+// with a fixed-order DPP reduction.  Every store comes after all arithmetic:
+// the vector memory counter also counts stores, so arithmetic placed after a
+// store would wait for that store to complete.
 __global__ void __launch_bounds__(256) affine_prep_kernel(const float* __restrict__ x,
                                                           __bf16* __restrict__ xh,
                                                           __bf16* __restrict__ xl,
@@ -65,28 +67,32 @@ __global__ void __launch_bounds__(256) affine_prep_kernel(const float* __restric
       for (int i = 0; i < 8; ++i) v[i] = x[base + i];
     }
   }
-  bf16x8 hv, lv;
+  const bool sums = sh != nullptr;  // uniform across the grid
+  const int lanes = gs / 8;         // threads per group (4..64)
   float s = 0.0f;
+  __bf16 s_hi = (__bf16)0.0f, s_lo = (__bf16)0.0f;
+  if (sums) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += v[i];
+    s = group_sum(s, lanes);
+    s_hi = (__bf16)s;
+    s_lo = (__bf16)(s - (float)s_hi);
+  }
+  bf16x8 hv, lv;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const __bf16 h = (__bf16)v[i];
     hv[i] = h;
     lv[i] = (__bf16)(v[i] - (float)h);
-    s += v[i];
   }
   if (ok) {
     *reinterpret_cast<bf16x8*>(xh + base) = hv;
     *reinterpret_cast<bf16x8*>(xl + base) = lv;
-  }
-  if (sh == nullptr) return;  // uniform across the grid
-  const int lanes = gs / 8;  // threads per group (4..64)
-  s = group_sum(s, lanes);
-  if (ok && (c8 % lanes) == 0) {
-    const int groups = k / gs;
-    const size_t gi = (size_t)m * groups + c8 / lanes;
-    const __bf16 h = (__bf16)s;
-    sh[gi] = h;
-    sl[gi] = (__bf16)(s - (float)h);
+    if (sums && (c8 % lanes) == 0) {
+      const size_t gi = (size_t)m * (k / gs) + c8 / lanes;
+      sh[gi] = s_hi;
+      sl[gi] = s_lo;
+    }
   }
 }
 

@@ -6,8 +6,9 @@
  * ---------------------------------------
  *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
  *    keeps no pointer after a call returns.  The product calls allocate and
- *    free stream-ordered scratch for their matrix-core path (see "Prefill
- *    rows" below); nothing else allocates.
+ *    free stream-ordered scratch for their matrix-core path, or under stream
+ *    capture take graph-owned scratch (see "Prefill rows" below); nothing
+ *    else allocates.
  *  - Row-major, contiguous.  x is [M, K] f32, y is [M, N] f32:
  *        y[m, n] = sum_k x[m, k] * w[n, k]
  *    where w is the dequantized weight.
@@ -33,7 +34,14 @@
  *    tolerance above still holds.  That path takes stream-ordered scratch
  *    (hipMallocAsync / hipFreeAsync on `stream`) of 4*M*K bytes, plus
  *    4*M*(K/gs) bytes for the formats with an offset or bias term (Q4_K: gs =
- *    32; affine), each array rounded up to 256 bytes.
+ *    32; affine), each array rounded up to 256 bytes.  While `stream` is
+ *    being captured into a graph, the call instead takes a device buffer
+ *    owned by that graph (hipMalloc in relaxed capture mode on first need,
+ *    attached to the graph as a user object); once the graph and every
+ *    executable graph made from it are destroyed, the buffer returns to a
+ *    per-device pool that later captures reuse (it is never freed back).
+ *    Executable graphs made from one captured graph or its clones share
+ *    these buffers and must not run at the same time.
  *  - Few rows on the matrix cores: for 2 <= M below that threshold, the
  *    affine formats with group_size >= 64, K a multiple of 512 with K/512 in
  *    {1, 2, 4, 8} and codes aligned (16 bytes for u8, 8 for packed) run on
