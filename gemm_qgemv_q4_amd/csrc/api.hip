@@ -377,16 +377,27 @@ size_t ks_lds(int mt, int nw, int l, int r, int j, int wv) {
 
 // Waves per workgroup of the K-sliced kernel (the arithmetic is the same
 // either way).  The affine formats use 8.  For the 64-weight chunks of
-// Q4_0/Q4_K, 4 waves of 8 virtual lanes (row groups of 8 rows, twice the
-// workgroups) measured faster where every virtual lane has a chunk (K >=
-// 2048): 6.6 vs 7.0 us for the multi-part q|k|v product, 11.5 vs 12.3 us for
-// its three separate calls, a tie at 4096 x 4096; at K = 1024 8 waves are
-// faster (2.35 vs 2.48 us).  64 lanes per row always take 8 waves (8 virtual
-// lanes per wave and row).
+// Q4_0/Q4_K at 32 lanes per row, 4 waves of 8 virtual lanes (row groups of 8
+// rows, twice the workgroups) measured faster where every virtual lane has a
+// chunk (K >= 2048): 6.6 vs 7.0 us for the multi-part q|k|v product, 11.5 vs
+// 12.3 us for its three separate calls, a tie at 4096 x 4096; at K = 1024 8
+// waves are faster (2.35 vs 2.48 us).  64 lanes per row take 8 waves (8
+// virtual lanes per wave and row), or 16 waves of 4 (row groups of 16 rows,
+// one workgroup per CU) for one weight stream and one x row when those row
+// groups fill the CUs in a single round and each lane holds at most two
+// chunks (K <= 8192; more would spill at 128 VGPRs): x is then read into each
+// CU once instead of twice.  Q4_K 4096 x 4096: 4.45 -> 4.34 us; with two
+// weight streams (6.5 -> 6.9 us) or a second round of groups (6144 rows: 6.1
+// -> 6.9 us) 16 waves are slower.
 template <int FMT>
-int ks_waves(int64_t k, int l) {
+int ks_waves(int64_t k, int l, int mt, int nw, int64_t rows) {
   if constexpr (FMT != FMT_Q40 && FMT != FMT_Q4K) return 8;
-  if (l == 64) return 8;
+  if (l == 64) {
+    const int64_t groups16 = cdiv(rows, 16);
+    const int64_t cus = device_cus();
+    const bool one_round = groups16 <= cus && 4 * groups16 >= 3 * cus;
+    return nw == 1 && mt == 1 && k / 64 <= 2 * 64 && one_round ? 16 : 8;
+  }
   return k / 64 >= 32 ? 4 : 8;
 }
 
@@ -405,7 +416,7 @@ int ks_chunks(const CallCfg& cfg, const GemvPlan& pl, int64_t k) {
   // tiles of 2 or 4 rows of x: the dual Q4_0 product at M = 4 takes 11.0 us
   // here against 14.1 us on the chunked kernel; at 8 rows (22.1 vs 18.5 us)
   // the chunked kernel stays
-  if (pl.mt > 1 && !(Q4 && ((pl.l == 32 && pl.mt <= 4 && ks_waves<FMT>(k, pl.l) == 4) || (pl.l == 64 && pl.mt == 2))))
+  if (pl.mt > 1 && !(Q4 && ((pl.l == 32 && pl.mt <= 4 && ks_waves<FMT>(k, pl.l, pl.mt, NW, 0) == 4) || (pl.l == 64 && pl.mt == 2))))
     return 0;
   if (Q4 ? !((pl.l == 32 || (pl.l == 64 && pl.mt <= 2)) && pl.r == 1) : !(pl.l == 64 && (pl.r == 1 || pl.r == 2)))
     return 0;
@@ -419,19 +430,28 @@ hipError_t launch_gemv_ks_lr(int j, const GemvParams& p, dim3 grid, hipStream_t 
   switch (j) {
     case 1: return launch_gemv_ks_j<FMT, MT, NW, L, R, 1, WV>(p, grid, lds, s);
     case 2: return launch_gemv_ks_j<FMT, MT, NW, L, R, 2, WV>(p, grid, lds, s);
-    case 3: return launch_gemv_ks_j<FMT, MT, NW, L, R, 3, WV>(p, grid, lds, s);
-    case 4: return launch_gemv_ks_j<FMT, MT, NW, L, R, 4, WV>(p, grid, lds, s);
+  }
+  if constexpr (WV <= 8) {  // 16 waves take at most two chunks per lane
+    switch (j) {
+      case 3: return launch_gemv_ks_j<FMT, MT, NW, L, R, 3, WV>(p, grid, lds, s);
+      case 4: return launch_gemv_ks_j<FMT, MT, NW, L, R, 4, WV>(p, grid, lds, s);
+    }
   }
   return hipErrorInvalidValue;
 }
 
 template <int FMT, int NW>
-hipError_t launch_gemv_ks(const GemvPlan& pl, int j, const GemvParams& p, dim3 grid, hipStream_t s) {
+hipError_t launch_gemv_ks(const GemvPlan& pl, int j, int wv, const GemvParams& p, dim3 grid, hipStream_t s) {
   if constexpr (FMT == FMT_Q40 || FMT == FMT_Q4K) {
-    if (pl.l == 64 && pl.r == 1 && pl.mt == 1) return launch_gemv_ks_lr<FMT, 1, NW, 64, 1, 8>(j, p, grid, s);
+    if (pl.l == 64 && pl.r == 1 && pl.mt == 1) {
+      if constexpr (NW == 1) {
+        if (wv == 16) return j <= 2 ? launch_gemv_ks_lr<FMT, 1, NW, 64, 1, 16>(j, p, grid, s) : hipErrorInvalidValue;
+      }
+      return launch_gemv_ks_lr<FMT, 1, NW, 64, 1, 8>(j, p, grid, s);
+    }
     if (pl.l == 64 && pl.r == 1 && pl.mt == 2) return launch_gemv_ks_lr<FMT, 2, NW, 64, 1, 8>(j, p, grid, s);
     if (!(pl.l == 32 && pl.r == 1)) return hipErrorInvalidValue;
-    const bool four = ks_waves<FMT>(p.k, pl.l) == 4;
+    const bool four = wv == 4;
     switch (pl.mt) {
       case 1: return four ? launch_gemv_ks_lr<FMT, 1, NW, 32, 1, 4>(j, p, grid, s)
                           : launch_gemv_ks_lr<FMT, 1, NW, 32, 1, 8>(j, p, grid, s);
@@ -592,18 +612,20 @@ qg_status run_gemv_fma(const char* op, const CallCfg& cfg, const HostPart* parts
   const GemvPlan pl = plan_gemv<FMT>(m, k, NW);
   const int ks = ks_chunks<FMT, NW>(cfg, pl, k);
   if (ks) {
-    // Up to 16 waves per CU (two 8-wave or four 4-wave workgroups; they are
-    // resident together where the kernel stays within 128 VGPRs), walking row
-    // groups beyond that.  Measured on Q4_K K = 4096 at N = 6144 ... 28672
-    // rows: 3-12% faster than 8 waves per CU.
-    const int ks_wv = ks_waves<FMT>(k, pl.l);
+    // Up to 16 waves per CU (one 16-wave, two 8-wave or four 4-wave
+    // workgroups; they are resident together where the kernel stays within
+    // 128 VGPRs), walking row groups beyond that.  Measured on Q4_K K = 4096
+    // at N = 6144 ... 28672 rows: 3-12% faster than 8 waves per CU.
+    int64_t rows16 = 0;  // rows of all parts, each rounded up to 16-row groups
+    for (int pi = 0; pi < nparts; ++pi) rows16 += cdiv(parts[pi].n, 16) * 16;
+    const int ks_wv = ks_waves<FMT>(k, pl.l, pl.mt, NW, rows16);
     const int64_t rows_per_group = kWave / (pl.l / ks_wv) * pl.r;
     GemvParams p = gemv_params(parts, nparts, NW, false, rows_per_group, k, gs, row_bytes_of<FMT>(k));
     p.kt = pl.kt;
-    const int64_t cap = 2 * (8 / ks_wv) * device_cus();
+    const int64_t cap = (16 / ks_wv) * device_cus();
     const int64_t grid = p.n_groups < cap ? p.n_groups : cap;
     for (int64_t m0 = 0; m0 < m; m0 += pl.mt) {
-      const hipError_t e = launch_gemv_ks<FMT, NW>(pl, ks, m_tile(p, x, m0, m, k, pl.mt), dim3((unsigned)grid), s);
+      const hipError_t e = launch_gemv_ks<FMT, NW>(pl, ks, ks_wv, m_tile(p, x, m0, m, k, pl.mt), dim3((unsigned)grid), s);
       if (e != hipSuccess) return launch_error(op, "launch setup failed", e);
     }
     return launch_status(op);

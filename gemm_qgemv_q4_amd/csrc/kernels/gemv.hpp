@@ -616,10 +616,10 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams p) {
 //     then pairs of pairs, and so on.
 // A workgroup walks row groups of 64/LW*R rows; x stays in LDS between them.
 template <int FMT, int MT, int NW, int L, int R, int J, int WV, bool MULTI>
-__global__ void __launch_bounds__(512) gemv_ks_kernel(GemvParams p) {
+__global__ void __launch_bounds__(64 * WV) gemv_ks_kernel(GemvParams p) {
   // the in-wave part of the butterfly below covers 4 or 8 virtual lanes
-  static_assert((L == 32 || L == 64) && (WV == 4 || WV == 8) && (L / WV == 4 || L / WV == 8),
-                "4 or 8 waves of 4 or 8 virtual lanes");
+  static_assert((L == 32 || L == 64) && (WV == 4 || WV == 8 || WV == 16) && (L / WV == 4 || L / WV == 8),
+                "4, 8 or 16 waves of 4 or 8 virtual lanes");
   constexpr int CH = FmtTraits<FMT>::CH;
   constexpr int NE4 = CH / 4;
   constexpr int LW = L / WV;             // lanes of a row inside one wave
@@ -783,7 +783,15 @@ __global__ void __launch_bounds__(512) gemv_ks_kernel(GemvParams p) {
       const float b0 = a[0 * WS] + a[1 * WS];
       const float b1 = a[2 * WS] + a[3 * WS];
       float t;
-      if constexpr (WV == 8) {
+      if constexpr (WV == 16) {
+        const float b2 = a[4 * WS] + a[5 * WS];
+        const float b3 = a[6 * WS] + a[7 * WS];
+        const float b4 = a[8 * WS] + a[9 * WS];
+        const float b5 = a[10 * WS] + a[11 * WS];
+        const float b6 = a[12 * WS] + a[13 * WS];
+        const float b7 = a[14 * WS] + a[15 * WS];
+        t = ((b0 + b1) + (b2 + b3)) + ((b4 + b5) + (b6 + b7));
+      } else if constexpr (WV == 8) {
         const float b2 = a[4 * WS] + a[5 * WS];
         const float b3 = a[6 * WS] + a[7 * WS];
         t = (b0 + b1) + (b2 + b3);

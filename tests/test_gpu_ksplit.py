@@ -149,3 +149,40 @@ def test_dual_and_multi_ksplit_rows_of_x_equal_chunked(lib, m):
     dws, dxm = [dev(w) for w in ws], dev(xm)
     a, b = both(lambda: host(lib.qgemv_q4_k_multi(dws, dxm, list(ns), k)))
     assert np.array_equal(bits(a), bits(b))
+
+
+# Row counts whose 16-row groups fill the CUs in one round take 16-wave
+# workgroups (one per CU) at 64 lanes per row; the additions are the same.
+@pytest.mark.parametrize("fmt,n,k", [("q4_k", 4096, 4096), ("q4_k", 3600, 8192), ("q4_0", 4000, 4096),
+                                     ("q4_0", 3900, 6144)])
+def test_sixteen_wave_groups_equal_chunked(lib, fmt, n, k):
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if not (3 * cus <= 4 * -(-n // 16) <= 4 * cus):
+        pytest.skip(f"{n} rows are not one round of 16-row groups on {cus} CUs")
+    if fmt == "q4_k":
+        w, x = synth.q4_k_case(8600 + n, 1, n, k)
+        call, dec = lib.qgemv_q4_k, oracle.decode_q4_k
+    else:
+        w, x = synth.q4_0_case(8600 + n, 1, n, k)
+        call, dec = lib.qgemv_q4_0, oracle.decode_q4_0
+    dw, dx = dev(w), dev(x)
+    a, b = both(lambda: host(call(dw, dx, n, k)))
+    assert np.array_equal(bits(a), bits(b))
+    assert_close(a, dec(w, n, k), x, f"{fmt} 16 waves n{n} k{k}")
+
+
+def test_sixteen_wave_multi_part_equals_single_calls(lib):
+    """Parts of 2048 + 1024 + 1024 rows (one round of 16-row groups): each part
+    equals its single call and the chunked kernel."""
+    ns, k = (2048, 1024, 1024), 4096
+    ws, x = synth.q4_k_multi_case(8700, 1, ns, k)
+    dws, dx = [dev(w) for w in ws], dev(x)
+    a, b = both(lambda: host(lib.qgemv_q4_k_multi(dws, dx, list(ns), k)))
+    assert np.array_equal(bits(a), bits(b))
+    col = 0
+    for w, dw, nn in zip(ws, dws, ns):
+        single = host(lib.qgemv_q4_k(dw, dx, nn, k))
+        assert np.array_equal(bits(a[:, col:col + nn]), bits(single))
+        col += nn
+    assert_close(a[:, :ns[0]], oracle.decode_q4_k(ws[0], ns[0], k), x, "multi part 0")
