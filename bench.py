@@ -70,10 +70,14 @@ class Case:
     """One workload: device inputs rotated over copies, a launch closure,
     byte/flop counts, and the oracle call on the same host inputs."""
 
-    def __init__(self, name, desc, nbytes, flops, copies, launch, bound="hbm", oracle=None, context=None):
+    def __init__(self, name, desc, nbytes, flops, copies, launch, bound="hbm", oracle=None, context=None,
+                 gemm_shape=None):
         self.name, self.desc, self.nbytes, self.flops = name, desc, nbytes, flops
         self.copies, self.launch, self.bound = copies, launch, bound
         self.oracle, self.context = oracle, context
+        # (M, N, K') of the bf16 GEMM that the matrix-core path issues (x split
+        # into hi + lo: K' = 2K), for the vendor-GEMM reference ceiling
+        self.gemm_shape = gemm_shape
 
 
 def _orc():
@@ -181,7 +185,7 @@ def build_cases(qg, torch, only=None):
                           2 * c["m"] * c["n"] * c["k"], r,
                           lambda i, qs_=qs_, ss_=ss_, bs_=bs_, dx=dx, qkv=qkv, r=r, gs=c["gs"]:
                           qg.qmm_affine_t(dx, qs_[i % r], ss_[i % r], bs_[i % r], gs, y=qkv),
-                          bound="mfma",
+                          bound="mfma", gemm_shape=(c["m"], c["n"], 2 * c["k"]),
                           oracle=lambda x=x, q=q, s=s, b=b, c=c:
                           _orc().qmm_affine_t(x, q, s, b, c["m"], c["n"], c["k"], c["gs"])))
         # the same product through the allocation-free entry point (static
@@ -268,6 +272,7 @@ def build_cases(qg, torch, only=None):
                           2 * c["m"] * c["n"] * c["k"], r,
                           lambda i, ws=ws, dx=dx, y=y, r=r, n=c["n"], k=c["k"]:
                           qg.qgemv_q4_0(ws[i % r], dx, n, k, y=y), bound="mfma",
+                          gemm_shape=(c["m"], c["n"], 2 * c["k"]),
                           oracle=lambda w=w, x=x, c=c: _orc().qgemv_q4_0(w, x, c["m"], c["n"], c["k"])))
     # fused projection + q|k|v split on the prefill workload
     if want("prefill_qkv_fused_512x2048"):
@@ -344,6 +349,22 @@ def copy_ceiling(torch, nbytes, calls, warmup):
     return {"us": round(us, 3), "GBps": round(8 * n / (us * 1e-6) / 1e9, 1), "copies": pairs}
 
 
+def gemm_ceiling(torch, m, n, k, calls, warmup):
+    """The vendor bf16 GEMM (torch.matmul, hipBLASLt) of the matrix-core
+    path's issued shape: x [m, k] times a bf16 weight [n, k] transposed, f32
+    accumulation, with the weight rotated over >= 1 GiB of copies like the
+    quantized weights.  A reference ceiling for the matrix-core kernels: the
+    same MFMA work on operands that need no decode."""
+    a = torch.randn(m, k, device="cuda", dtype=torch.bfloat16)
+    copies = max(2, min(64, -(-ROTATE_BYTES // (n * k * 2))))
+    bs = [torch.randn(n, k, device="cuda", dtype=torch.bfloat16) for _ in range(copies)]
+    reps, _ = _replay_timing(torch, lambda i: torch.matmul(a, bs[i % copies].t()), calls, warmup)
+    del a, bs
+    us = reps[0]
+    return {"us": round(us, 3), "TFLOPs": round(2 * m * n * k / (us * 1e-6) / 1e12, 1), "copies": copies,
+            "shape": f"bf16 [{m}, {k}] x [{n}, {k}]^T"}
+
+
 def time_case(torch, case, steps, warmup, ceiling=True, profile=False):
     """Time ceil(copies / steps) passes of `steps` calls per replay (so that
     every replay reads every rotation copy), plus one cold call, and the copy
@@ -388,6 +409,10 @@ def time_case(torch, case, steps, warmup, ceiling=True, profile=False):
         out["copy_ceiling"] = cc
         out["copy_ceiling_GBps"] = cc["GBps"]
         out["frac_of_copy_ceiling"] = round(gbps / cc["GBps"], 4)
+    if ceiling and not profile and case.bound == "mfma" and case.gemm_shape:
+        gc = gemm_ceiling(torch, *case.gemm_shape, min(calls, 200), warmup)
+        out["vendor_bf16_gemm"] = gc
+        out["frac_of_vendor_bf16_gemm_time"] = round(gc["us"] / us, 4)
     if case.flops:
         out["TFLOPs"] = round(case.flops / (us * 1e-6) / 1e12, 2)
     if case.bound == "mfma":
