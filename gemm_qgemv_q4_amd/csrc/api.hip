@@ -653,6 +653,29 @@ size_t mfma_scratch_bytes(int64_t m, int64_t k, int64_t gs) {
   return 2 * bx + 2 * bs;
 }
 
+// Row tiles per XCD block of the matrix-core kernel (0: consecutive tiles).
+// The 8 XCDs each take an equal block of mb row tiles by nb column tiles that
+// together tile the grid; an XCD's L2 then fetches mb tiles' x split (xb
+// bytes each) and nb tiles' weight rows (wb bytes each), and the block shape
+// with the fewest such bytes wins.  Q4_0 512 x 4096 x 4096 (8 x 32 tiles of
+// 64 x 128): 4 x 8 blocks fetch 4 MB of x and 2.4 MB of weights per XCD
+// where the consecutive order (8 x 4) fetched the whole 8 MB x split.
+int xcd_block_rows(int64_t tiles_m, int64_t tiles_n, int64_t xb, int64_t wb) {
+  const int64_t total = tiles_m * tiles_n;
+  if (total % 8 != 0) return 0;
+  const int64_t per = total / 8;
+  int best = 0;
+  int64_t best_cost = 0;
+  for (int64_t mb = tiles_m; mb >= 1 && mb * 8 >= tiles_m; mb /= 2) {
+    if (tiles_m % mb != 0 || per % mb != 0) continue;
+    const int64_t nb = per / mb;
+    if (tiles_n % nb != 0 || (tiles_m / mb) * (tiles_n / nb) != 8) continue;
+    const int64_t cost = mb * xb + nb * wb;
+    if (best == 0 || cost < best_cost) best = (int)mb, best_cost = cost;
+  }
+  return best;
+}
+
 // x -> (x_hi, x_lo, group sums) in `scratch` (mfma_scratch_bytes, 256-byte
 // aligned), then one launch of the matrix-core kernel over every weight
 // stream's column tiles (both streams of a dual part are two parts of it).
@@ -707,6 +730,7 @@ qg_status launch_mfma(const char* op, const HostPart* parts, int nparts, int nw,
   mp.gs = gs;
   mp.tiles_m = (int)cdiv(m, 64 * sm);
   mp.tiles_n = (int)tiles_n;
+  mp.xcd_mb = xcd_block_rows(mp.tiles_m, mp.tiles_n, 64 * sm * k * 4, 128 * mp.row_bytes);
   const dim3 grid((unsigned)(mp.tiles_m * mp.tiles_n));
   // 128x128 runs as 4 x 2 wave pairs of 32x64 sub-tiles, 64x128 as 2 x 2
   const dim3 block((unsigned)(512 * sm));

@@ -117,6 +117,8 @@ struct MfmaParams {
   long long row_bytes;   // bytes per weight row
   int m, k, gs;
   int tiles_m, tiles_n;  // tiles_n over all parts
+  int xcd_mb;            // > 0: each XCD takes a block of xcd_mb row tiles by
+                         // tiles/(8 xcd_mb) column tiles; 0: consecutive tiles
 };
 
 constexpr int kBK = 64;
@@ -225,14 +227,26 @@ __global__ void __launch_bounds__(128 * SM * SN, 8 / TI) qmm_mfma_kernel(MfmaPar
   const int sub = wid % NSUB;
   const int wm = sub / SN, wn = sub % SN;
 
-  // Tiles of one column block (same weights) are consecutive and the
-  // dispatcher spreads consecutive ids over the 8 XCDs, so give each XCD a
-  // contiguous range of tiles when the count allows it.
+  // The dispatcher spreads consecutive workgroup ids over the 8 XCDs, each
+  // with its own L2.  With xcd_mb set, XCD x = id % 8 takes a block of xcd_mb
+  // row tiles by nb column tiles, so that its L2 holds the x rows and the
+  // weight rows of that block only (the host picks the block shape that
+  // fetches the fewest bytes).  Otherwise each XCD takes a contiguous range of
+  // tiles (row tiles fastest) when the count allows it.
   const int total = p.tiles_m * p.tiles_n;
-  int tile = blockIdx.x;
-  if ((total & 7) == 0) tile = (tile & 7) * (total >> 3) + (tile >> 3);
-  const int tm = tile % p.tiles_m;
-  const int tn = tile / p.tiles_m;  // column tile over all parts
+  int tm, tn;  // tn: column tile over all parts
+  if (p.xcd_mb > 0) {
+    const int x = blockIdx.x & 7, i = blockIdx.x >> 3;
+    const int rms = p.tiles_m / p.xcd_mb;  // blocks along the rows
+    const int nb = (total >> 3) / p.xcd_mb;
+    tm = (x % rms) * p.xcd_mb + i % p.xcd_mb;
+    tn = (x / rms) * nb + i / p.xcd_mb;
+  } else {
+    int tile = blockIdx.x;
+    if ((total & 7) == 0) tile = (tile & 7) * (total >> 3) + (tile >> 3);
+    tm = tile % p.tiles_m;
+    tn = tile / p.tiles_m;
+  }
   // a single-part launch (MULTI false) reads part 0 at fixed argument offsets
   MfmaPart pt = p.part[0];
   if constexpr (MULTI) {
