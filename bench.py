@@ -16,7 +16,9 @@ one cold call after a 512 MiB cache flush is reported beside it.
 
 Beside each workload: the same protocol applied to a plain device copy
 (torch.mul(src, 1.0, out=dst)) that moves the workload's byte count (half read,
-half written), as a measured ceiling for a memory-bound kernel of that size,
+half written) and to a plain streaming read of that byte count
+(libqg_read.so), as measured ceilings for a memory-bound kernel of that size;
+beside the matrix-core workloads, the vendor bf16 GEMM of the shape they issue;
 and (unless --no-cpu) the f64 CPU oracle timed on the host at 1 thread and at
 all cores.  The headline's `cpu_baseline` is the oracle on a bounded sample of
 full headline calls.  `roofline.traffic` comes from the committed rocprofv3
@@ -349,6 +351,44 @@ def copy_ceiling(torch, nbytes, calls, warmup):
     return {"us": round(us, 3), "GBps": round(8 * n / (us * 1e-6) / 1e9, 1), "copies": pairs}
 
 
+_READ_LIB = None
+
+
+def read_ceiling(torch, nbytes, calls, warmup):
+    """The plain streaming read of the workload's byte count (libqg_read.so,
+    16-byte loads, nothing written), rotated over >= 1 GiB of buffers and
+    timed with the same graph protocol: the read-only counterpart of the copy
+    ceiling, for kernels that read far more than they write."""
+    import ctypes
+    global _READ_LIB
+    if _READ_LIB is None:
+        path = os.path.join(ROOT, "gemm_qgemv_q4_amd", "lib", "libqg_read.so")
+        _READ_LIB = ctypes.CDLL(path)
+        _READ_LIB.qg_stream_read.restype = ctypes.c_int
+        _READ_LIB.qg_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_int,
+                                             ctypes.c_void_p]
+    n16 = max(16, nbytes // 16 * 16)
+    copies = max(2, min(4096, -(-ROTATE_BYTES // n16)))
+    bufs = [torch.empty(n16, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    # 4 blocks of 256 threads per CU (16 waves) walking the buffer: the best of
+    # a sweep of 144 to 4096 blocks at 9.5 MB (3.48 us) and 57 MB (9.84 us)
+    blocks = 4 * cus
+    out = torch.zeros(blocks, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def launch(i):
+        rc = _READ_LIB.qg_stream_read(bufs[i % copies].data_ptr(), n16, out.data_ptr(), blocks,
+                                      torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"qg_stream_read failed ({rc})")
+
+    reps, _ = _replay_timing(torch, launch, calls, warmup)
+    del bufs, out, stream
+    us = reps[0]
+    return {"us": round(us, 3), "GBps": round(n16 / (us * 1e-6) / 1e9, 1), "copies": copies}
+
+
 def gemm_ceiling(torch, m, n, k, calls, warmup):
     """The vendor bf16 GEMM (torch.matmul, hipBLASLt) of the matrix-core
     path's issued shape: x [m, k] times a bf16 weight [n, k] transposed, f32
@@ -409,6 +449,10 @@ def time_case(torch, case, steps, warmup, ceiling=True, profile=False):
         out["copy_ceiling"] = cc
         out["copy_ceiling_GBps"] = cc["GBps"]
         out["frac_of_copy_ceiling"] = round(gbps / cc["GBps"], 4)
+        rc = read_ceiling(torch, case.nbytes, calls, warmup)
+        out["read_ceiling"] = rc
+        out["read_ceiling_GBps"] = rc["GBps"]
+        out["frac_of_read_ceiling"] = round(gbps / rc["GBps"], 4)
     if ceiling and not profile and case.bound == "mfma" and case.gemm_shape:
         gc = gemm_ceiling(torch, *case.gemm_shape, min(calls, 200), warmup)
         out["vendor_bf16_gemm"] = gc
@@ -510,7 +554,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", default=None, help="run only workloads whose name starts with this")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU timings")
-    ap.add_argument("--no-ceiling", action="store_true", help="skip the plain-copy ceilings")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the plain-copy, plain-read and vendor-GEMM ceilings")
     ap.add_argument("--profile", action="store_true",
                     help="for counter runs: one timed replay per workload, no cold calls, no ceilings, no oracle")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -535,7 +579,8 @@ def main():
         log(f"[bench] {case.name}: {case.desc} ({case.copies} rotating copies)")
         us, res = time_case(torch, case, args.steps, args.warmup, ceiling=not args.no_ceiling, profile=args.profile)
         per[case.name] = res
-        cc = f", copy ceiling {res['copy_ceiling_GBps']} GB/s" if "copy_ceiling_GBps" in res else ""
+        cc = (f", copy ceiling {res['copy_ceiling_GBps']} GB/s, read ceiling {res['read_ceiling_GBps']} GB/s"
+              if "copy_ceiling_GBps" in res else "")
         log(f"[bench] {case.name}: {res['us_per_call']} us/call, {res['GBps']} GB/s{cc}")
         if case.name == HEADLINE:
             head_us = us
@@ -588,7 +633,9 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(value / HBM_PEAK_GBS, 4),
                      "traffic": read_traffic(),
                      "copy_ceiling_GBps": h.get("copy_ceiling_GBps"),
-                     "frac_of_copy_ceiling": h.get("frac_of_copy_ceiling")},
+                     "frac_of_copy_ceiling": h.get("frac_of_copy_ceiling"),
+                     "read_ceiling_GBps": h.get("read_ceiling_GBps"),
+                     "frac_of_read_ceiling": h.get("frac_of_read_ceiling")},
         "per_config": per,
     }
     if not args.no_cpu:

@@ -52,6 +52,23 @@ def build(verbose: bool = True) -> str:
     os.replace(tmp, out)
     if verbose:
         print(f"built {out} in {time.time() - t0:.1f}s")
+    build_read_probe(verbose)
+    return out
+
+
+def build_read_probe(verbose: bool = True) -> str:
+    """libqg_read.so: the streaming-read probe that bench.py times as a read
+    ceiling beside each memory-bound workload (not part of the product ABI)."""
+    out = os.path.join(LIBDIR, "libqg_read.so")
+    tmp = out + ".tmp"
+    cmd = [hipcc(), *HIP_FLAGS, os.path.join(CSRC, "stream_read.hip"), "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc failed for the read probe ({res.returncode})")
+    os.replace(tmp, out)
+    if verbose:
+        print(f"built {out}")
     return out
 
 
