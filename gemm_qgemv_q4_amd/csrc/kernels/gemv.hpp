@@ -602,7 +602,7 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams p) {
 // (rows per lane), so both kernels give the same bits; what changes is which
 // wave does which of them.
 //   * The L lanes of a row in gemv_kernel become "virtual lanes" spread over
-//     the WV waves of a workgroup (4 or 8): wave w holds virtual lanes
+//     the WV waves of a workgroup (4, 8 or 16): wave w holds virtual lanes
 //     LW*w .. LW*w+LW-1 (LW = L/WV) of 64/LW row sets of R rows each (hardware
 //     lane = LW * set + c, virtual lane LW*w + c), so it needs x only at its
 //     own chunks LW*w + c + L*j: one WV-th of K.
