@@ -73,13 +73,14 @@ class Case:
     byte/flop counts, and the oracle call on the same host inputs."""
 
     def __init__(self, name, desc, nbytes, flops, copies, launch, bound="hbm", oracle=None, context=None,
-                 gemm_shape=None):
+                 gemm_shape=None, bias_groups=0):
         self.name, self.desc, self.nbytes, self.flops = name, desc, nbytes, flops
         self.copies, self.launch, self.bound = copies, launch, bound
         self.oracle, self.context = oracle, context
         # (M, N, K') of the bf16 GEMM that the matrix-core path issues (x split
         # into hi + lo: K' = 2K), for the vendor-GEMM reference ceiling
         self.gemm_shape = gemm_shape
+        self.bias_groups = bias_groups  # K / group size for formats with a bias product, else 0
 
 
 def _orc():
@@ -187,7 +188,7 @@ def build_cases(qg, torch, only=None):
                           2 * c["m"] * c["n"] * c["k"], r,
                           lambda i, qs_=qs_, ss_=ss_, bs_=bs_, dx=dx, qkv=qkv, r=r, gs=c["gs"]:
                           qg.qmm_affine_t(dx, qs_[i % r], ss_[i % r], bs_[i % r], gs, y=qkv),
-                          bound="mfma", gemm_shape=(c["m"], c["n"], 2 * c["k"]),
+                          bound="mfma", gemm_shape=(c["m"], c["n"], 2 * c["k"]), bias_groups=c["k"] // c["gs"],
                           oracle=lambda x=x, q=q, s=s, b=b, c=c:
                           _orc().qmm_affine_t(x, q, s, b, c["m"], c["n"], c["k"], c["gs"])))
         # the same product through the allocation-free entry point (static
@@ -461,6 +462,16 @@ def time_case(torch, case, steps, warmup, ceiling=True, profile=False):
         out["TFLOPs"] = round(case.flops / (us * 1e-6) / 1e12, 2)
     if case.bound == "mfma":
         out["frac_mfma_bf16_peak_useful"] = round(case.flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+        if case.gemm_shape:
+            # issued by the matrix cores: the product with x split into hi + lo
+            # (2x the useful flops) plus, for formats with a bias term, the bias
+            # product over the group index (hi*hi, hi*lo, lo*hi, groups padded
+            # to 32)
+            m, n, k2 = case.gemm_shape
+            issued = 2 * m * n * k2 + (3 * 2 * m * n * -(-case.bias_groups // 32) * 32 if case.bias_groups else 0)
+            out["flops_issued"] = issued
+            out["TFLOPs_issued"] = round(issued / (us * 1e-6) / 1e12, 2)
+            out["frac_mfma_bf16_peak_issued"] = round(issued / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
     if case.context:
         out.update(case.context)
     return us, out
