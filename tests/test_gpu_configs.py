@@ -117,3 +117,40 @@ def test_config_prefill_qkv_fused_512x2048(lib):
         assert np.array_equal(host(got).view(np.uint32), host(ref).view(np.uint32))
     y = np.concatenate([host(t) for t in outs], axis=1)
     assert_close(y, oracle.decode_affine(q, s, b, c["n"], c["k"], c["gs"]), x, "C fused qkv")
+
+
+def test_config_prefills_replayed_from_a_graph(lib):
+    """bench.py times the prefill products as graph replays, where their
+    scratch belongs to the graph: the replays give the eager bits, and the
+    affine product is within the bar of the oracle."""
+    import torch
+    c = CFG["prefill_qkv_512x2048"]
+    x, q, s, b = synth.affine_case(c["seed"], c["m"], c["n"], c["k"], c["gs"])
+    dx, dq, ds, db = dev(x), dev(q), dev(s), dev(b)
+    n0 = NXT["q4_0_prefill_512x4096"]
+    w0, x0 = synth.q4_0_case(n0["seed"], n0["m"], n0["n"], n0["k"])
+    dw0, dx0 = dev(w0), dev(x0)
+    eager_a = host(lib.qmm_affine_t(dx, dq, ds, db, c["gs"]))
+    eager_q = host(lib.qgemv_q4_0(dw0, dx0, n0["n"], n0["k"]))
+    eager_f = [host(t) for t in lib.qmm_affine_t_qkv(dx, dq, ds, db, c["gs"], c["q_sp"], c["k_sp"], c["v_sp"])]
+    ya = torch.empty((c["m"], c["n"]), dtype=torch.float32, device="cuda")
+    yq = torch.empty((n0["m"], n0["n"]), dtype=torch.float32, device="cuda")
+    fo = [torch.empty((c["m"], sp), dtype=torch.float32, device="cuda") for sp in (c["q_sp"], c["k_sp"], c["v_sp"])]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        lib.qmm_affine_t(dx, dq, ds, db, c["gs"], y=ya)
+        lib.qgemv_q4_0(dw0, dx0, n0["n"], n0["k"], y=yq)
+        lib.qmm_affine_t_qkv(dx, dq, ds, db, c["gs"], c["q_sp"], c["k_sp"], c["v_sp"], q_out=fo[0], k_out=fo[1],
+                             v_out=fo[2])
+    bits = lambda a: np.ascontiguousarray(a).view(np.uint32)
+    for rep in range(2):
+        for t in [ya, yq, *fo]:
+            t.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(host(ya)), bits(eager_a)), f"replay {rep}: affine prefill"
+        assert np.array_equal(bits(host(yq)), bits(eager_q)), f"replay {rep}: q4_0 prefill"
+        for got, ref in zip(fo, eager_f):
+            assert np.array_equal(bits(host(got)), bits(ref)), f"replay {rep}: fused q|k|v"
+    assert_close(host(ya), oracle.decode_affine(q, s, b, c["n"], c["k"], c["gs"]), x, "C prefill gemm, replayed")
+    del g
