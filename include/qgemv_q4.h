@@ -54,8 +54,10 @@
  *    group size, that tensor's own alignment and size, and the two settings
  *    at the end of this header as the call reads them; never on the other
  *    tensors of the call.  So the equalities stated below (dual = two
- *    singles, multi-part = one call per part, packed = unpacked, fused split
- *    = product then split) hold bit for bit for every accepted alignment.
+ *    singles, multi-part = one call per part, fused split = product then
+ *    split) hold bit for bit for every accepted alignment; packed = unpacked
+ *    holds when both code tensors are 16-byte aligned (they are two tensors,
+ *    and each takes the kernel its own alignment allows).
  *  - Q4_0 blocks whose codes are all 8 (weights 0) contribute exactly 0 on
  *    every path: a row of such blocks gives +0 or -0 for any finite x.
  */
