@@ -376,7 +376,6 @@ def read_ceiling(torch, nbytes, calls, warmup):
     # a sweep of 144 to 4096 blocks at 9.5 MB (3.48 us) and 57 MB (9.84 us)
     blocks = 4 * cus
     out = torch.zeros(blocks, dtype=torch.int32, device="cuda")
-    stream = torch.cuda.current_stream()
 
     def launch(i):
         rc = _READ_LIB.qg_stream_read(bufs[i % copies].data_ptr(), n16, out.data_ptr(), blocks,
@@ -385,7 +384,7 @@ def read_ceiling(torch, nbytes, calls, warmup):
             raise RuntimeError(f"qg_stream_read failed ({rc})")
 
     reps, _ = _replay_timing(torch, launch, calls, warmup)
-    del bufs, out, stream
+    del bufs, out
     us = reps[0]
     return {"us": round(us, 3), "GBps": round(n16 / (us * 1e-6) / 1e9, 1), "copies": copies}
 
