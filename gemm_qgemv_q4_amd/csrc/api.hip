@@ -384,19 +384,20 @@ size_t ks_lds(int mt, int nw, int l, int r, int j, int wv) {
 // waves are faster (2.35 vs 2.48 us).  64 lanes per row take 8 waves (8
 // virtual lanes per wave and row), or 16 waves of 4 (row groups of 16 rows,
 // one workgroup per CU) for one weight stream and one x row when those row
-// groups fill the CUs in a single round and each lane holds at most two
-// chunks (K <= 8192; more would spill at 128 VGPRs): x is then read into each
-// CU once instead of twice.  Q4_K 4096 x 4096: 4.45 -> 4.34 us; with two
-// weight streams (6.5 -> 6.9 us) or a second round of groups (6144 rows: 6.1
-// -> 6.9 us) 16 waves are slower.
+// groups fill the CUs in whole rounds (or one round at least three quarters
+// full) and each lane holds at most two chunks (K <= 8192; more would spill
+// at 128 VGPRs): x is then read into each CU once instead of twice.  Q4_K
+// x 4096 at M = 1: 4096 rows 4.45 -> 4.34 us, 8192 rows 6.1 -> 5.9 us, 16384
+// rows 10.7 -> 9.6 us (Q4_0 alike); with two weight streams (6.5 -> 6.9 us) or
+// a part-filled last round (6144 rows: 6.1 -> 6.9 us) 16 waves are slower.
 template <int FMT>
 int ks_waves(int64_t k, int l, int mt, int nw, int64_t rows) {
   if constexpr (FMT != FMT_Q40 && FMT != FMT_Q4K) return 8;
   if (l == 64) {
     const int64_t groups16 = cdiv(rows, 16);
     const int64_t cus = device_cus();
-    const bool one_round = groups16 <= cus && 4 * groups16 >= 3 * cus;
-    return nw == 1 && mt == 1 && k / 64 <= 2 * 64 && one_round ? 16 : 8;
+    const bool rounds = (groups16 <= cus && 4 * groups16 >= 3 * cus) || groups16 % cus == 0;
+    return nw == 1 && mt == 1 && k / 64 <= 2 * 64 && rounds ? 16 : 8;
   }
   return k / 64 >= 32 ? 4 : 8;
 }

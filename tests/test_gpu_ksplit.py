@@ -151,15 +151,17 @@ def test_dual_and_multi_ksplit_rows_of_x_equal_chunked(lib, m):
     assert np.array_equal(bits(a), bits(b))
 
 
-# Row counts whose 16-row groups fill the CUs in one round take 16-wave
-# workgroups (one per CU) at 64 lanes per row; the additions are the same.
+# Row counts whose 16-row groups fill the CUs in whole rounds (or one round at
+# least three quarters full) take 16-wave workgroups (one per CU) at 64 lanes
+# per row; the additions are the same.
 @pytest.mark.parametrize("fmt,n,k", [("q4_k", 4096, 4096), ("q4_k", 3600, 8192), ("q4_0", 4000, 4096),
-                                     ("q4_0", 3900, 6144)])
+                                     ("q4_0", 3900, 6144), ("q4_k", 8192, 4096), ("q4_0", 12288, 4096)])
 def test_sixteen_wave_groups_equal_chunked(lib, fmt, n, k):
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    if not (3 * cus <= 4 * -(-n // 16) <= 4 * cus):
-        pytest.skip(f"{n} rows are not one round of 16-row groups on {cus} CUs")
+    groups = -(-n // 16)
+    if not (3 * cus <= 4 * groups <= 4 * cus or groups % cus == 0):
+        pytest.skip(f"{n} rows are not whole rounds of 16-row groups on {cus} CUs")
     if fmt == "q4_k":
         w, x = synth.q4_k_case(8600 + n, 1, n, k)
         call, dec = lib.qgemv_q4_k, oracle.decode_q4_k
