@@ -12,6 +12,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <climits>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -520,6 +521,9 @@ GemvParams gemv_params(const HostPart* parts, int nparts, int nw, bool split_str
       groups += cdiv(parts[pi].n, rows_per_group);
     }
   }
+  // unused slots start past every group: the kernels' part lookup compares
+  // against all slots without reading the part count
+  for (int pi = np; pi < kMaxParts; ++pi) p.part[pi].group0 = INT_MAX;
   p.parts = np;
   p.n_groups = (int)groups;
   p.row_bytes = row_bytes;
@@ -724,6 +728,7 @@ qg_status launch_mfma(const char* op, const HostPart* parts, int nparts, int nw,
   // product 64 us on 256 tiles of 128x128 and 72 us on 512 of 64x128.  The
   // arithmetic of an output does not depend on the shape.
   const int sm = 2 * cdiv(m, 128) * tiles_n > device_cus() ? 2 : 1;
+  for (int pi = np; pi < kMaxParts; ++pi) mp.part[pi].tile0 = INT_MAX;  // never reached
   mp.parts = np;
   mp.row_bytes = row_bytes_of<FMT>(k);
   mp.m = (int)m;

@@ -76,6 +76,21 @@ struct GemvParams {
 static_assert(offsetof(GemvParams, part) + offsetof(GemvPart, scales) == 64,
               "x, row_bytes, k, n_groups and part 0's w, y, n, group0 share the first 64 bytes");
 
+// Part of row group g in a multi-part launch.  The host sets the first group
+// of every unused part slot past the last group, so the comparisons need
+// neither the part count nor a loop bound: the loads of all first groups have
+// fixed offsets and leave together (part i's w, y, n and group0 share one
+// 64-byte line, which the lookup of part[pi] then finds in the scalar cache).
+// A loop up to `parts` reads the count from the last line of the arguments
+// first and then each first group in turn, one scalar-memory round trip after
+// another before the first weight load.
+__device__ __forceinline__ int part_of_group(const GemvParams& p, int g) {
+  int pi = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxParts; ++i) pi = g >= p.part[i].group0 ? i : pi;
+  return __builtin_amdgcn_readfirstlane(pi);
+}
+
 // CH: weights per chunk; SUMS: the format needs the per-32 sums of x (a
 // block offset or bias multiplies them).  Q4_0 decodes its codes as signed
 // values (q - 8) and has no offset term.
@@ -440,11 +455,7 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams p) {
   auto group_rows = [&](int g, View& v, int (&rows)[R], bool (&valid)[R]) {
     Span sp;
     if constexpr (MULTI) {
-      int pi = 0;
-      for (int i = 1; i < p.parts; ++i)
-        if (g >= p.part[i].group0) pi = i;
-      pi = __builtin_amdgcn_readfirstlane(pi);
-      view_of(p.part[pi], v, sp);
+      view_of(p.part[part_of_group(p, g)], v, sp);
     } else {
       view_of(p.part[0], v, sp);
     }
@@ -654,11 +665,7 @@ __global__ void __launch_bounds__(64 * WV) gemv_ks_kernel(GemvParams p) {
   };
   auto view_of = [&](int g, View& v) {
     int pi = 0;
-    if constexpr (MULTI) {
-      for (int i = 1; i < p.parts; ++i)
-        if (g >= p.part[i].group0) pi = i;
-      pi = __builtin_amdgcn_readfirstlane(pi);
-    }
+    if constexpr (MULTI) pi = part_of_group(p, g);
     const GemvPart& pt = p.part[pi];
 #pragma unroll
     for (int s = 0; s < NW; ++s) v.w[s] = pt.w[s];
@@ -686,10 +693,13 @@ __global__ void __launch_bounds__(64 * WV) gemv_ks_kernel(GemvParams p) {
     }
   };
 
+  // The first group's view is looked up before the range check (the grid never
+  // exceeds the groups; the check is a guard), so that a multi-part launch
+  // fetches its part table together with the group count.
   int g = blockIdx.x;
-  if (g >= p.n_groups) return;
   View cv;
   view_of(g, cv);
+  if (g >= p.n_groups) return;
   int grid;
 
   // x of this wave's chunks, for each of the MT rows of x: float4
@@ -799,10 +809,7 @@ __global__ void __launch_bounds__(64 * WV) gemv_ks_kernel(GemvParams p) {
         t = b0 + b1;
       }
       int pi = 0;
-      if constexpr (MULTI) {
-        for (int i = 1; i < p.parts; ++i)
-          if (g_done >= p.part[i].group0) pi = i;
-      }
+      if constexpr (MULTI) pi = part_of_group(p, g_done);
       const GemvPart& pt = p.part[pi];
       const int rr = (g_done - pt.group0) * ROWS + r;
       if (rr < pt.n && (MT == 1 || m < p.m_rows)) pt.y[s][(size_t)m * pt.ldy + rr] = t;

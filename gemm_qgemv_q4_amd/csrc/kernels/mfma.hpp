@@ -250,9 +250,11 @@ __global__ void __launch_bounds__(128 * SM * SN, 8 / TI) qmm_mfma_kernel(MfmaPar
   // a single-part launch (MULTI false) reads part 0 at fixed argument offsets
   MfmaPart pt = p.part[0];
   if constexpr (MULTI) {
+    // unused slots start past every tile (set by the host): fixed-offset
+    // loads that leave together, no read of the part count
     int pi = 0;
-    for (int i = 1; i < p.parts; ++i)
-      if (tn >= p.part[i].tile0) pi = i;
+#pragma unroll
+    for (int i = 1; i < kMaxParts; ++i) pi = tn >= p.part[i].tile0 ? i : pi;
     pi = __builtin_amdgcn_readfirstlane(pi);
     pt = p.part[pi];
   }

@@ -106,11 +106,7 @@ __global__ void __launch_bounds__(512) gemv_mma_kernel(GemvParams p) {
   const int gsh = __builtin_ctz((unsigned)p.gs) - 6;  // log2(gs / 64): pairs per group
   auto view_of = [&](int g, View& v) {
     int pi = 0;
-    if constexpr (MULTI) {
-      for (int i = 1; i < p.parts; ++i)
-        if (g >= p.part[i].group0) pi = i;
-      pi = __builtin_amdgcn_readfirstlane(pi);
-    }
+    if constexpr (MULTI) pi = part_of_group(p, g);
     const GemvPart& pt = p.part[pi];
     const int rr = (g - pt.group0) * ROWS + r16;
     v.row = rr < pt.n ? rr : pt.n - 1;  // clamped for the loads; not stored
@@ -230,10 +226,7 @@ __global__ void __launch_bounds__(512) gemv_mma_kernel(GemvParams p) {
       const float t = ((a[0 * WS] + a[1 * WS]) + (a[2 * WS] + a[3 * WS])) +
                       ((a[4 * WS] + a[5 * WS]) + (a[6 * WS] + a[7 * WS]));
       int pi = 0;
-      if constexpr (MULTI) {
-        for (int i = 1; i < p.parts; ++i)
-          if (g_done >= p.part[i].group0) pi = i;
-      }
+      if constexpr (MULTI) pi = part_of_group(p, g_done);
       const GemvPart& pt = p.part[pi];
       const int rr = (g_done - pt.group0) * ROWS + n;
       if (m < mrows && rr < pt.n) pt.y[0][(size_t)m * pt.ldy + rr] = t;

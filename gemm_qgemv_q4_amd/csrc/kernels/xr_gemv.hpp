@@ -110,11 +110,7 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p)
   // SLICE bytes, so every piece is 16-byte aligned when the weights are.
   auto part_of = [&](int tile) -> const GemvPart& {
     int pi = 0;
-    if constexpr (MULTI) {
-      for (int i = 1; i < p.parts; ++i)
-        if (tile >= p.part[i].group0) pi = i;
-      pi = __builtin_amdgcn_readfirstlane(pi);
-    }
+    if constexpr (MULTI) pi = part_of_group(p, tile);
     return p.part[pi];
   };
   constexpr int PPR = SLICE / 16;  // pieces per row
