@@ -389,8 +389,10 @@ size_t ks_lds(int mt, int nw, int l, int r, int j, int wv) {
 // full) and each lane holds at most two chunks (K <= 8192; more would spill
 // at 128 VGPRs): x is then read into each CU once instead of twice.  Q4_K
 // x 4096 at M = 1: 4096 rows 4.45 -> 4.34 us, 8192 rows 6.1 -> 5.9 us, 16384
-// rows 10.7 -> 9.6 us (Q4_0 alike); with two weight streams (6.5 -> 6.9 us) or
-// a part-filled last round (6144 rows: 6.1 -> 6.9 us) 16 waves are slower.
+// rows 10.7 -> 9.6 us (Q4_0 alike); with two weight streams per group (6.5 ->
+// 6.9 us; a dual product runs as a pair launch instead, see
+// launch_gemv_ks_pair) or a part-filled last round (6144 rows: 6.1 -> 6.9 us)
+// 16 waves are slower.
 template <int FMT>
 int ks_waves(int64_t k, int l, int mt, int nw, int64_t rows) {
   if constexpr (FMT != FMT_Q40 && FMT != FMT_Q4K) return 8;
@@ -608,6 +610,25 @@ qg_status run_plain(const char* op, const HostPart* parts, int nparts, const flo
   return launch_status(op);
 }
 
+// The two weight streams of a dual Q4_0 product as one stream of twice the
+// row groups (16-wave K-sliced kernel, one x row): each group holds one
+// stream's rows, as in the single calls, which take the same kernel shape.
+template <int FMT>
+hipError_t launch_gemv_ks_pair(int j, const GemvParams& p, dim3 grid, hipStream_t s) {
+  if constexpr (FMT == FMT_Q40) {
+    const size_t lds = ks_lds<FMT>(1, 1, 64, 1, j, 16);
+    switch (j) {
+      case 1:
+        hipLaunchKernelGGL((gemv_ks_kernel<FMT, 1, 1, 64, 1, 1, 16, false, true>), grid, dim3(1024), lds, s, p);
+        return hipSuccess;
+      case 2:
+        hipLaunchKernelGGL((gemv_ks_kernel<FMT, 1, 1, 64, 1, 2, 16, false, true>), grid, dim3(1024), lds, s, p);
+        return hipSuccess;
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
 // FMA GEMV: the K-sliced kernel where it applies, else the chunked one (same
 // bits), over all m-tiles of x.
 template <int FMT, int NW>
@@ -623,6 +644,23 @@ qg_status run_gemv_fma(const char* op, const CallCfg& cfg, const HostPart* parts
     // at N = 6144 ... 28672 rows: 3-12% faster than 8 waves per CU.
     int64_t rows16 = 0;  // rows of all parts, each rounded up to 16-row groups
     for (int pi = 0; pi < nparts; ++pi) rows16 += cdiv(parts[pi].n, 16) * 16;
+    if constexpr (FMT == FMT_Q40 && NW == 2) {
+      // A dual product whose two streams together fill the CUs in whole
+      // rounds of 16-row groups: one stream of twice the groups on 16 waves.
+      // Q4_0 4096 x 4096 at M = 1: 6.43 -> 5.9 us against the two-stream
+      // kernel on 8 waves (whose 16-wave form measured 6.9 us).
+      if (m == 1 && nparts == 1 && pl.mt == 1 && pl.l == 64 && pl.r == 1 && ks <= 2 &&
+          ks_waves<FMT>(k, pl.l, 1, 1, 2 * rows16) == 16) {
+        GemvParams p = m_tile(gemv_params(parts, 1, 2, false, 16, k, gs, row_bytes_of<FMT>(k)), x, 0, 1, k, 1);
+        p.n_groups *= 2;
+        p.kt = pl.kt;
+        const int64_t cus = device_cus();
+        const int64_t grid = p.n_groups < cus ? p.n_groups : cus;
+        const hipError_t e = launch_gemv_ks_pair<FMT>(ks, p, dim3((unsigned)grid), s);
+        if (e != hipSuccess) return launch_error(op, "launch setup failed", e);
+        return launch_status(op);
+      }
+    }
     const int ks_wv = ks_waves<FMT>(k, pl.l, pl.mt, NW, rows16);
     const int64_t rows_per_group = kWave / (pl.l / ks_wv) * pl.r;
     GemvParams p = gemv_params(parts, nparts, NW, false, rows_per_group, k, gs, row_bytes_of<FMT>(k));

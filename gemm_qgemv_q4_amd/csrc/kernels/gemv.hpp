@@ -626,11 +626,15 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams p) {
 //     combine the waves' partial sums through LDS as (w0 + w1, w2 + w3, ...),
 //     then pairs of pairs, and so on.
 // A workgroup walks row groups of 64/LW*R rows; x stays in LDS between them.
-template <int FMT, int MT, int NW, int L, int R, int J, int WV, bool MULTI>
+// PAIR: the two weight streams of part 0 (a dual product, NW = 1) run as one
+// stream of twice the row groups, the first half on w[0] / y[0] and the second
+// on w[1] / y[1]; each group then holds one stream's rows, as in a single call.
+template <int FMT, int MT, int NW, int L, int R, int J, int WV, bool MULTI, bool PAIR = false>
 __global__ void __launch_bounds__(64 * WV) gemv_ks_kernel(GemvParams p) {
   // the in-wave part of the butterfly below covers 4 or 8 virtual lanes
   static_assert((L == 32 || L == 64) && (WV == 4 || WV == 8 || WV == 16) && (L / WV == 4 || L / WV == 8),
                 "4, 8 or 16 waves of 4 or 8 virtual lanes");
+  static_assert(!PAIR || (NW == 1 && !MULTI), "a pair launch has one stream per group and one part");
   constexpr int CH = FmtTraits<FMT>::CH;
   constexpr int NE4 = CH / 4;
   constexpr int LW = L / WV;             // lanes of a row inside one wave
@@ -663,17 +667,25 @@ __global__ void __launch_bounds__(64 * WV) gemv_ks_kernel(GemvParams p) {
     const float* bi;
     int row[R];
   };
+  // groups of one stream of a pair launch
+  const int pair_groups = PAIR ? (p.part[0].n + ROWS - 1) / ROWS : 0;
   auto view_of = [&](int g, View& v) {
     int pi = 0;
     if constexpr (MULTI) pi = part_of_group(p, g);
     const GemvPart& pt = p.part[pi];
+    int gl = g - pt.group0;
 #pragma unroll
     for (int s = 0; s < NW; ++s) v.w[s] = pt.w[s];
+    if constexpr (PAIR) {
+      const bool second = gl >= pair_groups;
+      v.w[0] = second ? pt.w[1] : pt.w[0];
+      gl -= second ? pair_groups : 0;
+    }
     v.sc = pt.scales;
     v.bi = pt.biases;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int rr = (g - pt.group0) * ROWS + rset + RS * r;
+      const int rr = gl * ROWS + rset + RS * r;
       v.row[r] = rr < pt.n ? rr : pt.n - 1;
     }
   };
@@ -811,8 +823,15 @@ __global__ void __launch_bounds__(64 * WV) gemv_ks_kernel(GemvParams p) {
       int pi = 0;
       if constexpr (MULTI) pi = part_of_group(p, g_done);
       const GemvPart& pt = p.part[pi];
-      const int rr = (g_done - pt.group0) * ROWS + r;
-      if (rr < pt.n && (MT == 1 || m < p.m_rows)) pt.y[s][(size_t)m * pt.ldy + rr] = t;
+      int gl = g_done - pt.group0;
+      float* yo = pt.y[s];
+      if constexpr (PAIR) {
+        const bool second = gl >= pair_groups;
+        yo = second ? pt.y[1] : pt.y[0];
+        gl -= second ? pair_groups : 0;
+      }
+      const int rr = gl * ROWS + r;
+      if (rr < pt.n && (MT == 1 || m < p.m_rows)) yo[(size_t)m * pt.ldy + rr] = t;
     }
   };
   // The first group is peeled off the loop, so that its loads, issued in

@@ -174,6 +174,28 @@ def test_sixteen_wave_groups_equal_chunked(lib, fmt, n, k):
     assert_close(a, dec(w, n, k), x, f"{fmt} 16 waves n{n} k{k}")
 
 
+# A dual Q4_0 product at one x row whose two streams together make whole rounds
+# of 16-row groups (or one round at least three quarters full) runs as one
+# stream of twice the row groups on 16 waves: ragged N, one and two chunks
+# per lane.
+@pytest.mark.parametrize("n,k", [(4096, 4096), (1999, 4096), (1536, 6144), (2048, 8192)])
+def test_dual_pair_launch_equals_chunked_and_single_calls(lib, n, k):
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    groups = 2 * -(-n // 16)
+    if not (3 * cus <= 4 * groups <= 4 * cus or groups % cus == 0):
+        pytest.skip(f"2 x {n} rows are not whole rounds of 16-row groups on {cus} CUs")
+    wa, wb, x = synth.dual_q4_0_case(8800 + n, 1, n, k)
+    dwa, dwb, dx = dev(wa), dev(wb), dev(x)
+    a, b = both(lambda: tuple(host(t) for t in lib.qgemv_dual_q4_0(dwa, dwb, dx, n, k)))
+    for s in range(2):
+        assert np.array_equal(bits(a[s]), bits(b[s])), f"stream {s}: pair launch vs chunked kernel"
+    assert np.array_equal(bits(a[0]), bits(host(lib.qgemv_q4_0(dwa, dx, n, k))))
+    assert np.array_equal(bits(a[1]), bits(host(lib.qgemv_q4_0(dwb, dx, n, k))))
+    assert_close(a[0], oracle.decode_q4_0(wa, n, k), x, f"dual pair a n{n} k{k}")
+    assert_close(a[1], oracle.decode_q4_0(wb, n, k), x, f"dual pair b n{n} k{k}")
+
+
 def test_sixteen_wave_multi_part_equals_single_calls(lib):
     """Parts of 2048 + 1024 + 1024 rows (one round of 16-row groups): each part
     equals its single call and the chunked kernel."""
