@@ -504,12 +504,13 @@ hipError_t launch_gemv_mma(int np, const GemvParams& p, dim3 grid, hipStream_t s
 GemvParams gemv_params(const HostPart* parts, int nparts, int nw, bool split_streams, int64_t rows_per_group,
                        int64_t k, int gs, int64_t row_bytes) {
   GemvParams p{};
+  for (int i = 0; i < kLaunchParts; ++i) p.hot.group0[i] = INT_MAX;  // unused slots: past every group
   int64_t groups = 0;
   int np = 0;
   for (int pi = 0; pi < nparts; ++pi) {
     const int ns = split_streams ? nw : 1;
-    for (int st = 0; st < ns; ++st) {
-      GemvPart& gp = p.part[np++];
+    for (int st = 0; st < ns && np < kLaunchParts; ++st) {  // callers keep to kLaunchParts streams
+      GemvPart gp{};
       for (int j = 0; j < 2; ++j) {
         const int src = split_streams ? st : j;
         gp.w[j] = static_cast<const uint8_t*>(parts[pi].w[src] ? parts[pi].w[src] : parts[pi].w[0]);
@@ -521,11 +522,19 @@ GemvParams gemv_params(const HostPart* parts, int nparts, int nw, bool split_str
       gp.n = (int)parts[pi].n;
       gp.group0 = (int)groups;
       groups += cdiv(parts[pi].n, rows_per_group);
+      if (np == 0) p.part0 = gp;
+      // the multi-part table: one stream per part (a dual part is a
+      // multi-part launch only with split_streams)
+      p.hot.group0[np] = gp.group0;
+      p.hot.n[np] = gp.n;
+      p.hot.w[np] = gp.w[0];
+      p.out.y[np] = gp.y[0];
+      p.out.ldy[np] = gp.ldy;
+      p.aff.scales[np] = gp.scales;
+      p.aff.biases[np] = gp.biases;
+      ++np;
     }
   }
-  // unused slots start past every group: the kernels' part lookup compares
-  // against all slots without reading the part count
-  for (int pi = np; pi < kMaxParts; ++pi) p.part[pi].group0 = INT_MAX;
   p.parts = np;
   p.n_groups = (int)groups;
   p.row_bytes = row_bytes;
@@ -538,8 +547,8 @@ GemvParams gemv_params(const HostPart* parts, int nparts, int nw, bool split_str
 GemvParams m_tile(const GemvParams& p, const float* x, int64_t m0, int64_t m, int64_t k, int mt) {
   GemvParams q = p;
   q.x = x + m0 * k;
-  for (int pi = 0; pi < p.parts; ++pi)
-    for (int st = 0; st < 2; ++st) q.part[pi].y[st] = p.part[pi].y[st] + m0 * p.part[pi].ldy;
+  for (int st = 0; st < 2; ++st) q.part0.y[st] = p.part0.y[st] + m0 * p.part0.ldy;
+  for (int pi = 0; pi < p.parts; ++pi) q.out.y[pi] = p.out.y[pi] + m0 * p.out.ldy[pi];
   q.m_rows = (int)(m - m0 < mt ? m - m0 : mt);
   return q;
 }
@@ -549,7 +558,7 @@ GemvParams m_tile(const GemvParams& p, const float* x, int64_t m0, int64_t m, in
 template <int FMT>
 qg_status run_gemv_xr(const char* op, const HostPart* parts, int nparts, int nw, const float* x, int64_t m,
                       int64_t k, int gs, hipStream_t s) {
-  if (nparts * nw > kMaxParts) return fail("%s: too many weight streams for one launch", op);
+  if (nparts * nw > kLaunchParts) return fail("%s: too many weight streams for one launch", op);
   (void)hipGetLastError();
   const GemvParams p = gemv_params(parts, nparts, nw, true, 16, k, gs, row_bytes_of<FMT>(k));
   // x of a workgroup lives in its waves' registers: one workgroup per CU for
@@ -919,10 +928,21 @@ qg_status run_mfma(const char* op, const HostPart* parts, int nparts, int nw, co
   return ls;
 }
 
-// Runs one part list whose weight streams all take `path`.
+// Runs one part list whose weight streams all take `path`.  A GEMV launch
+// takes at most kLaunchParts weight streams; longer lists run as several
+// launches (each part's arithmetic does not depend on its launch).
 template <int FMT, int NW>
 qg_status run_path(const char* op, Path path, const CallCfg& cfg, const HostPart* parts, int nparts,
                    const float* x, int64_t m, int64_t k, int gs, hipStream_t s) {
+  const int per = kLaunchParts / NW;
+  if (path != P_MFMA && path != P_PLAIN && nparts > per) {
+    for (int p0 = 0; p0 < nparts; p0 += per) {
+      const qg_status st = run_path<FMT, NW>(op, path, cfg, parts + p0, nparts - p0 < per ? nparts - p0 : per, x,
+                                             m, k, gs, s);
+      if (st != QG_OK) return st;
+    }
+    return QG_OK;
+  }
   switch (path) {
     case P_MFMA: return run_mfma<FMT>(op, parts, nparts, NW, x, m, k, gs, s);
     case P_PLAIN: return run_plain<FMT, NW>(op, parts, nparts, x, m, k, gs, s);

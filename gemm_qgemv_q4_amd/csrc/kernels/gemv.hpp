@@ -37,10 +37,10 @@
 //     number of waves or which part a row belongs to, which makes the dual
 //     kernel bitwise equal to two single calls, the multi-part product equal
 //     to one call per part, and the packed affine format equal to the u8 one.
-//   * A product may have up to kMaxParts parts: weight tensors of one format
-//     that share x, each with its own rows and output slice.  Row groups are
-//     numbered part after part, so the part of a workgroup's group is uniform
-//     and its pointers live in scalar registers.
+//   * A launch may have up to kLaunchParts parts: weight tensors of one
+//     format that share x, each with its own rows and output slice.  Row
+//     groups are numbered part after part, so the part of a workgroup's group
+//     is uniform and its pointers live in scalar registers.
 #pragma once
 #include "common.hpp"
 
@@ -57,38 +57,139 @@ struct GemvPart {
   long long ldy;
 };
 
+// Parts of one GEMV launch (a call with more parts makes several launches;
+// each part's arithmetic does not depend on its launch).
+constexpr int kLaunchParts = 4;
+
+// Part table of a multi-part launch, each array of the four parts' fields in
+// one 64-byte line: what a group's weight loads need (first group, rows,
+// weights), where its outputs go, and the affine scales and biases.  Unused
+// slots have their first group past every group.
+struct PartQuad {
+  int group0[kLaunchParts];  // slot 0 (part 0) is always 0
+  int n[kLaunchParts];
+  const uint8_t* w[kLaunchParts];
+};
+struct PartQuadOut {
+  float* y[kLaunchParts];    // output (m, r) of part i at y[i][m * ldy[i] + r]
+  long long ldy[kLaunchParts];
+};
+struct PartQuadAff {
+  const float* scales[kLaunchParts];
+  const float* biases[kLaunchParts];
+};
+
 // Kernel arguments.  The wavefront reads them through the scalar cache in
-// 64-byte lines, and every line beyond the first costs about 0.2 us before the
-// first weight load can leave (measured on a 4096 x 4096 Q4_K product): the
-// fields that a one-part block-format GEMV needs at M = 1 (x, row_bytes, k,
-// n_groups and part 0's w, y, n, group0) fill exactly the first 64 bytes.
+// 64-byte lines, and every line beyond the first costs time before the first
+// weight load can leave (about 0.2 us for one more line on a 4096 x 4096 Q4_K
+// product).  So:
+//   * line 0 holds what a one-part block-format GEMV needs at M = 1: x,
+//     row_bytes, k, n_groups and part 0's weights, outputs, rows and first
+//     group;
+//   * line 1 the rest of part 0 (scales, biases, ldy) and the settings the
+//     affine formats, tiles of several x rows and the chunked kernel read;
+//   * a multi-part launch finds its parts in one more line, its outputs in
+//     another and, for the affine formats, scales and biases in a third.
 struct GemvParams {
   const float* x;         // [m_rows, K] of this m-tile
   long long row_bytes;    // bytes per weight row
   int k;
   int n_groups;           // row groups over all parts
-  GemvPart part[kMaxParts];
+  GemvPart part0;         // the only part of a single-part launch
   int kt;                 // K elements staged per LDS tile (multiple of L*CH, or == k)
   int m_rows;             // valid x rows in this tile (<= MT)
   int gs;                 // affine group size
   int parts;
+  alignas(64) PartQuad hot;
+  PartQuadOut out;
+  PartQuadAff aff;
 };
-static_assert(offsetof(GemvParams, part) + offsetof(GemvPart, scales) == 64,
+static_assert(offsetof(GemvParams, part0) + offsetof(GemvPart, scales) == 64,
               "x, row_bytes, k, n_groups and part 0's w, y, n, group0 share the first 64 bytes");
+static_assert(offsetof(GemvParams, parts) + sizeof(int) <= 128, "part 0's rest and the settings fill line 1");
+static_assert(sizeof(PartQuad) == 64 && sizeof(PartQuadOut) == 64 && sizeof(PartQuadAff) == 64 &&
+                  offsetof(GemvParams, hot) % 64 == 0,
+              "each array of the multi-part table fills one 64-byte line");
 
-// Part of row group g in a multi-part launch.  The host sets the first group
-// of every unused part slot past the last group, so the comparisons need
-// neither the part count nor a loop bound: the loads of all first groups have
-// fixed offsets and leave together (part i's w, y, n and group0 share one
-// 64-byte line, which the lookup of part[pi] then finds in the scalar cache).
-// A loop up to `parts` reads the count from the last line of the arguments
-// first and then each first group in turn, one scalar-memory round trip after
-// another before the first weight load.
+// Part of row group g in a multi-part launch: compared against the first
+// groups of parts 1..3 (fixed offsets, one line; unused slots never match).
+// A loop over the parts up to a count read from a later line took one
+// scalar-memory round trip per part before the first weight load.
 __device__ __forceinline__ int part_of_group(const GemvParams& p, int g) {
   int pi = 0;
 #pragma unroll
-  for (int i = 1; i < kMaxParts; ++i) pi = g >= p.part[i].group0 ? i : pi;
+  for (int i = 1; i < kLaunchParts; ++i) pi = g >= p.hot.group0[i] ? i : pi;
   return __builtin_amdgcn_readfirstlane(pi);
+}
+
+// Entry pi of a part-table array, picked by selects among its values, which
+// are loaded at fixed offsets (and kept in scalar registers across the row
+// groups of a workgroup): an index computed from pi would be a scalar load
+// that waits for the lookup, before every group's weight loads.  The empty
+// asm hides each value's origin, so that the compiler cannot fold the selects
+// back into such a load.
+template <typename T>
+__device__ __forceinline__ T pick_part(const T (&a)[kLaunchParts], int pi) {
+  T v = a[0];
+#pragma unroll
+  for (int i = 1; i < kLaunchParts; ++i) {
+    T e = a[i];
+    asm("" : "+s"(e));
+    v = pi == i ? e : v;
+  }
+  return v;
+}
+// The same for pointers, picked as integers and turned back into pointers to
+// global memory: a pointer that went through the asm would lose its address
+// space, and its loads and stores would become flat instructions, which
+// count against both wait counters and make every wait a full one.
+template <typename T>
+__device__ __forceinline__ T* pick_part(T* const (&a)[kLaunchParts], int pi) {
+  unsigned long long v = reinterpret_cast<unsigned long long>(a[0]);
+#pragma unroll
+  for (int i = 1; i < kLaunchParts; ++i) {
+    unsigned long long e = reinterpret_cast<unsigned long long>(a[i]);
+    asm("" : "+s"(e));
+    v = pi == i ? e : v;
+  }
+  using G = __attribute__((address_space(1))) T*;
+  return (T*)(G)v;
+}
+
+// What the weight loads of a group need from part pi of a multi-part launch
+// (fields a format does not use are never loaded).
+struct PartLoad {
+  const uint8_t* w;
+  const float* scales;
+  const float* biases;
+  int n;
+  int group0;
+};
+__device__ __forceinline__ PartLoad part_load(const GemvParams& p, int pi) {
+  return {pick_part(p.hot.w, pi), pick_part(p.aff.scales, pi), pick_part(p.aff.biases, pi),
+          pick_part(p.hot.n, pi), pick_part(p.hot.group0, pi)};
+}
+
+// Loads line 0 of the arguments with the part table before the lookup: the
+// compiler would otherwise issue them one after the other.
+template <bool AFFINE>
+__device__ __forceinline__ void prefetch_part_table(const GemvParams& p) {
+  if constexpr (AFFINE) {
+    asm volatile("" ::"s"(p.x), "s"(p.n_groups), "s"(p.hot.group0[1]), "s"(p.aff.scales[0]));
+  } else {
+    asm volatile("" ::"s"(p.x), "s"(p.n_groups), "s"(p.hot.group0[1]));
+  }
+}
+
+// Where the outputs of part pi go (a multi-part launch has one stream per part).
+struct PartStore {
+  float* y;
+  long long ldy;
+  int n;
+  int group0;
+};
+__device__ __forceinline__ PartStore part_store(const GemvParams& p, int pi) {
+  return {pick_part(p.out.y, pi), pick_part(p.out.ldy, pi), pick_part(p.hot.n, pi), pick_part(p.hot.group0, pi)};
 }
 
 // CH: weights per chunk; SUMS: the format needs the per-32 sums of x (a
@@ -455,9 +556,18 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams p) {
   auto group_rows = [&](int g, View& v, int (&rows)[R], bool (&valid)[R]) {
     Span sp;
     if constexpr (MULTI) {
-      view_of(p.part[part_of_group(p, g)], v, sp);
+      const int pi = part_of_group(p, g);
+      const PartLoad pl = part_load(p, pi);
+      v.w[0] = pl.w;
+      v.sc = pl.scales;
+      v.bi = pl.biases;
+      sp.n = pl.n;
+      sp.group0 = pl.group0;
+      const PartStore ps = part_store(p, pi);
+      v.y[0] = ps.y;
+      v.ldy = ps.ldy;
     } else {
-      view_of(p.part[0], v, sp);
+      view_of(p.part0, v, sp);
     }
     const int n = sp.n;
     const int row0 = (g - sp.group0) * rows_per_group + wv * (P * R) + rp;
@@ -538,6 +648,7 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams p) {
 
   const bool persistent = p.kt >= p.k;
   int g = blockIdx.x;
+  if constexpr (MULTI) prefetch_part_table<FMT == FMT_AFF || FMT == FMT_AFF4>(p);
   View cv;
   int rows[R];
   bool rvalid[R];
@@ -668,25 +779,34 @@ __global__ void __launch_bounds__(64 * WV) gemv_ks_kernel(GemvParams p) {
     int row[R];
   };
   // groups of one stream of a pair launch
-  const int pair_groups = PAIR ? (p.part[0].n + ROWS - 1) / ROWS : 0;
+  const int pair_groups = PAIR ? (p.part0.n + ROWS - 1) / ROWS : 0;
   auto view_of = [&](int g, View& v) {
-    int pi = 0;
-    if constexpr (MULTI) pi = part_of_group(p, g);
-    const GemvPart& pt = p.part[pi];
-    int gl = g - pt.group0;
+    int gl, n;
+    if constexpr (MULTI) {
+      const PartLoad pl = part_load(p, part_of_group(p, g));
+      v.w[0] = pl.w;
+      v.sc = pl.scales;
+      v.bi = pl.biases;
+      n = pl.n;
+      gl = g - pl.group0;
+    } else {
+      const GemvPart& pt = p.part0;
 #pragma unroll
-    for (int s = 0; s < NW; ++s) v.w[s] = pt.w[s];
-    if constexpr (PAIR) {
-      const bool second = gl >= pair_groups;
-      v.w[0] = second ? pt.w[1] : pt.w[0];
-      gl -= second ? pair_groups : 0;
+      for (int s = 0; s < NW; ++s) v.w[s] = pt.w[s];
+      v.sc = pt.scales;
+      v.bi = pt.biases;
+      n = pt.n;
+      gl = g - pt.group0;
+      if constexpr (PAIR) {
+        const bool second = gl >= pair_groups;
+        v.w[0] = second ? pt.w[1] : pt.w[0];
+        gl -= second ? pair_groups : 0;
+      }
     }
-    v.sc = pt.scales;
-    v.bi = pt.biases;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int rr = gl * ROWS + rset + RS * r;
-      v.row[r] = rr < pt.n ? rr : pt.n - 1;
+      v.row[r] = rr < n ? rr : n - 1;
     }
   };
 
@@ -705,13 +825,15 @@ __global__ void __launch_bounds__(64 * WV) gemv_ks_kernel(GemvParams p) {
     }
   };
 
-  // The first group's view is looked up before the range check (the grid never
-  // exceeds the groups; the check is a guard), so that a multi-part launch
-  // fetches its part table together with the group count.
+  // No range check on the first group: the host never launches more
+  // workgroups than groups, and a group past the last one would only load
+  // clamped rows and store nothing.  Without the check the compiler issues the
+  // group count, x and a multi-part launch's part table together instead of
+  // one after the other.
   int g = blockIdx.x;
+  if constexpr (MULTI) prefetch_part_table<FMT == FMT_AFF || FMT == FMT_AFF4>(p);
   View cv;
   view_of(g, cv);
-  if (g >= p.n_groups) return;
   int grid;
 
   // x of this wave's chunks, for each of the MT rows of x: float4
@@ -820,18 +942,21 @@ __global__ void __launch_bounds__(64 * WV) gemv_ks_kernel(GemvParams p) {
       } else {
         t = b0 + b1;
       }
-      int pi = 0;
-      if constexpr (MULTI) pi = part_of_group(p, g_done);
-      const GemvPart& pt = p.part[pi];
-      int gl = g_done - pt.group0;
-      float* yo = pt.y[s];
-      if constexpr (PAIR) {
-        const bool second = gl >= pair_groups;
-        yo = second ? pt.y[1] : pt.y[0];
-        gl -= second ? pair_groups : 0;
+      PartStore ps;
+      if constexpr (MULTI) {
+        ps = part_store(p, part_of_group(p, g_done));
+      } else {
+        const GemvPart& p0 = p.part0;
+        ps = PartStore{p0.y[s], p0.ldy, p0.n, p0.group0};
+        if constexpr (PAIR) {
+          // groups of the second stream are numbered after the first's
+          const bool second = g_done - p0.group0 >= pair_groups;
+          ps.y = second ? p0.y[1] : p0.y[0];
+          ps.group0 += second ? pair_groups : 0;
+        }
       }
-      const int rr = gl * ROWS + r;
-      if (rr < pt.n && (MT == 1 || m < p.m_rows)) yo[(size_t)m * pt.ldy + rr] = t;
+      const int rr = (g_done - ps.group0) * ROWS + r;
+      if (rr < ps.n && (MT == 1 || m < p.m_rows)) ps.y[(size_t)m * ps.ldy + rr] = t;
     }
   };
   // The first group is peeled off the loop, so that its loads, issued in

@@ -105,13 +105,17 @@ __global__ void __launch_bounds__(512) gemv_mma_kernel(GemvParams p) {
   const int groups = p.k / p.gs;
   const int gsh = __builtin_ctz((unsigned)p.gs) - 6;  // log2(gs / 64): pairs per group
   auto view_of = [&](int g, View& v) {
-    int pi = 0;
-    if constexpr (MULTI) pi = part_of_group(p, g);
-    const GemvPart& pt = p.part[pi];
+    PartLoad pt;
+    if constexpr (MULTI) {
+      pt = part_load(p, part_of_group(p, g));
+    } else {
+      const GemvPart& p0 = p.part0;
+      pt = PartLoad{p0.w[0], p0.scales, p0.biases, p0.n, p0.group0};
+    }
     const int rr = (g - pt.group0) * ROWS + r16;
     v.row = rr < pt.n ? rr : pt.n - 1;  // clamped for the loads; not stored
     const int kc = FMT == FMT_AFF ? k0 + 16 * kp : (k0 + 16 * kp) / 2;
-    v.w = pt.w[0] + (size_t)v.row * (size_t)p.row_bytes + kc;
+    v.w = pt.w + (size_t)v.row * (size_t)p.row_bytes + kc;
     const size_t gi = (size_t)v.row * groups + (k0 >> (gsh + 6));
     v.sc = pt.scales + gi;
     v.bi = pt.biases + gi;
@@ -132,6 +136,7 @@ __global__ void __launch_bounds__(512) gemv_mma_kernel(GemvParams p) {
 
   int g = blockIdx.x;
   if (g >= p.n_groups) return;
+  if constexpr (MULTI) prefetch_part_table<true>(p);
   View cv;
   view_of(g, cv);
 
@@ -225,11 +230,15 @@ __global__ void __launch_bounds__(512) gemv_mma_kernel(GemvParams p) {
       constexpr int WS = MM * 16;  // stride between waves
       const float t = ((a[0 * WS] + a[1 * WS]) + (a[2 * WS] + a[3 * WS])) +
                       ((a[4 * WS] + a[5 * WS]) + (a[6 * WS] + a[7 * WS]));
-      int pi = 0;
-      if constexpr (MULTI) pi = part_of_group(p, g_done);
-      const GemvPart& pt = p.part[pi];
+      PartStore pt;
+      if constexpr (MULTI) {
+        pt = part_store(p, part_of_group(p, g_done));
+      } else {
+        const GemvPart& p0 = p.part0;
+        pt = PartStore{p0.y[0], p0.ldy, p0.n, p0.group0};
+      }
       const int rr = (g_done - pt.group0) * ROWS + n;
-      if (m < mrows && rr < pt.n) pt.y[0][(size_t)m * pt.ldy + rr] = t;
+      if (m < mrows && rr < pt.n) pt.y[(size_t)m * pt.ldy + rr] = t;
     }
     // the partial sums are read before the next group writes them
     __syncthreads();

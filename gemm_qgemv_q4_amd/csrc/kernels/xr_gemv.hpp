@@ -108,10 +108,11 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p)
   // 16 (i % (SLICE / 16)) of the wave's slice); lane l loads pieces l + 64 j
   // (past the last piece: the last one again).  Rows are whole multiples of
   // SLICE bytes, so every piece is 16-byte aligned when the weights are.
-  auto part_of = [&](int tile) -> const GemvPart& {
-    int pi = 0;
-    if constexpr (MULTI) pi = part_of_group(p, tile);
-    return p.part[pi];
+  // what the loads of a tile need from its part
+  auto part_of = [&](int tile) -> PartLoad {
+    if constexpr (MULTI) return part_load(p, part_of_group(p, tile));
+    const GemvPart& p0 = p.part0;
+    return PartLoad{p0.w[0], p0.scales, p0.biases, p0.n, p0.group0};
   };
   constexpr int PPR = SLICE / 16;  // pieces per row
   constexpr int PIECES = 16 * PPR;
@@ -124,13 +125,13 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p)
   u32x4 ga[LOADS];  // the next row group in flight
   float gsb[AF ? 4 : 1];  // affine: its scales or biases
   auto fetch = [&](u32x4 (&gq)[LOADS], int tile) {
-    const GemvPart& pt = part_of(tile);
+    const PartLoad pt = part_of(tile);
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
       const int i = lane + kWave * j < PIECES ? lane + kWave * j : PIECES - 1;
       const int rr = (tile - pt.group0) * 16 + i / PPR;
       const int row = rr < pt.n ? rr : pt.n - 1;  // clamped for the loads; not stored
-      gq[j] = *reinterpret_cast<const u32x4*>(pt.w[0] + (size_t)row * (size_t)p.row_bytes + SLICE * wv + 16 * (i % PPR));
+      gq[j] = *reinterpret_cast<const u32x4*>(pt.w + (size_t)row * (size_t)p.row_bytes + SLICE * wv + 16 * (i % PPR));
     }
     if constexpr (AF) {
       // lanes 0..31 the scales, 32..63 the biases, 4 entries each
@@ -172,6 +173,7 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p)
   // this workgroup and are not used.  (Two groups in flight measured 4-8%
   // slower.)
   const int G = (int)gridDim.x;
+  if constexpr (MULTI) prefetch_part_table<AF>(p);
   fetch(ga, t);
   // the weight loads leave before the x arithmetic below, behind the x loads only
   __builtin_amdgcn_sched_barrier(0);
@@ -347,9 +349,15 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p)
       const int n = e & 15;
       float sum = red[it & 1][0][m][n] + red[it & 1][0][m + 8][n];
       for (int w = 1; w < waves; ++w) sum += red[it & 1][w][m][n] + red[it & 1][w][m + 8][n];
-      const GemvPart& pt = part_of(t);
+      PartStore pt;
+      if constexpr (MULTI) {
+        pt = part_store(p, part_of_group(p, t));
+      } else {
+        const GemvPart& p0 = p.part0;
+        pt = PartStore{p0.y[0], p0.ldy, p0.n, p0.group0};
+      }
       const int rr = (t - pt.group0) * 16 + n;
-      if (m < p.m_rows && rr < pt.n) pt.y[0][(size_t)m * pt.ldy + rr] = sum;
+      if (m < p.m_rows && rr < pt.n) pt.y[(size_t)m * pt.ldy + rr] = sum;
     }
     // red[it & 1] is written again two groups later, after the next barrier
     ++it;

@@ -158,7 +158,8 @@ qg_status qmm_affine_t_noalloc(const float* x, const uint8_t* q, const float* sc
                                void* stream);
 
 /*
- * qgemv_q4_k_multi -- the parts of a fused projection in one launch.
+ * qgemv_q4_k_multi -- the parts of a fused projection in one launch (up to
+ * four parts per launch of the GEMV kernels; more parts take more launches).
  * Defined by: ferrum-kernels `q4_k_gemv_v2.rs` (doc of
  * dispatch_gemv_q4k_v2_offset: each part of a fused projection has its own
  * weights and writes a disjoint slice of a shared output buffer).

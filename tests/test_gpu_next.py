@@ -85,7 +85,9 @@ def test_dual_mfma_bitwise_equals_two_singles(lib, force_mfma, m, n, k):
 
 
 # ------------------------------------------------------------------ multi-part Q4_K
-MULTI = [(1, (5, 130, 64), 256), (3, (7, 1, 40), 1024), (8, (64, 64), 2048), (1, (33,) * 8, 512)]
+# more than four parts run as several launches of up to four parts each
+MULTI = [(1, (5, 130, 64), 256), (3, (7, 1, 40), 1024), (8, (64, 64), 2048), (1, (33,) * 8, 512),
+         (1, (300, 5, 1024, 17, 64, 1, 2, 100), 4096), (4, (40, 3, 17, 90, 33), 4096)]
 
 
 def _check_multi(lib, m, ns, k, seed, tag):
