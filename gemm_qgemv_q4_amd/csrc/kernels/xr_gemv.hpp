@@ -90,8 +90,11 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p)
   const bool lo_row = r >= 8;
   const int kb0 = wv * NB;  // first block of this wave
 
+  // No range check on the first tile: the host never launches more
+  // workgroups than tiles, and a tile past the last one would only load
+  // clamped rows and store nothing.  Without it the x loads need one
+  // scalar-memory round trip less.
   int t = blockIdx.x;
-  if (t >= p.n_groups) return;
 
   // ---- x slice: for every block lane r < 8 loads the first four of its K
   // piece's x values, lane r + 8 the last four; the two then trade halves.
@@ -347,8 +350,15 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p)
     for (int e = threadIdx.x; e < kXrMaxM * 16; e += blockDim.x) {
       const int m = e >> 4;
       const int n = e & 15;
-      float sum = red[it & 1][0][m][n] + red[it & 1][0][m + 8][n];
-      for (int w = 1; w < waves; ++w) sum += red[it & 1][w][m][n] + red[it & 1][w][m + 8][n];
+      // every wave's partial read first (slots past the last wave are read
+      // and not used), then added in wave order: a loop up to `waves` waited
+      // for each read before the next one left
+      float pw[kXrMaxWaves];
+#pragma unroll
+      for (int w = 0; w < kXrMaxWaves; ++w) pw[w] = red[it & 1][w][m][n] + red[it & 1][w][m + 8][n];
+      float sum = pw[0];
+#pragma unroll
+      for (int w = 1; w < kXrMaxWaves; ++w) sum = w < waves ? sum + pw[w] : sum;
       PartStore pt;
       if constexpr (MULTI) {
         pt = part_store(p, part_of_group(p, t));
