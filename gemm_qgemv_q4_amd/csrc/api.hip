@@ -509,7 +509,7 @@ GemvParams gemv_params(const HostPart* parts, int nparts, int nw, bool split_str
   int np = 0;
   for (int pi = 0; pi < nparts; ++pi) {
     const int ns = split_streams ? nw : 1;
-    for (int st = 0; st < ns && np < kLaunchParts; ++st) {  // callers keep to kLaunchParts streams
+    for (int st = 0; st < ns && np < kLaunchParts; ++st) {  // callers check kLaunchParts streams
       GemvPart gp{};
       for (int j = 0; j < 2; ++j) {
         const int src = split_streams ? st : j;
@@ -576,6 +576,7 @@ qg_status run_gemv_xr(const char* op, const HostPart* parts, int nparts, int nw,
 template <int FMT>
 qg_status run_gemv_mma(const char* op, const HostPart* parts, int nparts, const float* x, int64_t m, int64_t k,
                        int gs, hipStream_t s) {
+  if (nparts > kLaunchParts) return fail("%s: too many weight streams for one launch", op);
   (void)hipGetLastError();
   const GemvParams p = gemv_params(parts, nparts, 1, false, 16, k, gs, row_bytes_of<FMT>(k));
   // one workgroup per CU (the x tile fills most of the LDS), walking row groups
@@ -643,6 +644,7 @@ hipError_t launch_gemv_ks_pair(int j, const GemvParams& p, dim3 grid, hipStream_
 template <int FMT, int NW>
 qg_status run_gemv_fma(const char* op, const CallCfg& cfg, const HostPart* parts, int nparts, const float* x,
                        int64_t m, int64_t k, int gs, hipStream_t s) {
+  if (nparts * NW > kLaunchParts) return fail("%s: too many weight streams for one launch", op);
   (void)hipGetLastError();
   const GemvPlan pl = plan_gemv<FMT>(m, k, NW);
   const int ks = ks_chunks<FMT, NW>(cfg, pl, k);
