@@ -27,6 +27,9 @@ HIP_FLAGS = [
     "-mcode-object-version=5",
     # packed FP32 instructions (v_pk_*_f32) are kept out of the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # leading scalar kernel arguments are preloaded into scalar registers
+    # (the K-sliced GEMV passes what a single-part launch needs that way)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wno-unused-command-line-argument",
 ]
 

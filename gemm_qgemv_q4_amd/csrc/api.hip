@@ -352,18 +352,25 @@ hipError_t launch_gemv_mt(const GemvPlan& pl, const GemvParams& p, dim3 g, dim3 
   return hipErrorInvalidValue;
 }
 
+// The K-sliced kernel's leading scalar arguments (preloaded into scalar
+// registers) followed by the whole parameter block.
+#define KS_ARGS(p)                                                                                             \
+  (p).x, (p).part0.w[0], (p).part0.w[1], (p).part0.y[0], (p).k, (p).n_groups, (p).part0.n, (p).part0.group0, \
+      (int)(p).row_bytes, (p)
+
 // K-sliced kernel for tiles of MT rows of x (same bits as the chunked kernel
 // with the same MT, L and R); J = chunks per lane and row.
 template <int FMT, int MT, int NW, int L, int R, int J, int WV>
 hipError_t launch_gemv_ks_j(const GemvParams& p, dim3 grid, size_t lds, hipStream_t s) {
   if (p.parts > 1) {
     if constexpr (NW == 1 && (FMT == FMT_Q4K || FMT == FMT_AFF)) {
-      hipLaunchKernelGGL((gemv_ks_kernel<FMT, MT, NW, L, R, J, WV, true>), grid, dim3(64 * WV), lds, s, p);
+      hipLaunchKernelGGL((gemv_ks_kernel<FMT, MT, NW, L, R, J, WV, true>), grid, dim3(64 * WV), lds, s,
+                         KS_ARGS(p));
       return hipSuccess;
     }
     return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL((gemv_ks_kernel<FMT, MT, NW, L, R, J, WV, false>), grid, dim3(64 * WV), lds, s, p);
+  hipLaunchKernelGGL((gemv_ks_kernel<FMT, MT, NW, L, R, J, WV, false>), grid, dim3(64 * WV), lds, s, KS_ARGS(p));
   return hipSuccess;
 }
 
@@ -629,10 +636,12 @@ hipError_t launch_gemv_ks_pair(int j, const GemvParams& p, dim3 grid, hipStream_
     const size_t lds = ks_lds<FMT>(1, 1, 64, 1, j, 16);
     switch (j) {
       case 1:
-        hipLaunchKernelGGL((gemv_ks_kernel<FMT, 1, 1, 64, 1, 1, 16, false, true>), grid, dim3(1024), lds, s, p);
+        hipLaunchKernelGGL((gemv_ks_kernel<FMT, 1, 1, 64, 1, 1, 16, false, true>), grid, dim3(1024), lds, s,
+                           KS_ARGS(p));
         return hipSuccess;
       case 2:
-        hipLaunchKernelGGL((gemv_ks_kernel<FMT, 1, 1, 64, 1, 2, 16, false, true>), grid, dim3(1024), lds, s, p);
+        hipLaunchKernelGGL((gemv_ks_kernel<FMT, 1, 1, 64, 1, 2, 16, false, true>), grid, dim3(1024), lds, s,
+                           KS_ARGS(p));
         return hipSuccess;
     }
   }

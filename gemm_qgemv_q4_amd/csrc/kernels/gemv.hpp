@@ -180,6 +180,16 @@ __device__ __forceinline__ void prefetch_part_table(const GemvParams& p) {
     asm volatile("" ::"s"(p.x), "s"(p.n_groups), "s"(p.hot.group0[1]));
   }
 }
+// The same without line 0, for a kernel that has x and the group count in
+// preloaded scalar arguments.
+template <bool AFFINE>
+__device__ __forceinline__ void prefetch_part_quads(const GemvParams& p) {
+  if constexpr (AFFINE) {
+    asm volatile("" ::"s"(p.hot.group0[1]), "s"(p.aff.scales[0]));
+  } else {
+    asm volatile("" ::"s"(p.hot.group0[1]));
+  }
+}
 
 // Where the outputs of part pi go (a multi-part launch has one stream per part).
 struct PartStore {
@@ -216,11 +226,11 @@ template <> struct ChunkOf<FMT_AFF4> { using T = ChunkAff4; };
 // Chunk tg of row `row` of a weight tensor starting at w (affine: its scales
 // and biases start at sc, bi).
 template <int FMT>
-__device__ __forceinline__ typename ChunkOf<FMT>::T load_chunk(const GemvParams& p, const uint8_t* w,
+__device__ __forceinline__ typename ChunkOf<FMT>::T load_chunk(long long row_bytes, int k, int gs, const uint8_t* w,
                                                                const float* sc, const float* bi, int row,
                                                                int tg) {
   typename ChunkOf<FMT>::T c;
-  const uint8_t* rw = w + (size_t)row * (size_t)p.row_bytes;
+  const uint8_t* rw = w + (size_t)row * (size_t)row_bytes;
   if constexpr (FMT == FMT_Q40) {
     const uint8_t* base = rw + 36 * (size_t)tg;
     c.a = *(const u32x4a4*)(base);
@@ -238,8 +248,8 @@ __device__ __forceinline__ typename ChunkOf<FMT>::T load_chunk(const GemvParams&
     } else {
       c.q = *(const u32x4*)(rw + 16 * (size_t)tg);
     }
-    const int groups = p.k / p.gs;
-    const size_t gi = (size_t)row * groups + (32 * tg) / p.gs;
+    const int groups = k / gs;
+    const size_t gi = (size_t)row * groups + (32 * tg) / gs;
     c.s = sc[gi];
     c.b = bi[gi];
   }
@@ -582,7 +592,7 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams p) {
 #pragma unroll
     for (int s = 0; s < NW; ++s)
 #pragma unroll
-      for (int r = 0; r < R; ++r) dst[s][r] = load_chunk<FMT>(p, v.w[s], v.sc, v.bi, rows[r], tg);
+      for (int r = 0; r < R; ++r) dst[s][r] = load_chunk<FMT>(p.row_bytes, p.k, p.gs, v.w[s], v.sc, v.bi, rows[r], tg);
   };
 
   // Stage x[:, k0:k0+ktile] as [m][e4][chunk] float4 columns plus the sums of
@@ -741,7 +751,15 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams p) {
 // stream of twice the row groups, the first half on w[0] / y[0] and the second
 // on w[1] / y[1]; each group then holds one stream's rows, as in a single call.
 template <int FMT, int MT, int NW, int L, int R, int J, int WV, bool MULTI, bool PAIR = false>
-__global__ void __launch_bounds__(64 * WV) gemv_ks_kernel(GemvParams p) {
+__global__ void __launch_bounds__(64 * WV) gemv_ks_kernel(const float* ax, const uint8_t* aw0, const uint8_t* aw1,
+                                                          float* ay0, int ak, int an_groups, int an, int agroup0,
+                                                          int arow_bytes, GemvParams p) {
+  // The leading scalar arguments repeat what a single-part launch needs from
+  // p (x, part 0's weights and output, K, the group count, part 0's rows and
+  // first group, the row stride): the hardware preloads leading scalar
+  // kernel arguments into scalar registers before the wave starts (the build
+  // asks for it), so the first loads leave without waiting for a
+  // kernel-argument load.
   // the in-wave part of the butterfly below covers 4 or 8 virtual lanes
   static_assert((L == 32 || L == 64) && (WV == 4 || WV == 8 || WV == 16) && (L / WV == 4 || L / WV == 8),
                 "4, 8 or 16 waves of 4 or 8 virtual lanes");
@@ -765,7 +783,7 @@ __global__ void __launch_bounds__(64 * WV) gemv_ks_kernel(GemvParams p) {
   const int rset = lane / LW;
   const int c = lane % LW;
   const int vl = LW * wv + c;
-  const int n_chunks = p.k / CH;
+  const int n_chunks = ak / CH;
   f32x4* xs = smem + wv * (MT * NE4 * XP);                                         // [m][e4][u] of this wave
   float* xsum = reinterpret_cast<float*>(smem + WV * MT * NE4 * XP) + wv * NSUM;  // [m][u][2]
   float* red = reinterpret_cast<float*>(smem + WV * MT * NE4 * XP) + WV * NSUM;   // [2][NW][WV][ROWS][MT]
@@ -779,7 +797,7 @@ __global__ void __launch_bounds__(64 * WV) gemv_ks_kernel(GemvParams p) {
     int row[R];
   };
   // groups of one stream of a pair launch
-  const int pair_groups = PAIR ? (p.part0.n + ROWS - 1) / ROWS : 0;
+  const int pair_groups = PAIR ? (an + ROWS - 1) / ROWS : 0;
   auto view_of = [&](int g, View& v) {
     int gl, n;
     if constexpr (MULTI) {
@@ -790,16 +808,15 @@ __global__ void __launch_bounds__(64 * WV) gemv_ks_kernel(GemvParams p) {
       n = pl.n;
       gl = g - pl.group0;
     } else {
-      const GemvPart& pt = p.part0;
-#pragma unroll
-      for (int s = 0; s < NW; ++s) v.w[s] = pt.w[s];
-      v.sc = pt.scales;
-      v.bi = pt.biases;
-      n = pt.n;
-      gl = g - pt.group0;
+      v.w[0] = aw0;
+      if constexpr (NW == 2) v.w[1] = aw1;
+      v.sc = p.part0.scales;
+      v.bi = p.part0.biases;
+      n = an;
+      gl = g - agroup0;
       if constexpr (PAIR) {
         const bool second = gl >= pair_groups;
-        v.w[0] = second ? pt.w[1] : pt.w[0];
+        v.w[0] = second ? aw1 : aw0;
         gl -= second ? pair_groups : 0;
       }
     }
@@ -821,7 +838,7 @@ __global__ void __launch_bounds__(64 * WV) gemv_ks_kernel(GemvParams p) {
 #pragma unroll
       for (int s = 0; s < NW; ++s)
 #pragma unroll
-        for (int r = 0; r < R; ++r) ch[j][s][r] = load_chunk<FMT>(p, v.w[s], v.sc, v.bi, v.row[r], tl);
+        for (int r = 0; r < R; ++r) ch[j][s][r] = load_chunk<FMT>(arow_bytes, ak, p.gs, v.w[s], v.sc, v.bi, v.row[r], tl);
     }
   };
 
@@ -831,7 +848,7 @@ __global__ void __launch_bounds__(64 * WV) gemv_ks_kernel(GemvParams p) {
   // group count, x and a multi-part launch's part table together instead of
   // one after the other.
   int g = blockIdx.x;
-  if constexpr (MULTI) prefetch_part_table<FMT == FMT_AFF || FMT == FMT_AFF4>(p);
+  if constexpr (MULTI) prefetch_part_quads<FMT == FMT_AFF || FMT == FMT_AFF4>(p);
   View cv;
   view_of(g, cv);
   int grid;
@@ -840,15 +857,15 @@ __global__ void __launch_bounds__(64 * WV) gemv_ks_kernel(GemvParams p) {
   // NE4 * (LW*w + L*j) + lane covers chunks LW*w + L*j .. +LW-1.  The loads go
   // out before the first weights; rows past m_rows are zero.
   {
-    const bool x_vec = (reinterpret_cast<uintptr_t>(p.x) & 15u) == 0;
-    const int n4 = p.k >> 2;
+    const bool x_vec = (reinterpret_cast<uintptr_t>(ax) & 15u) == 0;
+    const int n4 = ak >> 2;
     f32x4 xv[MT][J * XS];
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
       for (int j = 0; j < J * XS; ++j) {
         const int f = NE4 * (LW * wv + L * (j / XS)) + kWave * (j % XS) + lane;
-        const float* xr = p.x + (size_t)m * p.k;
+        const float* xr = ax + (size_t)m * ak;
         xv[m][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         if ((MT == 1 || m < p.m_rows) && f < n4) {
           if (x_vec) xv[m][j] = *reinterpret_cast<const f32x4*>(xr + 4 * f);
@@ -913,7 +930,7 @@ __global__ void __launch_bounds__(64 * WV) gemv_ks_kernel(GemvParams p) {
         }
     const int g_done = g;
     g += grid;
-    if (g < p.n_groups) {
+    if (g < an_groups) {
       view_of(g, cv);
       fetch_all(cv);
     }
@@ -946,12 +963,11 @@ __global__ void __launch_bounds__(64 * WV) gemv_ks_kernel(GemvParams p) {
       if constexpr (MULTI) {
         ps = part_store(p, part_of_group(p, g_done));
       } else {
-        const GemvPart& p0 = p.part0;
-        ps = PartStore{p0.y[s], p0.ldy, p0.n, p0.group0};
+        ps = PartStore{s == 0 ? ay0 : p.part0.y[1], p.part0.ldy, an, agroup0};
         if constexpr (PAIR) {
           // groups of the second stream are numbered after the first's
-          const bool second = g_done - p0.group0 >= pair_groups;
-          ps.y = second ? p0.y[1] : p0.y[0];
+          const bool second = g_done - agroup0 >= pair_groups;
+          ps.y = second ? p.part0.y[1] : ay0;
           ps.group0 += second ? pair_groups : 0;
         }
       }
@@ -962,7 +978,7 @@ __global__ void __launch_bounds__(64 * WV) gemv_ks_kernel(GemvParams p) {
   // The first group is peeled off the loop, so that its loads, issued in
   // straight-line code, are waited for one chunk at a time.
   group(0);
-  for (int it = 1; g < p.n_groups; ++it) group(it);
+  for (int it = 1; g < an_groups; ++it) group(it);
 }
 
 // ---------------------------------------------------------------------------
