@@ -72,7 +72,14 @@ __device__ __forceinline__ uint32_t dpp_row_ror8(uint32_t v) {
 }
 
 template <int FMT, bool MULTI>
-__global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p) {
+__global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(const float* ax, const uint8_t* aw0, int ak,
+                                                                  int am_rows, int an_groups, int an, int agroup0,
+                                                                  int arow_bytes, GemvParams p) {
+  // The leading scalar arguments repeat what the x loads and a single-part
+  // launch's weight loads need from p (x, part 0's weights, K, the x rows of
+  // the tile, the tile count, part 0's rows and first tile, the row stride):
+  // the hardware preloads them into scalar registers before the wave starts,
+  // so those loads leave without waiting for a kernel-argument load.
   constexpr bool K4 = FMT == FMT_Q4K;
   constexpr bool AF = FMT == FMT_AFF || FMT == FMT_AFF4;
   constexpr int SLICE = XrRow<FMT>::bytes;
@@ -99,12 +106,15 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p)
   // ---- x slice: for every block lane r < 8 loads the first four of its K
   // piece's x values, lane r + 8 the last four; the two then trade halves.
   const int mx = r & 7;
-  const bool live = mx < p.m_rows;
+  const bool live = mx < am_rows;
   const int e0 = FMT == FMT_Q40 ? 4 * kp + (lo_row ? 16 : 0) : 8 * kp + (lo_row ? 4 : 0);
-  const float* xp = p.x + (size_t)(live ? mx : 0) * p.k + 32 * kb0 + e0;
+  const float* xp = ax + (size_t)(live ? mx : 0) * ak + 32 * kb0 + e0;
   f32x4 xv[NB];
 #pragma unroll
   for (int s = 0; s < NB; ++s) xv[s] = *reinterpret_cast<const f32x4a4*>(xp + 32 * s);
+  // the x loads leave before anything that waits for a kernel-argument load
+  // (the part lookup of a multi-part launch)
+  __builtin_amdgcn_sched_barrier(0);
 
   // ---- weight loads of one row group: 16 rows x SLICE bytes (288 for the
   // block formats) as pieces of 16 bytes (piece i: row i / (SLICE / 16), bytes
@@ -114,8 +124,7 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p)
   // what the loads of a tile need from its part
   auto part_of = [&](int tile) -> PartLoad {
     if constexpr (MULTI) return part_load(p, part_of_group(p, tile));
-    const GemvPart& p0 = p.part0;
-    return PartLoad{p0.w[0], p0.scales, p0.biases, p0.n, p0.group0};
+    return PartLoad{aw0, p.part0.scales, p.part0.biases, an, agroup0};
   };
   constexpr int PPR = SLICE / 16;  // pieces per row
   constexpr int PIECES = 16 * PPR;
@@ -134,13 +143,13 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p)
       const int i = lane + kWave * j < PIECES ? lane + kWave * j : PIECES - 1;
       const int rr = (tile - pt.group0) * 16 + i / PPR;
       const int row = rr < pt.n ? rr : pt.n - 1;  // clamped for the loads; not stored
-      gq[j] = *reinterpret_cast<const u32x4*>(pt.w + (size_t)row * (size_t)p.row_bytes + SLICE * wv + 16 * (i % PPR));
+      gq[j] = *reinterpret_cast<const u32x4*>(pt.w + (size_t)row * (size_t)arow_bytes + SLICE * wv + 16 * (i % PPR));
     }
     if constexpr (AF) {
       // lanes 0..31 the scales, 32..63 the biases, 4 entries each
       const int rr = (tile - pt.group0) * 16 + (lane & 31) / 2;
       const int row = rr < pt.n ? rr : pt.n - 1;
-      const float* src = (lane < 32 ? pt.scales : pt.biases) + (size_t)row * (size_t)(p.k >> gsh) + g0;
+      const float* src = (lane < 32 ? pt.scales : pt.biases) + (size_t)row * (size_t)(ak >> gsh) + g0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int g = 4 * (lane & 1) + e;
@@ -176,7 +185,6 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p)
   // this workgroup and are not used.  (Two groups in flight measured 4-8%
   // slower.)
   const int G = (int)gridDim.x;
-  if constexpr (MULTI) prefetch_part_table<AF>(p);
   fetch(ga, t);
   // the weight loads leave before the x arithmetic below, behind the x loads only
   __builtin_amdgcn_sched_barrier(0);
@@ -221,7 +229,7 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p)
   auto tile = [&](u32x4 (&gq)[LOADS]) {
     stage(gq);
     const int t2 = t + G;
-    fetch(gq, t2 < p.n_groups ? t2 : t);
+    fetch(gq, t2 < an_groups ? t2 : t);
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     const uint8_t* rl = wl + kRowLds * r;
     auto mfma = [&](int s, uint32_t c0, uint32_t c1) -> f32x4 {
@@ -363,18 +371,17 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(GemvParams p)
       if constexpr (MULTI) {
         pt = part_store(p, part_of_group(p, t));
       } else {
-        const GemvPart& p0 = p.part0;
-        pt = PartStore{p0.y[0], p0.ldy, p0.n, p0.group0};
+        pt = PartStore{p.part0.y[0], p.part0.ldy, an, agroup0};
       }
       const int rr = (t - pt.group0) * 16 + n;
-      if (m < p.m_rows && rr < pt.n) pt.y[(size_t)m * pt.ldy + rr] = sum;
+      if (m < am_rows && rr < pt.n) pt.y[(size_t)m * pt.ldy + rr] = sum;
     }
     // red[it & 1] is written again two groups later, after the next barrier
     ++it;
     t += G;
   };
   tile(ga);
-  while (t < p.n_groups) tile(ga);
+  while (t < an_groups) tile(ga);
 }
 
 }  // namespace qg
