@@ -352,11 +352,20 @@ hipError_t launch_gemv_mt(const GemvPlan& pl, const GemvParams& p, dim3 g, dim3 
   return hipErrorInvalidValue;
 }
 
-// The K-sliced kernel's leading scalar arguments (preloaded into scalar
-// registers) followed by the whole parameter block.
+// The K-sliced kernels' leading scalar arguments (preloaded into scalar
+// registers).  Single part (or a part table read from p): x, part 0's
+// weights (both streams), its first output, K, its rows, the row stride and
+// the group count.  Parts in the arguments (up to three Q4_K parts): x, the
+// parts' weights, K, their rows and the first groups of parts 1 and 2 (a
+// two-part launch repeats part 1's weights, gives part 2 no rows and the
+// group count as its first group).
 #define KS_ARGS(p)                                                                                             \
-  (p).x, (p).part0.w[0], (p).part0.w[1], (p).part0.y[0], (p).k, (p).n_groups, (p).part0.n, (p).part0.group0, \
-      (int)(p).row_bytes, (p)
+  (p).x, (p).part0.w[0], (p).part0.w[1], (p).part0.y[0], (p).k, (p).part0.n, (int)(p).row_bytes, (p).n_groups, \
+      (p)
+#define KS_MP_ARGS(p)                                                                                           \
+  (p).x, (p).hot.w[0], (p).hot.w[1], (p).parts > 2 ? (p).hot.w[2] : (p).hot.w[1], (p).k, (p).hot.n[0],       \
+      (p).hot.n[1], (p).parts > 2 ? (p).hot.n[2] : 0, (p).hot.group0[1],                                       \
+      (p).parts > 2 ? (p).hot.group0[2] : (p).n_groups, (p)
 
 // K-sliced kernel for tiles of MT rows of x (same bits as the chunked kernel
 // with the same MT, L and R); J = chunks per lane and row.
@@ -364,8 +373,15 @@ template <int FMT, int MT, int NW, int L, int R, int J, int WV>
 hipError_t launch_gemv_ks_j(const GemvParams& p, dim3 grid, size_t lds, hipStream_t s) {
   if (p.parts > 1) {
     if constexpr (NW == 1 && (FMT == FMT_Q4K || FMT == FMT_AFF)) {
-      hipLaunchKernelGGL((gemv_ks_kernel<FMT, MT, NW, L, R, J, WV, true>), grid, dim3(64 * WV), lds, s,
-                         KS_ARGS(p));
+      // up to three Q4_K parts take their part table from the arguments too
+      if constexpr (FMT == FMT_Q4K) {
+        if (p.parts <= 3) {
+          hipLaunchKernelGGL((gemv_ks_mp_kernel<FMT, MT, NW, L, R, J, WV>), grid, dim3(64 * WV), lds, s,
+                             KS_MP_ARGS(p));
+          return hipSuccess;
+        }
+      }
+      hipLaunchKernelGGL((gemv_ks_kernel<FMT, MT, NW, L, R, J, WV, true>), grid, dim3(64 * WV), lds, s, KS_ARGS(p));
       return hipSuccess;
     }
     return hipErrorInvalidValue;

@@ -750,16 +750,35 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvParams p) {
 // PAIR: the two weight streams of part 0 (a dual product, NW = 1) run as one
 // stream of twice the row groups, the first half on w[0] / y[0] and the second
 // on w[1] / y[1]; each group then holds one stream's rows, as in a single call.
-template <int FMT, int MT, int NW, int L, int R, int J, int WV, bool MULTI, bool PAIR = false>
-__global__ void __launch_bounds__(64 * WV) gemv_ks_kernel(const float* ax, const uint8_t* aw0, const uint8_t* aw1,
-                                                          float* ay0, int ak, int an_groups, int an, int agroup0,
-                                                          int arow_bytes, GemvParams p) {
-  // The leading scalar arguments repeat what a single-part launch needs from
-  // p (x, part 0's weights and output, K, the group count, part 0's rows and
-  // first group, the row stride): the hardware preloads leading scalar
-  // kernel arguments into scalar registers before the wave starts (the build
-  // asks for it), so the first loads leave without waiting for a
-  // kernel-argument load.
+// Scalar arguments of the K-sliced body (the leading, preloaded arguments of
+// the two kernels at the end of this section):
+//   single part (or MULTI without MPRE, which reads its part table from p):
+//     aw0 = part 0's weights, aw1 = its second stream (dual or pair launch),
+//     a3 = its first stream's output, an0 = its rows, an1 = the row stride,
+//     an2 = the group count; ag1 and ag2 are unused;
+//   MULTI && MPRE (up to three parts without scales or biases): aw0, aw1, a3
+//     = the parts' weights, an0..an2 their rows, ag1 and ag2 the first
+//     groups of parts 1 and 2 (a two-part launch passes a3 = aw1, an2 = 0
+//     and ag2 = the group count); the row stride follows from K and the
+//     format, the group count from the parts' rows.
+// Part 0 starts at group 0.
+template <typename T> __device__ __forceinline__ T sel(bool c, T a, T b) { return c ? a : b; }
+template <int FMT> __device__ __forceinline__ int row_bytes_for(int k) {
+  if constexpr (FMT == FMT_Q40) return k / 32 * 18;
+  else if constexpr (FMT == FMT_Q4K) return k / 256 * 144;
+  else if constexpr (FMT == FMT_AFF) return k;
+  else return k / 2;
+}
+
+// The body of both K-sliced kernels below (gemv_ks_kernel and
+// gemv_ks_mp_kernel), which differ only in their leading scalar arguments.
+template <int FMT, int MT, int NW, int L, int R, int J, int WV, bool MULTI, bool PAIR, bool MPRE>
+__device__ __forceinline__ void gemv_ks_body(const float* ax, const uint8_t* aw0, const uint8_t* aw1, const void* a3,
+                                             int ak, int an0, int an1, int an2, int ag1, int ag2,
+                                             const GemvParams& p) {
+  const uint8_t* const aw2 = static_cast<const uint8_t*>(a3);
+  static_assert(!MPRE || (MULTI && NW == 1 && FMT != FMT_AFF && FMT != FMT_AFF4),
+                "parts from the arguments: one stream per part, no scales or biases");
   // the in-wave part of the butterfly below covers 4 or 8 virtual lanes
   static_assert((L == 32 || L == 64) && (WV == 4 || WV == 8 || WV == 16) && (L / WV == 4 || L / WV == 8),
                 "4, 8 or 16 waves of 4 or 8 virtual lanes");
@@ -797,10 +816,24 @@ __global__ void __launch_bounds__(64 * WV) gemv_ks_kernel(const float* ax, const
     int row[R];
   };
   // groups of one stream of a pair launch
-  const int pair_groups = PAIR ? (an + ROWS - 1) / ROWS : 0;
+  const int pair_groups = PAIR ? (an0 + ROWS - 1) / ROWS : 0;
+  const int arow_bytes = MULTI ? row_bytes_for<FMT>(ak) : an1;
+  int an_groups;
+  if constexpr (!MULTI) an_groups = an2;
+  else if constexpr (MPRE) an_groups = ag2 + (an2 + ROWS - 1) / ROWS;
+  else an_groups = p.n_groups;
   auto view_of = [&](int g, View& v) {
     int gl, n;
-    if constexpr (MULTI) {
+    if constexpr (MULTI && MPRE) {
+      // selects of values: a conditional over the arguments themselves is a
+      // select of their addresses, which puts the arguments in scratch memory
+      const bool past0 = g >= ag1, past1 = g >= ag2;
+      v.w[0] = sel(past1, aw2, sel(past0, aw1, aw0));
+      n = sel(past1, an2, sel(past0, an1, an0));
+      gl = g - sel(past1, ag2, sel(past0, ag1, 0));
+      v.sc = nullptr;
+      v.bi = nullptr;
+    } else if constexpr (MULTI) {
       const PartLoad pl = part_load(p, part_of_group(p, g));
       v.w[0] = pl.w;
       v.sc = pl.scales;
@@ -812,8 +845,8 @@ __global__ void __launch_bounds__(64 * WV) gemv_ks_kernel(const float* ax, const
       if constexpr (NW == 2) v.w[1] = aw1;
       v.sc = p.part0.scales;
       v.bi = p.part0.biases;
-      n = an;
-      gl = g - agroup0;
+      n = an0;
+      gl = g;  // part 0 starts at group 0
       if constexpr (PAIR) {
         const bool second = gl >= pair_groups;
         v.w[0] = second ? aw1 : aw0;
@@ -848,10 +881,11 @@ __global__ void __launch_bounds__(64 * WV) gemv_ks_kernel(const float* ax, const
   // group count, x and a multi-part launch's part table together instead of
   // one after the other.
   int g = blockIdx.x;
-  if constexpr (MULTI) prefetch_part_quads<FMT == FMT_AFF || FMT == FMT_AFF4>(p);
+  if constexpr (MULTI && !MPRE) prefetch_part_quads<FMT == FMT_AFF || FMT == FMT_AFF4>(p);
   View cv;
   view_of(g, cv);
   int grid;
+  float* ys[3] = {nullptr, nullptr, nullptr};  // outputs of parts 0..2 (single part: of its two streams)
 
   // x of this wave's chunks, for each of the MT rows of x: float4
   // NE4 * (LW*w + L*j) + lane covers chunks LW*w + L*j .. +LW-1.  The loads go
@@ -878,6 +912,21 @@ __global__ void __launch_bounds__(64 * WV) gemv_ks_kernel(const float* ax, const
     // the arithmetic, where its latency would add to every launch.
     grid = (int)gridDim.x;
     asm volatile("" ::"s"(grid));
+    // The output pointers are not among the preloaded arguments: read them
+    // here too, in the same wait, rather than before the store, where the
+    // load would add its latency to the end of every launch.
+    if constexpr (!MULTI) {
+      ys[0] = static_cast<float*>(const_cast<void*>(a3));
+      if constexpr (NW == 2 || PAIR) {
+        ys[1] = p.part0.y[1];
+        asm volatile("" ::"s"(ys[1]));
+      }
+    } else if constexpr (MPRE) {
+      ys[0] = p.out.y[0];
+      ys[1] = p.out.y[1];
+      ys[2] = p.out.y[2];
+      asm volatile("" ::"s"(ys[0]), "s"(ys[1]), "s"(ys[2]));
+    }
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -929,6 +978,26 @@ __global__ void __launch_bounds__(64 * WV) gemv_ks_kernel(const float* ax, const
           if (c == 0) rb[((s * WV + wv) * ROWS + rset + RS * r) * MT + m] = v;
         }
     const int g_done = g;
+    // where group g_done's outputs go (stream 0; a dual part's stream 1 is
+    // picked per thread below), worked out here where it is uniform
+    PartStore ps;
+    if constexpr (MULTI && MPRE) {
+      const bool past0 = g_done >= ag1, past1 = g_done >= ag2;
+      ps.y = sel(past1, ys[2], sel(past0, ys[1], ys[0]));
+      ps.n = sel(past1, an2, sel(past0, an1, an0));
+      ps.group0 = sel(past1, ag2, sel(past0, ag1, 0));
+      ps.ldy = MT == 1 ? 0 : p.out.ldy[__builtin_amdgcn_readfirstlane((past0 ? 1 : 0) + (past1 ? 1 : 0))];
+    } else if constexpr (MULTI) {
+      ps = part_store(p, part_of_group(p, g_done));
+    } else {
+      ps = PartStore{ys[0], MT == 1 ? 0 : p.part0.ldy, an0, 0};
+      if constexpr (PAIR) {
+        // groups of the second stream are numbered after the first's
+        const bool second = g_done >= pair_groups;
+        ps.y = sel(second, ys[1], ys[0]);
+        ps.group0 = second ? pair_groups : 0;
+      }
+    }
     g += grid;
     if (g < an_groups) {
       view_of(g, cv);
@@ -959,26 +1028,45 @@ __global__ void __launch_bounds__(64 * WV) gemv_ks_kernel(const float* ax, const
       } else {
         t = b0 + b1;
       }
-      PartStore ps;
-      if constexpr (MULTI) {
-        ps = part_store(p, part_of_group(p, g_done));
-      } else {
-        ps = PartStore{s == 0 ? ay0 : p.part0.y[1], p.part0.ldy, an, agroup0};
-        if constexpr (PAIR) {
-          // groups of the second stream are numbered after the first's
-          const bool second = g_done - agroup0 >= pair_groups;
-          ps.y = second ? p.part0.y[1] : ay0;
-          ps.group0 += second ? pair_groups : 0;
-        }
-      }
+      float* yo = ps.y;
+      if constexpr (NW == 2) yo = sel(s == 0, ps.y, ys[1]);
       const int rr = (g_done - ps.group0) * ROWS + r;
-      if (rr < ps.n && (MT == 1 || m < p.m_rows)) ps.y[(size_t)m * ps.ldy + rr] = t;
+      if (rr < ps.n && (MT == 1 || m < p.m_rows)) yo[(size_t)m * ps.ldy + rr] = t;
     }
   };
   // The first group is peeled off the loop, so that its loads, issued in
   // straight-line code, are waited for one chunk at a time.
   group(0);
   for (int it = 1; g < an_groups; ++it) group(it);
+}
+
+// The leading scalar arguments repeat what the first loads need from p: the
+// hardware preloads leading scalar kernel arguments into scalar registers
+// before the wave starts (the build asks for it; a struct argument is not
+// preloaded), so those loads leave without waiting for a kernel-argument
+// load.  The number of preloaded dwords costs time too: 14 instead of 13
+// measured 0.04 us more per launch of the 4096 x 4096 Q4_K product, so a
+// single-part launch passes 12 and only a multi-part launch with its parts
+// in the arguments passes 14.
+//
+// Single part, or a multi-part launch that reads its part table from p:
+// x, part 0's weights (both streams of a dual or pair launch), its first
+// output, K, its rows, the row stride and the group count.
+template <int FMT, int MT, int NW, int L, int R, int J, int WV, bool MULTI, bool PAIR = false>
+__global__ void __launch_bounds__(64 * WV) gemv_ks_kernel(const float* ax, const uint8_t* aw0, const uint8_t* aw1,
+                                                          float* ay0, int ak, int an0, int arow_bytes, int an_groups,
+                                                          GemvParams p) {
+  gemv_ks_body<FMT, MT, NW, L, R, J, WV, MULTI, PAIR, false>(ax, aw0, aw1, ay0, ak, an0, arow_bytes, an_groups, 0, 0,
+                                                              p);
+}
+
+// Up to three Q4_K parts with their parts in the arguments: x, the parts'
+// weights, K, their rows, and the first groups of parts 1 and 2.
+template <int FMT, int MT, int NW, int L, int R, int J, int WV>
+__global__ void __launch_bounds__(64 * WV) gemv_ks_mp_kernel(const float* ax, const uint8_t* aw0, const uint8_t* aw1,
+                                                             const uint8_t* aw2, int ak, int an0, int an1, int an2,
+                                                             int ag1, int ag2, GemvParams p) {
+  gemv_ks_body<FMT, MT, NW, L, R, J, WV, true, false, true>(ax, aw0, aw1, aw2, ak, an0, an1, an2, ag1, ag2, p);
 }
 
 // ---------------------------------------------------------------------------
