@@ -23,9 +23,11 @@
 //
 // Work split: a workgroup of K/512 waves owns 16 weight rows at a time; wave
 // w owns columns 512 w .. 512 w + 511, i.e. NB = 16 blocks (288 bytes of each
-// row for the block formats, 512 for u8 and 256 for packed codes).  The wave keeps its slice of x as 16 MFMA A operands (64 VGPRs) and
-// the block sums (64 VGPRs) for the whole launch, so after the first load x
-// costs no memory or LDS traffic.  The MFMA wants, in lane l, 4 code bytes of
+// row for the block formats, 512 for u8 and 256 for packed codes).  The wave
+// keeps its slice of x as 16 MFMA A operands (64 VGPRs) and the block sums
+// (64 VGPRs) for the whole launch, so after the first load x costs no memory
+// or LDS traffic; that first load reads x row by row and is moved to the MFMA
+// lanes through LDS.  The MFMA wants, in lane l, 4 code bytes of
 // weight row l % 16; loads that narrow touch 16 rows per instruction and
 // stream poorly, so the wave reads its 16 rows with 16-byte loads along the
 // rows (18 lanes per row for the block formats), writes them to its own LDS
@@ -67,6 +69,14 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, c);
 }
 
+// LDS operations of one wave complete in order; this only keeps the compiler
+// from moving a wave's LDS accesses across each other.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ uint32_t dpp_row_ror8(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, true);  // row_ror:8
 }
@@ -91,7 +101,7 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(const float* 
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x / kWave;
-  const int waves = blockDim.x / kWave;
+  const int waves = ak >> 9;  // the launch has K / 512 waves (no hidden-argument load)
   const int r = lane & 15;  // MFMA row of A (x row r & 7; bf16(x) for r < 8, the remainder for r >= 8) and column of B
   const int kp = lane >> 4;  // K piece: weights 4kp..4kp+3, 16+4kp..16+4kp+3 of a Q4_0 block, 8kp..8kp+7 of a Q4_K sub-block
   const bool lo_row = r >= 8;
@@ -103,12 +113,19 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(const float* 
   // scalar-memory round trip less.
   int t = blockIdx.x;
 
-  // ---- x slice: for every block lane r < 8 loads the first four of its K
-  // piece's x values, lane r + 8 the last four; the two then trade halves.
+  // ---- x slice.  The MFMA layout wants, for every block, in lane r < 8 the
+  // first four of its K piece's x values (row r & 7) and in lane r + 8 the
+  // last four; the two then trade halves.  Loaded that way, the 8 lanes of
+  // a quad pair sit on 8 rows of x, and the slice (16 KB per wave at 8 rows)
+  // arrived 1-3 us after the launch.  So the loads read x row by row instead
+  // (lane l: float4 l % 8 of row l / 8 of every block, one 128-byte line per
+  // 8 lanes), and the wave moves the values to the MFMA lanes through its
+  // LDS region, XB blocks at a time.
   const int mx = r & 7;
   const bool live = mx < am_rows;
   const int e0 = FMT == FMT_Q40 ? 4 * kp + (lo_row ? 16 : 0) : 8 * kp + (lo_row ? 4 : 0);
-  const float* xp = ax + (size_t)(live ? mx : 0) * ak + 32 * kb0 + e0;
+  const int xrow = lane >> 3;  // row of x this lane loads (rows past the tile load row 0, unused)
+  const float* xp = ax + (size_t)(xrow < am_rows ? xrow : 0) * ak + 32 * kb0 + 4 * (lane & 7);
   f32x4 xv[NB];
 #pragma unroll
   for (int s = 0; s < NB; ++s) xv[s] = *reinterpret_cast<const f32x4a4*>(xp + 32 * s);
@@ -174,20 +191,18 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(const float* 
 #pragma unroll
       for (int e = 0; e < 4; ++e) d[e] = gsb[e];
     }
-    // LDS operations of one wave complete in order; this only keeps the
-    // compiler from moving the reads above the writes.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    wave_lds_sync();
   };
   // Row group t is loaded first; group t + G (G workgroups) leaves when group
   // t has been copied to LDS.  Past the last group the loads repeat a group of
   // this workgroup and are not used.  (Two groups in flight measured 4-8%
   // slower.)
-  const int G = (int)gridDim.x;
   fetch(ga, t);
   // the weight loads leave before the x arithmetic below, behind the x loads only
   __builtin_amdgcn_sched_barrier(0);
+  // the grid size (a hidden kernel argument) is read while the loads are in flight
+  const int G = (int)gridDim.x;
+  asm volatile("" ::"s"(G));
 
   // ---- A operands and block sums.  Row r < 8 takes bf16(x) of its K piece's
   // 8 weights, row r + 8 takes bf16(x - bf16(x)) of the same.  The block
@@ -201,9 +216,26 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(const float* 
     const bf16x8 ones = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
                          (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
     const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+    // XB blocks of the slice in the wave's LDS region as 8 rows of XROW
+    // floats (132: the 8 rows of one read fall in distinct banks); the first
+    // row group is staged there only after the last pass.
+    constexpr int XB = 4;
+    constexpr int XROW = 32 * XB + 4;
+    static_assert(8 * XROW * 4 <= 16 * kRowLds, "x pass does not fit the wave's LDS region");
+    float* xl = reinterpret_cast<float*>(wl);
+    f32x4 xm[XB];
 #pragma unroll
     for (int s = 0; s < NB; ++s) {
-      const f32x4 v = live ? xv[s] : z;
+      if (s % XB == 0) {
+#pragma unroll
+        for (int b = 0; b < XB; ++b)
+          *reinterpret_cast<f32x4*>(xl + xrow * XROW + 32 * b + 4 * (lane & 7)) = xv[s + b];
+        wave_lds_sync();
+#pragma unroll
+        for (int b = 0; b < XB; ++b) xm[b] = *reinterpret_cast<const f32x4*>(xl + mx * XROW + 32 * b + e0);
+        wave_lds_sync();
+      }
+      const f32x4 v = live ? xm[s % XB] : z;
       // pairs of this lane's four values: (0, 1), (2, 3), or (0, 2), (1, 3) for affine codes
       const float u0 = v.x, u1 = AF ? v.z : v.y, u2 = AF ? v.y : v.z, u3 = v.w;
       const uint32_t h01 = pk_bf16(u0, u1), h23 = pk_bf16(u2, u3);
@@ -244,17 +276,32 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(const float* 
       // (odd) half of the dword holding the block start.  The codes enter the
       // MFMA as the exact bf16 values 16 (q - 8) (int8 bytes, q40_lo16 /
       // q40_hi16), and d / 16 scales the block's product.
-      auto product = [&](int s, uint32_t& db) -> f32x4 {
-        uint32_t v;
+      // All of the lane's code and scale words of the group are read before
+      // the first MFMA (40 registers): read block by block, each MFMA waited
+      // for its own LDS round trip.  The scheduling barrier also keeps the
+      // next group's loads ahead of the MFMAs.
+      uint32_t qw[NB], qe[NB / 2], dw[NB];
+#pragma unroll
+      for (int s = 0; s < NB; ++s) {
         const uint8_t* blk = rl + 18 * s;
         if (s % 2 == 0) {
-          const uint32_t q0 = *reinterpret_cast<const uint32_t*>(blk + 4 * kp);
-          const uint32_t q1 = *reinterpret_cast<const uint32_t*>(blk + 4 * kp + 4);
-          v = __builtin_amdgcn_alignbyte(q1, q0, 2);
-          db = *reinterpret_cast<const uint32_t*>(blk);
+          qw[s] = *reinterpret_cast<const uint32_t*>(blk + 4 * kp);
+          qe[s / 2] = *reinterpret_cast<const uint32_t*>(blk + 4 * kp + 4);
+          dw[s] = *reinterpret_cast<const uint32_t*>(blk);
         } else {
-          v = *reinterpret_cast<const uint32_t*>(blk + 2 + 4 * kp);
-          db = *reinterpret_cast<const uint32_t*>(blk - 2) >> 16;
+          qw[s] = *reinterpret_cast<const uint32_t*>(blk + 2 + 4 * kp);
+          dw[s] = *reinterpret_cast<const uint32_t*>(blk - 2);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      auto product = [&](int s, uint32_t& db) -> f32x4 {
+        uint32_t v;
+        if (s % 2 == 0) {
+          v = __builtin_amdgcn_alignbyte(qe[s / 2], qw[s], 2);
+          db = dw[s];
+        } else {
+          v = qw[s];
+          db = dw[s] >> 16;
         }
         float c[8];
         signed_codes_f32(q40_lo16(v), c[0], c[1], c[2], c[3]);  // elements 4kp .. 4kp+3
@@ -282,21 +329,27 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(const float* 
       // copy: d, dmin, 12 scale bytes, then 4 runs of 32 code bytes.  Sub-block
       // j takes the low (j even) or high nibbles of run j / 2; K piece kp is
       // its bytes 8kp .. 8kp + 7.
+      // both super-blocks' words are read before the first MFMA
+      uint2 hw[NB / 8][2], qw[NB / 8][4];
 #pragma unroll
       for (int b = 0; b < NB / 8; ++b) {
         const uint8_t* sb = rl + 144 * b;
-        const uint2 h0 = *reinterpret_cast<const uint2*>(sb), h1 = *reinterpret_cast<const uint2*>(sb + 8);
-        const u32x4 hd = {h0.x, h0.y, h1.x, h1.y};
+        hw[b][0] = *reinterpret_cast<const uint2*>(sb);
+        hw[b][1] = *reinterpret_cast<const uint2*>(sb + 8);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) qw[b][c] = *reinterpret_cast<const uint2*>(sb + 16 + 32 * c + 8 * kp);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int b = 0; b < NB / 8; ++b) {
+        const u32x4 hd = {hw[b][0].x, hw[b][0].y, hw[b][1].x, hw[b][1].y};
         const float d = f16_bits_to_f32(hd[0]), dmin = f16_bits_to_f32(hd[0] >> 16);
         // 6-bit scales and mins of sub-blocks 0..3 and 4..7, one per byte
         const uint32_t sc03 = hd[1] & 0x3F3F3F3Fu, mn03 = hd[2] & 0x3F3F3F3Fu;
         const uint32_t sc47 = (hd[3] & 0x0F0F0F0Fu) | ((hd[1] >> 2) & 0x30303030u);
         const uint32_t mn47 = ((hd[3] >> 4) & 0x0F0F0F0Fu) | ((hd[2] >> 2) & 0x30303030u);
-        uint2 qv[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) qv[c] = *reinterpret_cast<const uint2*>(sb + 16 + 32 * c + 8 * kp);
         auto product = [&](int j) -> f32x4 {
-          const uint2 v = qv[j / 2];
+          const uint2 v = qw[b][j / 2];
           const int sh = 4 * (j % 2);
           return mfma(8 * b + j, (v.x >> sh) & 0x0F0F0F0Fu, (v.y >> sh) & 0x0F0F0F0Fu);
         };
