@@ -589,11 +589,12 @@ qg_status run_gemv_xr(const char* op, const HostPart* parts, int nparts, int nw,
   const int waves = (int)(k / 512);
   const int64_t cap = (int64_t)device_cus() * (kXrMaxWaves / waves);
   const int64_t grid = p.n_groups < cap ? p.n_groups : cap;
-  auto kern = p.parts > 1 ? gemv_xr_kernel<FMT, true> : gemv_xr_kernel<FMT, false>;
+  auto kern = waves > 4 ? (p.parts > 1 ? gemv_xr_kernel<FMT, true, 8> : gemv_xr_kernel<FMT, false, 8>)
+                        : (p.parts > 1 ? gemv_xr_kernel<FMT, true, 4> : gemv_xr_kernel<FMT, false, 4>);
   for (int64_t m0 = 0; m0 < m; m0 += kXrMaxM) {
     const GemvParams q = m_tile(p, x, m0, m, k, kXrMaxM);
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * waves), 0, s, q.x, q.part0.w[0], q.k, q.m_rows,
-                       q.n_groups, q.part0.n, q.part0.group0, (int)q.row_bytes, q);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * waves), 0, s, q.x,
+                       q.part0.w[0], q.k, q.m_rows, q.n_groups, q.part0.n, q.part0.group0, (int)q.row_bytes, q);
   }
   return launch_status(op);
 }

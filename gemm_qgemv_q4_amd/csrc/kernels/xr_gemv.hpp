@@ -43,6 +43,10 @@ namespace qg {
 constexpr int kXrNB = 16;        // 32-weight blocks per wave
 constexpr int kXrMaxWaves = 8;   // K <= 4096
 constexpr int kXrMaxM = 8;       // x rows per launch
+// Row groups whose wave partials are added after one barrier: 4, or 1 for u8
+// codes, whose larger row groups, loaded early by the waves that run ahead,
+// delayed the x loads of the others (12288 x 4096 at M = 8: 16.9 -> 17.6 us).
+template <int FMT> struct XrSlots { static constexpr int n = FMT == FMT_AFF ? 1 : 4; };
 
 // Bytes of one weight row in a wave's 512-column slice, and the LDS stride of
 // its copy: a stride of 2 mod 32 dwords puts the 16 rows of one MFMA operand
@@ -53,6 +57,18 @@ template <> struct XrRow<FMT_Q40> { static constexpr int bytes = 288, lds = 392;
 template <> struct XrRow<FMT_Q4K> { static constexpr int bytes = 288, lds = 392; };
 template <> struct XrRow<FMT_AFF> { static constexpr int bytes = 512, lds = 520; };
 template <> struct XrRow<FMT_AFF4> { static constexpr int bytes = 256, lds = 264; };
+
+// LDS of one wave: its copy of a row group (16 rows of XrRow::lds bytes), its partial sums of
+// up to XrSlots::n row groups in each of two buffers, and for the affine
+// formats the staged scales and biases of a row group.
+template <int FMT> struct XrLds {
+  static constexpr int rows = 16 * XrRow<FMT>::lds;
+  static constexpr int red = 2 * XrSlots<FMT>::n * 16 * 16 * 4;
+  static constexpr int sb = (FMT == FMT_AFF || FMT == FMT_AFF4) ? 2 * 16 * 8 * 4 : 0;
+  static constexpr int wave = rows + red + sb;
+  static_assert(rows % 16 == 0 && wave % 16 == 0, "wave regions stay 16-byte aligned");
+  static_assert(kXrMaxWaves * wave <= 160 * 1024, "a workgroup's LDS exceeds the CU's");
+};
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -81,7 +97,11 @@ __device__ __forceinline__ uint32_t dpp_row_ror8(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, true);  // row_ror:8
 }
 
-template <int FMT, bool MULTI>
+// WV: the most waves a launch of this instance has (8, or 4 for K <= 2048,
+// whose workgroups then fit twice in a CU's LDS).  The LDS is static:
+// the same layout as dynamic shared memory measured 0.3-0.5 us slower on
+// u8 codes at 8 rows of x.
+template <int FMT, bool MULTI, int WV>
 __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(const float* ax, const uint8_t* aw0, int ak,
                                                                   int am_rows, int an_groups, int an, int agroup0,
                                                                   int arow_bytes, GemvParams p) {
@@ -95,9 +115,10 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(const float* 
   constexpr int SLICE = XrRow<FMT>::bytes;
   constexpr int kRowLds = XrRow<FMT>::lds;
   constexpr int NB = kXrNB;
-  __shared__ float red[2][kXrMaxWaves][16][16];  // [buffer][wave][MFMA row][column]
-  __shared__ u32x4 wlds[kXrMaxWaves][16 * kRowLds / 16];  // per wave: 16 rows of kRowLds bytes
-  __shared__ float sbl[AF ? kXrMaxWaves : 1][2][16][8];   // affine: per wave, scale and bias of 16 rows x 8 groups
+  using LW = XrLds<FMT>;
+  static_assert(WV == 4 || WV == kXrMaxWaves, "instances for 4 and 8 waves");
+  __shared__ u32x4 xr_lds[WV * LW::wave / 16];
+  uint8_t* const lds = reinterpret_cast<uint8_t*>(xr_lds);
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x / kWave;
@@ -175,7 +196,13 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(const float* 
     }
   };
   // The wave's LDS copy: row n at byte kRowLds n (stride chosen in XrRow).
-  uint8_t* wl = reinterpret_cast<uint8_t*>(&wlds[wv][0]);
+  uint8_t* wl = lds + wv * LW::wave;
+  // the wave's partial sums: [buffer][slot][MFMA row][column]
+  auto red_of = [&](int w, int buf, int slot) -> float* {
+    return reinterpret_cast<float*>(lds + w * LW::wave + LW::rows) + (buf * XrSlots<FMT>::n + slot) * 256;
+  };
+  // affine: scale and bias of 16 rows x 8 groups, [2][16][8]
+  float* const sbw = reinterpret_cast<float*>(wl + LW::rows + LW::red);
   auto stage = [&](const u32x4 (&gq)[LOADS]) {
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
@@ -187,7 +214,7 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(const float* 
       d[1] = uint2{gq[j][2], gq[j][3]};
     }
     if constexpr (AF) {
-      float* d = &sbl[wv][lane >> 5][(lane & 31) / 2][4 * (lane & 1)];
+      float* d = sbw + ((lane >> 5) * 16 + (lane & 31) / 2) * 8 + 4 * (lane & 1);
 #pragma unroll
       for (int e = 0; e < 4; ++e) d[e] = gsb[e];
     }
@@ -257,7 +284,8 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(const float* 
 
   // One row group from buffer gq: copy it to LDS, send the loads of the next
   // group into gq, multiply, add the wave partials.
-  int it = 0;
+  int it = 0;    // partial-sum buffer (alternates after every barrier)
+  int slot = 0;  // row groups in it so far
   auto tile = [&](u32x4 (&gq)[LOADS]) {
     stage(gq);
     const int t2 = t + G;
@@ -374,8 +402,8 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(const float* 
       // the row's copy; K piece kp is its bytes 8kp .. 8kp + 7 (u8) or word kp
       // (packed), taken in the order [0, 2, 4, 6, 1, 3, 5, 7].  The scale and
       // bias of its group come from the staged table.
-      const float* sr = &sbl[wv][0][r][0];
-      const float* br = &sbl[wv][1][r][0];
+      const float* sr = sbw + r * 8;
+      const float* br = sbw + 128 + r * 8;
       auto product = [&](int s) -> f32x4 {
         if constexpr (FMT == FMT_AFF) {
           const uint2 v = *reinterpret_cast<const uint2*>(rl + 32 * s + 8 * kp);
@@ -404,34 +432,47 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(const float* 
       }
     }
     // acc[i]: MFMA row 4 kp + i (x row (4kp+i) & 7, high or low part) for weight row r of the group
-    float* rb = &red[it & 1][wv][0][0];
+    float* rb = red_of(wv, it & 1, slot);
 #pragma unroll
     for (int i = 0; i < 4; ++i) rb[(4 * kp + i) * 16 + r] = acc[i];
-    __syncthreads();
-    for (int e = threadIdx.x; e < kXrMaxM * 16; e += blockDim.x) {
-      const int m = e >> 4;
-      const int n = e & 15;
-      // every wave's partial read first (slots past the last wave are read
-      // and not used), then added in wave order: a loop up to `waves` waited
-      // for each read before the next one left
-      float pw[kXrMaxWaves];
-#pragma unroll
-      for (int w = 0; w < kXrMaxWaves; ++w) pw[w] = red[it & 1][w][m][n] + red[it & 1][w][m + 8][n];
-      float sum = pw[0];
-#pragma unroll
-      for (int w = 1; w < kXrMaxWaves; ++w) sum = w < waves ? sum + pw[w] : sum;
-      PartStore pt;
-      if constexpr (MULTI) {
-        pt = part_store(p, part_of_group(p, t));
-      } else {
-        pt = PartStore{p.part0.y[0], p.part0.ldy, an, agroup0};
-      }
-      const int rr = (t - pt.group0) * 16 + n;
-      if (m < am_rows && rr < pt.n) pt.y[(size_t)m * pt.ldy + rr] = sum;
-    }
-    // red[it & 1] is written again two groups later, after the next barrier
-    ++it;
+    ++slot;
     t += G;
+    // The wave partials are added once per XrSlots::n row groups (or after
+    // the last one), so a wave whose x arrived early works on ahead instead
+    // of waiting at a barrier after every group.
+    if (slot == XrSlots<FMT>::n || t >= an_groups) {
+      __syncthreads();
+      const int t0 = t - slot * G;  // first row group of these slots
+      for (int e = threadIdx.x; e < slot * (kXrMaxM * 16); e += blockDim.x) {
+        const int si = e >> 7;
+        const int m = (e >> 4) & 7;
+        const int n = e & 15;
+        const int tt = t0 + si * G;
+        // every wave's partial read first (slots past the last wave read the
+        // last wave's and are not used), then added in wave order: a loop up
+        // to `waves` waited for each read before the next one left
+        float pw[WV];
+#pragma unroll
+        for (int w = 0; w < WV; ++w) {
+          const float* rw = red_of(w < waves ? w : waves - 1, it & 1, si);
+          pw[w] = rw[m * 16 + n] + rw[(m + 8) * 16 + n];
+        }
+        float sum = pw[0];
+#pragma unroll
+        for (int w = 1; w < WV; ++w) sum = w < waves ? sum + pw[w] : sum;
+        PartStore pt;
+        if constexpr (MULTI) {
+          pt = part_store(p, part_of_group(p, tt));
+        } else {
+          pt = PartStore{p.part0.y[0], p.part0.ldy, an, agroup0};
+        }
+        const int rr = (tt - pt.group0) * 16 + n;
+        if (m < am_rows && rr < pt.n) pt.y[(size_t)m * pt.ldy + rr] = sum;
+      }
+      // this buffer is written again after the next barrier
+      ++it;
+      slot = 0;
+    }
   };
   tile(ga);
   while (t < an_groups) tile(ga);
