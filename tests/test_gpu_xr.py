@@ -230,3 +230,59 @@ def test_xr_unaligned_x_gives_the_same_bits(lib, fmt):
     xu.copy_(torch.from_numpy(x).cuda())
     assert xu.data_ptr() % 16 == 4
     assert np.array_equal(bits(host(call(xu))), bits(host(call(dev(x)))))
+
+
+# ---------------------------------------------- many row groups per workgroup
+def _random_blocks(rng, n, k, fmt):
+    """Random but valid weight bytes (any nibbles and scale bytes, finite
+    fp16 d / dmin of either sign) without running a quantizer over N x K
+    values."""
+    if fmt == "q4_0":
+        w = rng.integers(0, 256, size=(n, k // 32, 18), dtype=np.uint8)
+        d = (rng.uniform(0.001, 0.01, size=(n, k // 32)) * rng.choice([-1.0, 1.0], size=(n, k // 32)))
+        w[:, :, 0:2] = d.astype(np.float16).view(np.uint8).reshape(n, k // 32, 2)
+    else:
+        w = rng.integers(0, 256, size=(n, k // 256, 144), dtype=np.uint8)
+        d = rng.uniform(0.001, 0.01, size=(n, k // 256, 2))
+        w[:, :, 0:4] = d.astype(np.float16).view(np.uint8).reshape(n, k // 256, 4)
+    return w.reshape(n, -1)
+
+
+@pytest.mark.parametrize("fmt,m,n,k", [("q4_0", 8, 16400, 4096), ("q4_k", 5, 16403, 4096), ("q4_0", 4, 33001, 2048),
+                                       ("packed", 8, 16411, 4096), ("u8", 3, 8200, 4096)])
+def test_xr_many_row_groups_per_workgroup(lib, fmt, m, n, k):
+    """More than four row groups per workgroup: the wave partials of up to four
+    groups wait in LDS slots for one barrier, in two alternating buffers.  Every
+    output row must equal the same rows computed by a call with few groups
+    (the arithmetic of an output does not depend on the other rows of the
+    call), and a slice agrees with the oracle."""
+    import torch
+    rng = np.random.default_rng(10600 + m + n)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    gs = 64
+    if fmt in ("q4_0", "q4_k"):
+        w = _random_blocks(rng, n, k, fmt)
+        f = lib.qgemv_q4_0 if fmt == "q4_0" else lib.qgemv_q4_k
+        call = lambda rows: f(dev(np.ascontiguousarray(w[rows])), dev(x), rows.stop - rows.start, k)
+        ref = lambda rows: (oracle.decode_q4_0 if fmt == "q4_0" else oracle.decode_q4_k)(
+            np.ascontiguousarray(w[rows]), rows.stop - rows.start, k)
+    else:
+        q = rng.integers(0, 16, size=(n, k), dtype=np.uint8)
+        s = rng.uniform(0.001, 0.01, size=(n, k // gs)).astype(np.float32)
+        b = (0.02 * rng.standard_normal((n, k // gs))).astype(np.float32)
+        if fmt == "u8":
+            call = lambda rows: lib.qmm_affine_t(dev(x), dev(np.ascontiguousarray(q[rows])),
+                                                 dev(np.ascontiguousarray(s[rows])), dev(np.ascontiguousarray(b[rows])), gs)
+        else:
+            wp = synth.pack_b4_u32(q).view(np.int32)
+            call = lambda rows: lib.qmm_affine_t_packed(dev(x), torch.from_numpy(np.ascontiguousarray(wp[rows])).cuda(),
+                                                        dev(np.ascontiguousarray(s[rows])), dev(np.ascontiguousarray(b[rows])), gs)
+        ref = lambda rows: oracle.decode_affine(np.ascontiguousarray(q[rows]), s[rows], b[rows], rows.stop - rows.start, k, gs)
+    y = host(call(slice(0, n)))
+    # slices starting on 16-row group boundaries keep each row's place in its group
+    for rows in (slice(0, 48), slice(16 * (n // 32), 16 * (n // 32) + 40), slice(16 * ((n - 37) // 16), n)):
+        got = y[:, rows]
+        assert np.array_equal(bits(got), bits(host(call(rows)))), f"{fmt} rows {rows}"
+    tail = slice(16 * ((n - 37) // 16), n)
+    assert_close(y[:, tail], ref(tail), x, f"{fmt} xr m{m} n{n} k{k} tail")
+    assert_close(y[:, 0:48], ref(slice(0, 48)), x, f"{fmt} xr m{m} n{n} k{k} head")
