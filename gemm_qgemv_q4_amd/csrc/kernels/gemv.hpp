@@ -246,7 +246,12 @@ __device__ __forceinline__ typename ChunkOf<FMT>::T load_chunk(long long row_byt
       c.qa = *(const u32x4*)(rw + 32 * (size_t)tg);
       c.qb = *(const u32x4*)(rw + 32 * (size_t)tg + 16);
     } else {
-      c.q = *(const u32x4*)(rw + 16 * (size_t)tg);
+      // non-temporal: each 16-byte piece is read once by one lane and the
+      // pieces of a wave are contiguous; 12288 x 4096 gs 64 at M = 1 8.15 ->
+      // 7.8 us.  (The Q4 formats and u8 codes read a line with two or three
+      // instructions; non-temporal loads there measured 4.1 -> 5.0 us on the
+      // Q4_K 4096 x 4096 product.)
+      c.q = __builtin_nontemporal_load((const u32x4*)(rw + 16 * (size_t)tg));
     }
     const int groups = k / gs;
     const size_t gi = (size_t)row * groups + (32 * tg) / gs;
