@@ -145,11 +145,20 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(const float* 
   const int mx = r & 7;
   const bool live = mx < am_rows;
   const int e0 = FMT == FMT_Q40 ? 4 * kp + (lo_row ? 16 : 0) : 8 * kp + (lo_row ? 4 : 0);
-  const int xrow = lane >> 3;  // row of x this lane loads (rows past the tile load row 0, unused)
-  const float* xp = ax + (size_t)(xrow < am_rows ? xrow : 0) * ak + 32 * kb0 + 4 * (lane & 7);
+  // Up to 4 rows of x (x4): each load covers two blocks of 4 rows (lane l:
+  // block l / 32 of the pair, row l / 8 % 4), 8 loads instead of 16.
+  const bool x4 = am_rows <= 4;  // uniform
+  const int xrow = x4 ? (lane >> 3) & 3 : lane >> 3;  // row of x this lane loads (rows past the tile load row 0, unused)
+  const int xblk = x4 ? lane >> 5 : 0;                // block of the pair (x4)
+  const float* xp = ax + (size_t)(xrow < am_rows ? xrow : 0) * ak + 32 * (kb0 + xblk) + 4 * (lane & 7);
   f32x4 xv[NB];
+  if (x4) {
 #pragma unroll
-  for (int s = 0; s < NB; ++s) xv[s] = *reinterpret_cast<const f32x4a4*>(xp + 32 * s);
+    for (int j = 0; j < NB / 2; ++j) xv[j] = *reinterpret_cast<const f32x4a4*>(xp + 64 * j);
+  } else {
+#pragma unroll
+    for (int s = 0; s < NB; ++s) xv[s] = *reinterpret_cast<const f32x4a4*>(xp + 32 * s);
+  }
   // the x loads leave before anything that waits for a kernel-argument load
   // (the part lookup of a multi-part launch)
   __builtin_amdgcn_sched_barrier(0);
@@ -254,9 +263,15 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(const float* 
 #pragma unroll
     for (int s = 0; s < NB; ++s) {
       if (s % XB == 0) {
+        if (x4) {  // rows 0..3 of the pass; rows 4..7 are not live
 #pragma unroll
-        for (int b = 0; b < XB; ++b)
-          *reinterpret_cast<f32x4*>(xl + xrow * XROW + 32 * b + 4 * (lane & 7)) = xv[s + b];
+          for (int j = 0; j < XB / 2; ++j)
+            *reinterpret_cast<f32x4*>(xl + xrow * XROW + 32 * (2 * j + xblk) + 4 * (lane & 7)) = xv[s / 2 + j];
+        } else {
+#pragma unroll
+          for (int b = 0; b < XB; ++b)
+            *reinterpret_cast<f32x4*>(xl + xrow * XROW + 32 * b + 4 * (lane & 7)) = xv[s + b];
+        }
         wave_lds_sync();
 #pragma unroll
         for (int b = 0; b < XB; ++b) xm[b] = *reinterpret_cast<const f32x4*>(xl + mx * XROW + 32 * b + e0);
