@@ -31,9 +31,10 @@
 // weight row l % 16; loads that narrow touch 16 rows per instruction and
 // stream poorly, so the wave reads its 16 rows with 16-byte loads along the
 // rows (18 lanes per row for the block formats), writes them to its own LDS
-// region and reads the MFMA operands from there.  The loads of the next row group leave
-// before the arithmetic on the current one.  The wave partials of an output
-// are added in a fixed order through LDS, one barrier per row group.
+// region and reads the MFMA operands from there.  The loads of the next row
+// group leave before the arithmetic on the current one.  The wave partials of
+// an output are added in a fixed order through LDS, one barrier per up to
+// four row groups (XrSlots).
 #pragma once
 #include "common.hpp"
 #include "gemv.hpp"

@@ -89,8 +89,13 @@ def test_unaligned_x_ksplit(lib):
 
 # affine codes: 32-code chunks, 64 lanes per row and two rows per lane in both
 # kernels; K from 2048 (one chunk per lane) to 8192 (four), ragged last lanes
+# (groups of 64 or 128 codes take their scales and biases through LDS, one
+# 16-byte load per lane: K = 2432 ends a wave's slice inside its 8 chunks,
+# K = 3072 leaves whole slices past the row's end)
 @pytest.mark.parametrize("n,k,gs,code_max", [(1, 2048, 64, 15), (17, 2208, 32, 255), (40, 4096, 64, 15),
-                                             (33, 6144, 512, 255), (300, 8192, 128, 15), (2049, 4096, 64, 255)])
+                                             (33, 6144, 512, 255), (300, 8192, 128, 15), (2049, 4096, 64, 255),
+                                             (77, 2432, 64, 255), (19, 2432, 128, 15), (50, 3072, 128, 15),
+                                             (9, 3072, 64, 255)])
 def test_affine_ksplit_equals_chunked(lib, n, k, gs, code_max):
     x, q, s, b = synth.affine_case(8600 + n, 1, n, k, gs, code_max)
     dx, dq, ds, db = dev(x), dev(q), dev(s), dev(b)
@@ -99,7 +104,7 @@ def test_affine_ksplit_equals_chunked(lib, n, k, gs, code_max):
     assert_close(a, oracle.decode_affine(q, s, b, n, k, gs), x, f"affine ksplit n{n} k{k} gs{gs}")
 
 
-@pytest.mark.parametrize("n,k,gs", [(29, 4096, 64), (64, 2208, 32), (5, 8192, 256)])
+@pytest.mark.parametrize("n,k,gs", [(29, 4096, 64), (64, 2208, 32), (5, 8192, 256), (13, 2432, 128), (21, 3072, 64)])
 def test_packed_ksplit_equals_chunked_and_u8(lib, n, k, gs):
     import torch
     x, q, s, b = synth.affine_case(8700 + n, 1, n, k, gs)
