@@ -228,7 +228,7 @@ template <> struct ChunkOf<FMT_AFF4> { using T = ChunkAff4; };
 template <int FMT>
 __device__ __forceinline__ typename ChunkOf<FMT>::T load_chunk(long long row_bytes, int k, int gs, const uint8_t* w,
                                                                const float* sc, const float* bi, int row,
-                                                               int tg) {
+                                                               int tg, bool with_sb = true) {
   typename ChunkOf<FMT>::T c;
   const uint8_t* rw = w + (size_t)row * (size_t)row_bytes;
   if constexpr (FMT == FMT_Q40) {
@@ -253,12 +253,25 @@ __device__ __forceinline__ typename ChunkOf<FMT>::T load_chunk(long long row_byt
       // Q4_K 4096 x 4096 product.)
       c.q = __builtin_nontemporal_load((const u32x4*)(rw + 16 * (size_t)tg));
     }
-    const int groups = k / gs;
-    const size_t gi = (size_t)row * groups + (32 * tg) / gs;
-    c.s = sc[gi];
-    c.b = bi[gi];
+    c.s = 0.0f;
+    c.b = 0.0f;
+    if (with_sb) {  // else the caller loads them (load_chunk_sb)
+      const int groups = k / gs;
+      const size_t gi = (size_t)row * groups + (32 * tg) / gs;
+      c.s = sc[gi];
+      c.b = bi[gi];
+    }
   }
   return c;
+}
+
+// The scale and bias of an affine chunk loaded without its codes.
+template <typename C>
+__device__ __forceinline__ void load_chunk_sb(C& c, int k, int gs, const float* sc, const float* bi, int row, int tg) {
+  const int groups = k / gs;
+  const size_t gi = (size_t)row * groups + (32 * tg) / gs;
+  c.s = sc[gi];
+  c.b = bi[gi];
 }
 
 // The eight u32 words of byte codes (element order, one code per byte) of an
@@ -868,6 +881,7 @@ __device__ __forceinline__ void gemv_ks_body(const float* ax, const uint8_t* aw0
   // Chunk tg = vl + L j of the lane's rows; past the last chunk the last one
   // is loaded again (same cache lines) and not used.
   Chunk ch[J][NW][R];
+  constexpr bool AFF = FMT == FMT_AFF || FMT == FMT_AFF4;
   auto fetch_all = [&](const View& v) {
 #pragma unroll
     for (int j = 0; j < J; ++j) {
@@ -876,7 +890,23 @@ __device__ __forceinline__ void gemv_ks_body(const float* ax, const uint8_t* aw0
 #pragma unroll
       for (int s = 0; s < NW; ++s)
 #pragma unroll
-        for (int r = 0; r < R; ++r) ch[j][s][r] = load_chunk<FMT>(arow_bytes, ak, p.gs, v.w[s], v.sc, v.bi, v.row[r], tl);
+        for (int r = 0; r < R; ++r)
+          ch[j][s][r] = load_chunk<FMT>(arow_bytes, ak, p.gs, v.w[s], v.sc, v.bi, v.row[r], tl, !AFF);
+    }
+    if constexpr (AFF) {
+      // The scales and biases after all codes: the vector memory counter
+      // completes in order, so a chunk's codes would otherwise wait for the
+      // scale loads issued before them.
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int tg = vl + L * j;
+        const int tl = tg < n_chunks ? tg : n_chunks - 1;
+#pragma unroll
+        for (int s = 0; s < NW; ++s)
+#pragma unroll
+          for (int r = 0; r < R; ++r) load_chunk_sb(ch[j][s][r], ak, p.gs, v.sc, v.bi, v.row[r], tl);
+      }
     }
   };
 
