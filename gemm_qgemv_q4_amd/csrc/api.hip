@@ -822,6 +822,10 @@ qg_status launch_mfma(const char* op, const HostPart* parts, int nparts, int nw,
   if (sm == 2) {
     if (multi) hipLaunchKernelGGL((qmm_mfma_kernel<FMT, true, 4, 2, 2>), grid, block, 0, s, mp);
     else hipLaunchKernelGGL((qmm_mfma_kernel<FMT, false, 4, 2, 2>), grid, block, 0, s, mp);
+  } else if (k % 128 == 0) {
+    // 64x128 tiles take two 64-column K steps per barrier (one workgroup per CU)
+    if (multi) hipLaunchKernelGGL((qmm_mfma_kernel<FMT, true, 2, 2, 2, 2>), grid, block, 0, s, mp);
+    else hipLaunchKernelGGL((qmm_mfma_kernel<FMT, false, 2, 2, 2, 2>), grid, block, 0, s, mp);
   } else {
     if (multi) hipLaunchKernelGGL((qmm_mfma_kernel<FMT, true, 2, 2, 2>), grid, block, 0, s, mp);
     else hipLaunchKernelGGL((qmm_mfma_kernel<FMT, false, 2, 2, 2>), grid, block, 0, s, mp);

@@ -205,8 +205,12 @@ __device__ __forceinline__ void mfma_substep(const __bf16* sAh, const __bf16* sA
 // both factors split into bf16 hi + lo (three MFMAs per 32 groups).  The
 // arithmetic of one output element is the same for every (SM, SN, TI), so
 // the host picks the tile shape from the tile count alone.
-template <int F, bool MULTI, int SM, int SN, int TI>
-__global__ void __launch_bounds__(128 * SM * SN, 8 / TI) qmm_mfma_kernel(MfmaParams p) {
+//
+// BKS: 64-column K steps per barrier (1 or 2).  With 2, a stage is two
+// consecutive steps, loaded, converted and multiplied together, in twice the
+// LDS; each step's arithmetic is unchanged, so the bits are the same.
+template <int F, bool MULTI, int SM, int SN, int TI, int BKS = 1>
+__global__ void __launch_bounds__(128 * SM * SN, BKS == 1 ? 8 / TI : 2) qmm_mfma_kernel(MfmaParams p) {
   constexpr int T = 128 * SM * SN;  // threads
   constexpr int NSUB = SM * SN;
   constexpr int SUBM = 16 * TI;     // rows of a wave pair's sub-tile
@@ -216,9 +220,10 @@ __global__ void __launch_bounds__(128 * SM * SN, 8 / TI) qmm_mfma_kernel(MfmaPar
   constexpr int NB = BN * 4;        // 16-code pieces of weights per stage
   constexpr int IB = NB >= T ? NB / T : 1;  // pieces per thread (threads past NB move none)
   static_assert(RA >= 1 && BM * 8 == RA * T, "x pieces must divide evenly over the threads");
-  __shared__ __attribute__((aligned(16))) __bf16 sA[2][2 * A_ELEMS];  // [buf][hi | lo]
-  __shared__ __attribute__((aligned(16))) __bf16 sB[2][B_ELEMS];
-  __shared__ float sS[2][2][BN];  // [buf][group in stage][n]
+  static_assert(BKS == 1 || BKS == 2, "one or two 64-column steps per stage");
+  __shared__ __attribute__((aligned(16))) __bf16 sA[2 * BKS][2 * A_ELEMS];  // [buf][hi | lo]
+  __shared__ __attribute__((aligned(16))) __bf16 sB[2 * BKS][B_ELEMS];
+  __shared__ float sS[2 * BKS][2][BN];  // [buf][group in step][n]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -428,15 +433,26 @@ __global__ void __launch_bounds__(128 * SM * SN, 8 / TI) qmm_mfma_kernel(MfmaPar
     if ((c0 + kBK) % p.gs == 0) scale_into_acc(buf, 0);
   };
 
-  Regs rg;
-  load(0, rg);
-  store(0, rg, 0);
+  // stage sb holds steps BKS sb .. BKS sb + BKS - 1 in buffers BKS (sb & 1) + u
+  Regs rg[BKS];
+#pragma unroll
+  for (int u = 0; u < BKS; ++u) load(u, rg[u]);
+#pragma unroll
+  for (int u = 0; u < BKS; ++u) store(u, rg[u], u);
   __syncthreads();
-  for (int st = 0; st < stages; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < stages) load(st + 1, rg);
-    compute(st, buf);
-    if (st + 1 < stages) store(st + 1, rg, buf ^ 1);
+  const int nsb = stages / BKS;  // the host launches BKS = 2 for K % 128 == 0 only
+  for (int sb = 0; sb < nsb; ++sb) {
+    const int buf = (sb & 1) * BKS, nbuf = BKS - buf;
+    if (sb + 1 < nsb) {
+#pragma unroll
+      for (int u = 0; u < BKS; ++u) load((sb + 1) * BKS + u, rg[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < BKS; ++u) compute(sb * BKS + u, buf + u);
+    if (sb + 1 < nsb) {
+#pragma unroll
+      for (int u = 0; u < BKS; ++u) store((sb + 1) * BKS + u, rg[u], nbuf + u);
+    }
     __syncthreads();
   }
 
