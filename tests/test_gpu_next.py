@@ -241,3 +241,32 @@ def test_mfma_tile_shape_does_not_change_bits(lib, force_mfma):
         assert np.array_equal(bits(y[:, col:col + n]), bits(single)), f"part at column {col}"
         col += n
     assert_close(y[:, :2048], oracle.decode_q4_k(ws[0], 2048, k), x, "tile shapes")
+
+
+@pytest.mark.parametrize("fmt,gs", [("affine", 32), ("affine", 64), ("affine", 128), ("affine", 512),
+                                    ("q4_0", 32), ("q4_k", 32)])
+def test_mfma_two_steps_per_barrier_same_bits(lib, fmt, gs):
+    """At M = 512 an 8192-row product runs on 128 x 128 tiles with one 64-column
+    K step per barrier, and its first 2048 rows alone on 64 x 128 tiles with
+    two steps per barrier (K a multiple of 128); the outputs they share must
+    be the same bits (groups of 32 codes: two groups per step; 128 and 512:
+    a group spans steps and stages)."""
+    m, n, n_small, k = 512, 8192, 2048, 1024
+    if fmt == "affine":
+        x, q, s, b = synth.affine_case(7000 + gs, m, n, k, gs)
+        dx = dev(x)
+        full = host(lib.qmm_affine_t(dx, dev(q), dev(s), dev(b), gs))
+        small = host(lib.qmm_affine_t(dx, dev(np.ascontiguousarray(q[:n_small])),
+                                      dev(np.ascontiguousarray(s[:n_small])), dev(np.ascontiguousarray(b[:n_small])), gs))
+        ref = oracle.decode_affine(np.ascontiguousarray(q[:64]), s[:64], b[:64], 64, k, gs)
+    else:
+        case = synth.q4_0_case if fmt == "q4_0" else synth.q4_k_case
+        w, x = case(7100, m, n, k)
+        f = lib.qgemv_q4_0 if fmt == "q4_0" else lib.qgemv_q4_k
+        dx = dev(x)
+        full = host(f(dev(w), dx, n, k))
+        small = host(f(dev(np.ascontiguousarray(w[:n_small])), dx, n_small, k))
+        dec = oracle.decode_q4_0 if fmt == "q4_0" else oracle.decode_q4_k
+        ref = dec(np.ascontiguousarray(w[:64]), 64, k)
+    assert np.array_equal(bits(full[:, :n_small]), bits(small)), f"{fmt} gs{gs}"
+    assert_close(small[:, :64], ref, x, f"{fmt} gs{gs} two steps")
