@@ -194,14 +194,17 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(const float* 
       gq[j] = *reinterpret_cast<const u32x4*>(pt.w + (size_t)row * (size_t)arow_bytes + SLICE * wv + 16 * (i % PPR));
     }
     if constexpr (AF) {
-      // lanes 0..31 the scales, 32..63 the biases, 4 entries each
-      const int rr = (tile - pt.group0) * 16 + (lane & 31) / 2;
-      const int row = rr < pt.n ? rr : pt.n - 1;
-      const float* src = (lane < 32 ? pt.scales : pt.biases) + (size_t)row * (size_t)(ak >> gsh) + g0;
+      // load e: rows 4e .. 4e + 3, lane l takes group l % 8 of array (l / 8) % 2
+      // (scales, biases) of row 4e + l / 16, so that each load touches 8 row
+      // segments of 32 bytes (with lanes 0..31 on the scales of 16 rows and
+      // 32..63 on the biases, every load touched 32)
+      const float* base = (((lane >> 3) & 1) ? pt.biases : pt.scales) + g0;
+      const int g = (lane & 7) < wgroups ? lane & 7 : wgroups - 1;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int g = 4 * (lane & 1) + e;
-        gsb[e] = src[g < wgroups ? g : wgroups - 1];
+        const int rr = (tile - pt.group0) * 16 + 4 * e + (lane >> 4);
+        const int row = rr < pt.n ? rr : pt.n - 1;
+        gsb[e] = base[(size_t)row * (size_t)(ak >> gsh) + g];
       }
     }
   };
@@ -224,9 +227,9 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(const float* 
       d[1] = uint2{gq[j][2], gq[j][3]};
     }
     if constexpr (AF) {
-      float* d = sbw + ((lane >> 5) * 16 + (lane & 31) / 2) * 8 + 4 * (lane & 1);
+      float* d = sbw + ((lane >> 3) & 1) * 128 + (lane >> 4) * 8 + (lane & 7);  // [array][row][group]
 #pragma unroll
-      for (int e = 0; e < 4; ++e) d[e] = gsb[e];
+      for (int e = 0; e < 4; ++e) d[32 * e] = gsb[e];  // row 4e + lane / 16
     }
     wave_lds_sync();
   };
