@@ -87,11 +87,11 @@ def test_unaligned_x_ksplit(lib):
     assert np.array_equal(bits(a), bits(host(lib.qgemv_q4_k(dw, dev(x), n, k))))
 
 
-# affine codes: 32-code chunks, 64 lanes per row and two rows per lane in both
-# kernels; K from 2048 (one chunk per lane) to 8192 (four), ragged last lanes
-# (groups of 64 or 128 codes take their scales and biases through LDS, one
-# 16-byte load per lane: K = 2432 ends a wave's slice inside its 8 chunks,
-# K = 3072 leaves whole slices past the row's end)
+# affine codes: 32-code chunks, 64 lanes per row (8 waves of 8 lanes each);
+# K from 2048 (one chunk per lane) to 8192 (four), ragged last lanes (K = 2432
+# ends a wave's slice of 8 chunks part way, K = 3072 leaves whole slices past
+# the row's end), group sizes 32 to 512 (each chunk's scale and bias loaded
+# after all of the row group's codes)
 @pytest.mark.parametrize("n,k,gs,code_max", [(1, 2048, 64, 15), (17, 2208, 32, 255), (40, 4096, 64, 15),
                                              (33, 6144, 512, 255), (300, 8192, 128, 15), (2049, 4096, 64, 255),
                                              (77, 2432, 64, 255), (19, 2432, 128, 15), (50, 3072, 128, 15),
