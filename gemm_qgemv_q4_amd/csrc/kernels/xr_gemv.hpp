@@ -177,8 +177,8 @@ __global__ void __launch_bounds__(64 * kXrMaxWaves) gemv_xr_kernel(const float* 
   constexpr int PPR = SLICE / 16;  // pieces per row
   constexpr int PIECES = 16 * PPR;
   constexpr int LOADS = (PIECES + kWave - 1) / kWave;  // 5, 8 (u8 codes) or 4 (packed)
-  // affine: scale and bias of group g of row i / 8, g = i % 8 (groups past the
-  // wave's last one repeat it)
+  // affine: the groups of the wave's 512-column slice, from g0 (8 groups or
+  // fewer; past the wave's last group a lane loads the last one again)
   const int gsh = AF ? __builtin_ctz((unsigned)p.gs) : 0;
   const int wgroups = AF ? (p.gs >= 512 ? 1 : 512 >> gsh) : 0;
   const int g0 = AF ? (512 * wv) >> gsh : 0;
